@@ -1,0 +1,357 @@
+"""Benchmark of the RAT+ hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+                    [--no-cpu-baseline] [--no-decode-workload]
+
+A step is one pass of the whole hot path over one batch of the prefill
+workload (default: the 1.5B-like shape B=4, H=16, hd=128, T=4096, D=16, no
+window): the recurrence scan with fused anchor compaction, the dilated
+attention over the anchor cache, and one decode step that appends token T to
+every sequence.  Inputs are synthetic (seeded), resident in HBM before the
+timed region, and alternate between two copies so no step re-reads the
+previous step's data from the 256 MB last-level cache.
+
+Printed: ONE JSON line.  ``value`` is prefill tokens per second of the whole
+step, B*T / (time of scan + attention + decode step).  Per-kernel times come
+from HIP events recorded on the stream the kernels are launched on.  The
+decode-step time of the metric is measured on the decode workload (batch 64,
+32 heads, context 32768, D=64, W=128, 256 steps) and reported beside it.
+``roofline`` is for the kernel that takes the most time in the step;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-workload", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method itself must move / compute)
+# ---------------------------------------------------------------------------
+def keyset_total(T, D, W):
+    """sum over t < T of |S(t)| = 1 + min(W,t) + floor(max(0,t-W)/D)."""
+    tot = 0
+    for t in range(T):
+        tot += 1 + min(W, t) + max(0, t - W) // D
+    return tot
+
+
+def scan_bytes(w, es=2):
+    # read k, v, g; write hk, hv; write Kc, Vc rows (1/D of positions); ring
+    per_head = 0
+    for h in range(w.H):
+        per_head += w.T * w.hd * es * 5 + (w.T // w.D[h]) * w.hd * es * 2
+        per_head += min(w.W[h], w.T) * w.hd * es * 2
+    return w.B * per_head + w.B * w.H * w.hd * 4 * 2  # + fp32 final state
+
+
+def attn_bytes(w, es=2):
+    # read q, hk, hv (each once), write o, read each anchor row once, lse
+    tot = 0
+    for h in range(w.H):
+        tot += w.T * w.hd * es * 4 + (w.T // w.D[h]) * w.hd * es * 2 + w.T * 4
+    return w.B * tot
+
+
+def attn_flops(w):
+    tot = 0
+    cache = {}
+    for h in range(w.H):
+        key = (w.D[h], w.W[h])
+        if key not in cache:
+            cache[key] = keyset_total(w.T, *key)
+        tot += 4 * w.hd * cache[key]
+    return w.B * tot
+
+
+def decode_bytes(B, H, hd, D, W, pos, es=2):
+    tot = 0
+    for h in range(H):
+        rows = max(0, pos - W[h]) // D[h] + min(W[h], pos)
+        tot += rows * hd * es * 2              # K and V cache rows
+        tot += 4 * hd * es + hd * es           # q, k, v, g in; o out
+        tot += 4 * hd * 4                      # fp32 state in and out (k, v)
+        tot += (2 * hd * es if W[h] > 0 else 0)  # ring slot
+        tot += (2 * hd * es if pos % D[h] == D[h] - 1 else 0)  # anchor row
+    return B * tot
+
+
+def kernel_source_hash(name):
+    p = os.path.join(ROOT, "dilated_sparse_attention_rat_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_file, launch_key):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d.get(launch_key)
+        if not e or e.get("source_sha") != kernel_source_hash(kernel_file):
+            return None
+        return float(e["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the RAT+ hot path "
+              "shards over (batch, head) with no exchange, and multi-GPU runs are not part "
+              "of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dilated_sparse_attention_rat_amd as rat
+    from dilated_sparse_attention_rat_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    rat.lib()  # fail loudly if the HIP library is missing
+
+    w = synth.WORKLOADS[args.workload]
+    assert w.decode_steps == 0, "the step workload must be a prefill workload"
+    st = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    es = 2 if w.dtype == "bf16" else 4
+    B, H, T, hd = w.B, w.H, w.T, w.hd
+    D, W = list(w.D), list(w.W)
+    T_cap = T + 1
+
+    # ---- inputs (two copies), outputs and caches resident in HBM ----------
+    x = synth.prefill_inputs(w)
+    sets = []
+    for copy in range(2):
+        s = {n: torch.from_numpy(x[n]).to(dev).to(st) for n in "qkvg"}
+        s["hk"] = torch.empty_like(s["k"])
+        s["hv"] = torch.empty_like(s["v"])
+        s["o"] = torch.empty_like(s["q"])
+        s["lse"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        s["cache"] = rat.alloc_cache(B, H, hd, T_cap, D, W, st, dev)
+        s["ws"] = rat.scan_workspace(B, H, T, hd, dev)
+        dx = synth.draw((B, H, 1, hd), w.seed + 77, w.qkv_std, w.g_bias, w.dtype)
+        s["dec"] = {n: torch.from_numpy(dx[n][:, :, 0]).to(dev).to(st) for n in "qkvg"}
+        s["do"] = torch.empty_like(s["dec"]["q"])
+        s["dws"] = rat.decode_workspace(B, H, hd, T_cap, D, W, dev)
+        sets.append(s)
+    del x
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        c = s["cache"]
+        if ev is not None:
+            ev[0].record(stream)
+        rat.rat_scan_prefill(s["k"], s["v"], s["g"], D, W, T_cap, c["Kc"], c["Vc"], c["state_k"],
+                             c["state_v"], s["ws"], hk=s["hk"], hv=s["hv"], k_ring=c["k_ring"],
+                             v_ring=c["v_ring"])
+        if ev is not None:
+            ev[1].record(stream)
+        rat.rat_dilated_attn_prefill(s["q"], s["hk"], s["hv"], c["Kc"], c["Vc"], D, W, T_cap,
+                                     s["o"], s["lse"])
+        if ev is not None:
+            ev[2].record(stream)
+        d = s["dec"]
+        rat.rat_decode_step(d["q"], d["k"], d["v"], d["g"], c["state_k"], c["state_v"], c["Kc"],
+                            c["Vc"], c["k_ring"], c["v_ring"], s["do"], D, W, T, T_cap,
+                            workspace=s["dws"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % 2])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % 2], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_per_step = wall * 1e3 / K
+    tok = B * T
+    value = tok / (ms_per_step / 1e3)
+
+    sb, ab, af = scan_bytes(w, es), attn_bytes(w, es), attn_flops(w)
+    db = decode_bytes(B, H, hd, D, W, T, es)
+    t_scan = float(np.mean(scan_ms)) / 1e3
+    t_attn = float(np.mean(attn_ms)) / 1e3
+    t_dec = float(np.mean(dec_ms)) / 1e3
+    kernels = {
+        "scan": dict(us=t_scan * 1e6, bytes=sb, gbs=sb / t_scan / 1e9),
+        "attention": dict(us=t_attn * 1e6, bytes=ab, flops=af, gbs=ab / t_attn / 1e9,
+                          tflops=af / t_attn / 1e12),
+        "decode_step": dict(us=t_dec * 1e6, bytes=db, gbs=db / t_dec / 1e9),
+    }
+    dom = max(("scan", "attention"), key=lambda k: kernels[k]["us"])
+    if dom == "scan":
+        roof = dict(bound="hbm", achieved=kernels["scan"]["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    kernel="scan_kernel", traffic=traffic_from_profiles("scan.hip", f"scan_w{args.workload}"))
+    else:
+        roof = dict(bound="hbm", achieved=kernels["attention"]["gbs"], peak=HBM_PEAK_GBS,
+                    unit="GB/s", kernel="attn_prefill_kernel",
+                    traffic=traffic_from_profiles("attn_prefill.hip", f"attn_w{args.workload}"))
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    kernels["attention"]["mfma_frac_useful"] = kernels["attention"]["tflops"] / MFMA_BF16_PEAK_TFLOPS
+    kernels["scan"]["hbm_frac"] = kernels["scan"]["gbs"] / HBM_PEAK_GBS
+    kernels["attention"]["hbm_frac"] = kernels["attention"]["gbs"] / HBM_PEAK_GBS
+
+    # ---- decode workload: µs per decode step ------------------------------
+    decode_info = None
+    if not args.no_decode_workload:
+        decode_info = bench_decode_workload(rat, synth, torch, np)
+
+    del sets
+    torch.cuda.empty_cache()
+
+    # ---- CPU oracle baseline (bounded sample of the same step) -----------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": "prefill tok/s + decode step µs per RAT+ layer; % of HBM / MFMA bf16 peak",
+        "value": value,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={B} H={H} hd={hd} T={T} D={D[0]} W={W[0]} "
+                        "(scan + dilated attention prefill + 1 decode step per step)",
+            "global_batch": B,
+            "seq_len": T,
+            "parallelism": "single GPU",
+            "decode_workload": "decode: batch 64, H=32, hd=128, context 32768, D=64, W=128, "
+                               "256 steps",
+        },
+        "prefill_tok_s_kernels_only": tok / (t_scan + t_attn),
+        "decode_us_per_step": decode_info["us_mean"] if decode_info else None,
+        "kernels": kernels,
+        "decode_workload": decode_info,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def bench_decode_workload(rat, synth, torch, np):
+    w = synth.WORKLOADS[3]
+    B, H, T, hd, steps = w.B, w.H, w.T, w.hd, w.decode_steps
+    T_cap = w.T_cap
+    D, W = list(w.D), list(w.W)
+    cache = rat.alloc_cache(B, H, hd, T_cap, D, W, torch.bfloat16, "cuda")
+    ws = rat.scan_workspace(1, H, T, hd, "cuda")
+    for b in range(B):  # context: cache-only prefill one batch row at a time
+        kvg = synth.decode_context_row(w, b)
+        rat.rat_scan_prefill(kvg["k"], kvg["v"], kvg["g"], D, W, T_cap, cache["Kc"][b:b + 1],
+                             cache["Vc"][b:b + 1], cache["state_k"][b:b + 1],
+                             cache["state_v"][b:b + 1], ws, k_ring=cache["k_ring"][b:b + 1],
+                             v_ring=cache["v_ring"][b:b + 1])
+        del kvg
+    inputs = [synth.decode_step_inputs(w, s) for s in range(steps)]
+    outs = torch.empty((B, H, hd), dtype=torch.bfloat16, device="cuda")
+    dws = rat.decode_workspace(B, H, hd, T_cap, D, W, "cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for s in range(steps):
+        x = inputs[s]
+        rat.rat_decode_step(x["q"], x["k"], x["v"], x["g"], cache["state_k"], cache["state_v"],
+                            cache["Kc"], cache["Vc"], cache["k_ring"], cache["v_ring"], outs, D,
+                            W, T + s, T_cap, workspace=dws)
+        evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([evs[s].elapsed_time(evs[s + 1]) * 1e3 for s in range(steps)])
+    nbytes = np.array([decode_bytes(B, H, hd, D, W, T + s) for s in range(steps)], dtype=np.float64)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = dict(us_mean=float(us.mean()), us_max=float(us.max()), us_min=float(us.min()),
+               bytes_mean=float(nbytes.mean()), gbs_mean=float(gbs.mean()),
+               hbm_frac=float(gbs.mean() / HBM_PEAK_GBS), steps=steps)
+    del cache, inputs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, target_s):
+    """Time the CPU oracle (as it stands) on whole (batch row, head) slices of
+    the step's prefill workload until about target_s seconds of work or the
+    whole workload, and scale to tokens of the full layer."""
+    import numpy as np
+    import oracle
+    from dilated_sparse_attention_rat_amd import synth
+    x = synth.prefill_inputs(w)
+    nthr = max(1, oracle.num_threads())
+    done_bh = 0
+    spent = 0.0
+    for b in range(w.B):
+        f = {n: x[n][b:b + 1].astype(np.float64) for n in "qkvg"}
+        for h0 in range(0, w.H, nthr):
+            sl = slice(h0, min(w.H, h0 + nthr))
+            t0 = time.perf_counter()
+            oracle.prefill(f["q"][:, sl], f["k"][:, sl], f["v"][:, sl], f["g"][:, sl],
+                           list(w.D[sl]), list(w.W[sl]), w.scale, w.dtype == "bf16")
+            spent += time.perf_counter() - t0
+            done_bh += sl.stop - sl.start
+            if spent >= target_s:
+                break
+        if spent >= target_s:
+            break
+    frac = done_bh / (w.B * w.H)
+    tok_equiv = w.B * w.T * frac
+    return dict(value=tok_equiv / spent, unit="tok/s", cores=nthr, kind="oracle",
+                sample=f"oracle prefill (scan + attention, fp64, OpenMP over heads) of {done_bh} "
+                       f"of {w.B * w.H} (batch row, head) sequences at T={w.T}, {spent:.1f} s; "
+                       "tokens scaled by the fraction of sequences done",
+                seconds=spent)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,16 @@
+"""RAT+ inference hot path on AMD MI355X (gfx950).
+
+The compute lives in ``librat.so`` (hand-written HIP kernels behind the C ABI
+of ``include/rat.h``); :mod:`.binding` is its argument-marshalling layer and
+:mod:`.synth` draws the seeded synthetic workloads.
+"""
+from .binding import (RAT_DTYPE_BF16, RAT_DTYPE_F32, RAT_ERR_CAPACITY,  # noqa: F401
+                      RAT_ERR_HIP, RAT_ERR_INVALID_ARG, RAT_ERR_UNSUPPORTED,
+                      RAT_ERR_WORKSPACE, RAT_MAX_HEADS, RAT_OK, RatError,
+                      alloc_cache, decode_workspace, lib, rat_anchor_rows,
+                      rat_decode_step, rat_decode_workspace_bytes,
+                      rat_dilated_attn_prefill, rat_ring_rows,
+                      rat_scan_prefill, rat_scan_workspace_bytes,
+                      rat_status_string, rat_version, scan_workspace)
+
+__version__ = "0.1.0"

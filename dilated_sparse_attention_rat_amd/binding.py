@@ -1,0 +1,315 @@
+"""Thin ctypes binding of ``librat.so`` (argument marshalling only).
+
+Every entry point of ``include/rat.h`` has a Python function of the same
+name.  The functions take torch tensors (device memory and streams are the
+only things torch is used for), check that each tensor has the shape, dtype,
+device and contiguity the C ABI expects (the library itself can only check
+pointers), pass ``data_ptr()`` and the current HIP stream, and raise
+:class:`RatError` on a non-zero status.  All computation happens in the HIP
+kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librat.so")
+
+RAT_OK = 0
+RAT_ERR_INVALID_ARG = -1
+RAT_ERR_UNSUPPORTED = -2
+RAT_ERR_CAPACITY = -3
+RAT_ERR_WORKSPACE = -4
+RAT_ERR_HIP = -5
+RAT_DTYPE_BF16 = 0
+RAT_DTYPE_F32 = 1
+RAT_MAX_HEADS = 128
+
+EXPORTED = [
+    "rat_version", "rat_status_string", "rat_anchor_rows", "rat_ring_rows",
+    "rat_scan_workspace_bytes", "rat_scan_prefill", "rat_dilated_attn_prefill",
+    "rat_decode_workspace_bytes", "rat_decode_step",
+]
+
+
+class RatError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({_status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; fails loudly if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m dilated_sparse_attention_rat_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                ctypes.c_float, ctypes.c_size_t)
+        L.rat_version.restype = ctypes.c_char_p
+        L.rat_status_string.argtypes = [i32]
+        L.rat_status_string.restype = ctypes.c_char_p
+        L.rat_anchor_rows.argtypes = [i32, i64, P, P]
+        L.rat_anchor_rows.restype = i64
+        L.rat_ring_rows.argtypes = [i32, P, P]
+        L.rat_ring_rows.restype = i64
+        L.rat_scan_workspace_bytes.argtypes = [i32, i32, i64, i32]
+        L.rat_scan_workspace_bytes.restype = i64
+        L.rat_scan_prefill.argtypes = [i32, i32, i32, i64, i32, P, P, i64,
+                                       P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.rat_scan_prefill.restype = i32
+        L.rat_dilated_attn_prefill.argtypes = [i32, i32, i32, i64, i32, P, P,
+                                               f32, i64, P, P, P, P, P, P, P, P]
+        L.rat_dilated_attn_prefill.restype = i32
+        L.rat_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, P, P, i32]
+        L.rat_decode_workspace_bytes.restype = i64
+        L.rat_decode_step.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64,
+                                      P, P, P, P, P, P, P, P, P, P, P, i32, P,
+                                      sz, P]
+        L.rat_decode_step.restype = i32
+        _lib = L
+    return _lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().rat_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - only while the library is missing
+        return "?"
+
+
+def _check(fn: str, status: int):
+    if status != RAT_OK:
+        raise RatError(fn, status)
+
+
+def _heads(x, H: int) -> np.ndarray:
+    a = np.ascontiguousarray(np.broadcast_to(np.asarray(x, dtype=np.int32), (H,)))
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling helpers
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RAT_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return RAT_DTYPE_F32
+    raise TypeError(f"unsupported storage dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t, name, shape, dtype, device):
+    """Pointer of a required device tensor after checking it."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype} != {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: device {t.device} != {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t, name, shape, dtype, device):
+    return None if t is None else _dev(t, name, shape, dtype, device)
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def rat_version() -> str:
+    return lib().rat_version().decode()
+
+
+def rat_status_string(status: int) -> str:
+    return _status_string(status)
+
+
+def rat_anchor_rows(H: int, T_cap: int, D):
+    """Returns (R, offsets[H+1]) of the anchor-only cache."""
+    Dh = _heads(D, H)
+    off = np.zeros(H + 1, dtype=np.int64)
+    r = lib().rat_anchor_rows(H, T_cap, _ptr(Dh), _ptr(off))
+    if r < 0:
+        raise RatError("rat_anchor_rows", int(r))
+    return int(r), off
+
+
+def rat_ring_rows(H: int, W):
+    Wh = _heads(W, H)
+    off = np.zeros(H + 1, dtype=np.int64)
+    r = lib().rat_ring_rows(H, _ptr(Wh), _ptr(off))
+    if r < 0:
+        raise RatError("rat_ring_rows", int(r))
+    return int(r), off
+
+
+def rat_scan_workspace_bytes(B: int, H: int, T: int, hd: int) -> int:
+    r = lib().rat_scan_workspace_bytes(B, H, T, hd)
+    if r < 0:
+        raise RatError("rat_scan_workspace_bytes", int(r))
+    return int(r)
+
+
+def rat_decode_workspace_bytes(B: int, H: int, hd: int, T_cap: int, D, W,
+                               num_splits: int = 0) -> int:
+    r = lib().rat_decode_workspace_bytes(B, H, hd, T_cap, _ptr(_heads(D, H)),
+                                         _ptr(_heads(W, H)), num_splits)
+    if r < 0:
+        raise RatError("rat_decode_workspace_bytes", int(r))
+    return int(r)
+
+
+def rat_scan_prefill(k, v, g, D, W, T_cap: int, Kc, Vc, state_k, state_v,
+                     workspace, hk=None, hv=None, k_ring=None, v_ring=None,
+                     stream=None):
+    """Recurrence + fused anchor compaction.  k, v, g: [B,H,T,hd]."""
+    torch = _torch()
+    B, H, T, hd = k.shape
+    st = k.dtype
+    dev = k.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    R, _ = rat_anchor_rows(H, T_cap, Dh)
+    WS, _ = rat_ring_rows(H, Wh)
+    args = [
+        _dtype_code(k), B, H, T, hd, _ptr(Dh), _ptr(Wh), T_cap,
+        _dev(k, "k", (B, H, T, hd), st, dev), _dev(v, "v", (B, H, T, hd), st, dev),
+        _dev(g, "g", (B, H, T, hd), st, dev),
+        _opt(hk, "hk", (B, H, T, hd), st, dev), _opt(hv, "hv", (B, H, T, hd), st, dev),
+        _opt(Kc, "Kc", (B, R, hd), st, dev), _opt(Vc, "Vc", (B, R, hd), st, dev),
+        _opt(k_ring, "k_ring", (B, WS, hd), st, dev), _opt(v_ring, "v_ring", (B, WS, hd), st, dev),
+        _dev(state_k, "state_k", (B, H, hd), torch.float32, dev),
+        _dev(state_v, "state_v", (B, H, hd), torch.float32, dev),
+    ]
+    need = rat_scan_workspace_bytes(B, H, T, hd)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    args += [ctypes.c_void_p(workspace.data_ptr()),
+             workspace.numel() * workspace.element_size(), _stream(stream, dev)]
+    _check("rat_scan_prefill", lib().rat_scan_prefill(*args))
+
+
+def rat_dilated_attn_prefill(q, hk, hv, Kc, Vc, D, W, T_cap: int, o, lse=None,
+                             scale: float = 0.0, stream=None):
+    """Dilated causal attention.  q, hk, hv, o: [B,H,T,hd]; Kc, Vc: [B,R,hd]."""
+    torch = _torch()
+    B, H, T, hd = q.shape
+    st = q.dtype
+    dev = q.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    R, _ = rat_anchor_rows(H, T_cap, Dh)
+    args = [
+        _dtype_code(q), B, H, T, hd, _ptr(Dh), _ptr(Wh), float(scale), T_cap,
+        _dev(q, "q", (B, H, T, hd), st, dev), _dev(hk, "hk", (B, H, T, hd), st, dev),
+        _dev(hv, "hv", (B, H, T, hd), st, dev),
+        _opt(Kc, "Kc", (B, R, hd), st, dev), _opt(Vc, "Vc", (B, R, hd), st, dev),
+        _dev(o, "o", (B, H, T, hd), st, dev),
+        _opt(lse, "lse", (B, H, T), torch.float32, dev), _stream(stream, dev),
+    ]
+    _check("rat_dilated_attn_prefill", lib().rat_dilated_attn_prefill(*args))
+
+
+def rat_decode_step(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, o,
+                    D, W, pos: int, T_cap: int, scale: float = 0.0,
+                    num_splits: int = 0, workspace=None, stream=None):
+    """One decode step at position pos.  q, k, v, g, o: [B,H,hd]."""
+    torch = _torch()
+    B, H, hd = q.shape
+    st = q.dtype
+    dev = q.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    R, _ = rat_anchor_rows(H, T_cap, Dh)
+    WS, _ = rat_ring_rows(H, Wh)
+    need = rat_decode_workspace_bytes(B, H, hd, T_cap, Dh, Wh, num_splits)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace must hold {need} bytes")
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the same device")
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr())
+        ws_bytes = workspace.numel() * workspace.element_size()
+    args = [
+        _dtype_code(q), B, H, hd, _ptr(Dh), _ptr(Wh), float(scale), pos, T_cap,
+        _dev(q, "q", (B, H, hd), st, dev), _dev(k, "k", (B, H, hd), st, dev),
+        _dev(v, "v", (B, H, hd), st, dev), _dev(g, "g", (B, H, hd), st, dev),
+        _dev(state_k, "state_k", (B, H, hd), torch.float32, dev),
+        _dev(state_v, "state_v", (B, H, hd), torch.float32, dev),
+        _opt(Kc, "Kc", (B, R, hd), st, dev), _opt(Vc, "Vc", (B, R, hd), st, dev),
+        _opt(k_ring, "k_ring", (B, WS, hd), st, dev), _opt(v_ring, "v_ring", (B, WS, hd), st, dev),
+        _dev(o, "o", (B, H, hd), st, dev), int(num_splits), ws_ptr, ws_bytes,
+        _stream(stream, dev),
+    ]
+    _check("rat_decode_step", lib().rat_decode_step(*args))
+
+
+# ---------------------------------------------------------------------------
+# allocation helpers (plumbing: device buffers in the layouts of rat.h)
+# ---------------------------------------------------------------------------
+def alloc_cache(B: int, H: int, hd: int, T_cap: int, D, W, dtype, device,
+                fill=None):
+    """Anchor cache, window ring and fp32 state for one layer."""
+    torch = _torch()
+    R, _ = rat_anchor_rows(H, T_cap, D)
+    WS, _ = rat_ring_rows(H, W)
+
+    def mk(shape, dt):
+        if fill is None:
+            return torch.empty(shape, dtype=dt, device=device)
+        return torch.full(shape, fill, dtype=dt, device=device)
+
+    return dict(
+        Kc=mk((B, R, hd), dtype), Vc=mk((B, R, hd), dtype),
+        k_ring=mk((B, WS, hd), dtype) if WS > 0 else None,
+        v_ring=mk((B, WS, hd), dtype) if WS > 0 else None,
+        state_k=torch.zeros((B, H, hd), dtype=torch.float32, device=device),
+        state_v=torch.zeros((B, H, hd), dtype=torch.float32, device=device),
+    )
+
+
+def scan_workspace(B: int, H: int, T: int, hd: int, device):
+    """Zero-filled scan workspace (zero it again only after a failed call)."""
+    torch = _torch()
+    n = rat_scan_workspace_bytes(B, H, T, hd)
+    return torch.zeros(((n + 15) // 16) * 4, dtype=torch.int32, device=device)
+
+
+def decode_workspace(B: int, H: int, hd: int, T_cap: int, D, W, device,
+                     num_splits: int = 0):
+    torch = _torch()
+    n = rat_decode_workspace_bytes(B, H, hd, T_cap, D, W, num_splits)
+    if n == 0:
+        return None
+    return torch.empty(((n + 15) // 16) * 4, dtype=torch.int32, device=device)

@@ -1,0 +1,328 @@
+// C-ABI layer of the RAT+ hot path: host-side validation, per-head offset
+// tables (anchor cache and window ring), launch configuration, and the
+// launches on the caller's stream.  No allocation, no synchronisation, no
+// global mutable state.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "rat.h"
+#include "rat_params.h"
+
+using namespace rat;
+
+namespace {
+
+constexpr int64_t kMaxT = (int64_t)1 << 30;  // positions are int32 in kernels
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int dtype, int B, int H, int hd, const int32_t* D, const int32_t* W) {
+  if (B < 0 || H < 0 || D == nullptr || W == nullptr) return RAT_ERR_INVALID_ARG;
+  if (H > RAT_MAX_HEADS) return RAT_ERR_UNSUPPORTED;
+  if (dtype != RAT_DTYPE_BF16 && dtype != RAT_DTYPE_F32) return RAT_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 128) return RAT_ERR_UNSUPPORTED;
+  for (int h = 0; h < H; ++h) {
+    if (D[h] < 1 || W[h] < 0) return RAT_ERR_INVALID_ARG;
+    if ((int64_t)W[h] > kMaxT) return RAT_ERR_INVALID_ARG;
+  }
+  return RAT_OK;
+}
+
+// Fills the per-head tables; returns RAT_OK or an error if an offset does
+// not fit the kernels' 32-bit row indices.
+int fill_tables(int H, int64_t T_cap, const int32_t* D, const int32_t* W, HeadTables& ht,
+                int64_t& R, int64_t& WS) {
+  std::memset(&ht, 0, sizeof(ht));
+  R = 0;
+  WS = 0;
+  for (int h = 0; h < H; ++h) {
+    ht.D[h] = D[h];
+    ht.W[h] = W[h];
+    ht.aoff[h] = (int32_t)R;
+    ht.roff[h] = (int32_t)WS;
+    R += T_cap / D[h];
+    WS += W[h];
+    if (R > INT32_MAX || WS > INT32_MAX) return RAT_ERR_UNSUPPORTED;
+  }
+  return RAT_OK;
+}
+
+int map_hip(int e) { return e == 0 ? RAT_OK : RAT_ERR_HIP; }
+
+// Workspace of the scan: header, then per tree node a tag (uint32) and an
+// aggregate (A, Bk, Bv: 3*hd fp32).  Level l has ceil(nchunk / 8^l) nodes per
+// sequence; levels are added until the top one has at most 8 nodes.
+struct ScanLayout {
+  int64_t nchunk = 0, nticket = 0, entries = 0;
+  int nlevels = 0;
+  int nodes[kScanMaxLevels] = {};
+  int64_t lbase[kScanMaxLevels] = {};
+  int64_t flags_off = 0, agg_off = 0, bytes = 0;
+};
+
+bool scan_layout(int B, int H, int64_t T, int hd, int dtype, ScanLayout& L) {
+  const int lc = scan_rows_per_chunk(dtype, hd);
+  L.nchunk = (T + lc - 1) / lc;
+  L.nticket = (int64_t)B * H * L.nchunk;
+  int64_t n = std::max<int64_t>(L.nchunk, 1);
+  L.nlevels = 0;
+  L.entries = 0;
+  while (true) {
+    if (L.nlevels >= kScanMaxLevels) return false;
+    L.nodes[L.nlevels] = (int)n;
+    L.lbase[L.nlevels] = L.entries;
+    L.entries += (int64_t)B * H * n;
+    ++L.nlevels;
+    if (n <= kScanRadix) break;
+    n = (n + kScanRadix - 1) / kScanRadix;
+  }
+  auto up = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
+  L.flags_off = kScanHeaderBytes;
+  L.agg_off = up(L.flags_off + L.entries * 4);
+  L.bytes = up(L.agg_off + L.entries * 3 * hd * 4);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rat_version(void) { return "rat-mi355x 0.1.0 (gfx950)"; }
+
+const char* rat_status_string(int status) {
+  switch (status) {
+    case RAT_OK: return "ok";
+    case RAT_ERR_INVALID_ARG: return "invalid argument";
+    case RAT_ERR_UNSUPPORTED: return "unsupported configuration (dtype, head dim or size)";
+    case RAT_ERR_CAPACITY: return "position beyond the cache capacity T_cap";
+    case RAT_ERR_WORKSPACE: return "workspace missing or too small";
+    case RAT_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int64_t rat_anchor_rows(int H, int64_t T_cap, const int32_t* D, int64_t* offsets_out) {
+  if (H < 0 || T_cap < 0 || (H > 0 && D == nullptr)) return RAT_ERR_INVALID_ARG;
+  int64_t r = 0;
+  for (int h = 0; h < H; ++h) {
+    if (D[h] < 1) return RAT_ERR_INVALID_ARG;
+    if (offsets_out) offsets_out[h] = r;
+    r += T_cap / D[h];
+  }
+  if (offsets_out) offsets_out[H] = r;
+  return r;
+}
+
+int64_t rat_ring_rows(int H, const int32_t* W, int64_t* offsets_out) {
+  if (H < 0 || (H > 0 && W == nullptr)) return RAT_ERR_INVALID_ARG;
+  int64_t r = 0;
+  for (int h = 0; h < H; ++h) {
+    if (W[h] < 0) return RAT_ERR_INVALID_ARG;
+    if (offsets_out) offsets_out[h] = r;
+    r += W[h];
+  }
+  if (offsets_out) offsets_out[H] = r;
+  return r;
+}
+
+int64_t rat_scan_workspace_bytes(int B, int H, int64_t T, int hd) {
+  if (B < 0 || H < 0 || T < 0 || T > kMaxT) return RAT_ERR_INVALID_ARG;
+  if (hd != 64 && hd != 128) return RAT_ERR_UNSUPPORTED;
+  // the chunk length depends on the storage type; size for the larger of the
+  // two layouts so one workspace serves both
+  ScanLayout a, b;
+  if (!scan_layout(B, H, T, hd, RAT_DTYPE_BF16, a) || !scan_layout(B, H, T, hd, RAT_DTYPE_F32, b))
+    return RAT_ERR_UNSUPPORTED;
+  return std::max(a.bytes, b.bytes);
+}
+
+int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* D,
+                     const int32_t* W, int64_t T_cap, const void* k, const void* v, const void* g,
+                     void* hk, void* hv, void* Kc, void* Vc, void* k_ring, void* v_ring,
+                     float* state_k, float* state_v, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_common(dtype, B, H, hd, D, W);
+  if (st != RAT_OK) return st;
+  if (T < 0 || T_cap < T || T_cap > kMaxT) return T_cap < T ? RAT_ERR_CAPACITY : RAT_ERR_INVALID_ARG;
+  if (B == 0 || H == 0) return RAT_OK;
+  ScanParams p;
+  std::memset(&p, 0, sizeof(p));
+  st = fill_tables(H, T_cap, D, W, p.ht, p.R, p.WS);
+  if (st != RAT_OK) return st;
+  if (state_k == nullptr || state_v == nullptr || !aligned16(state_k) || !aligned16(state_v))
+    return RAT_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!k || !v || !g || !aligned16(k) || !aligned16(v) || !aligned16(g)) return RAT_ERR_INVALID_ARG;
+    if ((hk == nullptr) != (hv == nullptr)) return RAT_ERR_INVALID_ARG;
+    if (hk && (!aligned16(hk) || !aligned16(hv))) return RAT_ERR_INVALID_ARG;
+    if (p.R > 0 && (!Kc || !Vc || !aligned16(Kc) || !aligned16(Vc))) return RAT_ERR_INVALID_ARG;
+    if (p.WS > 0 && (!k_ring || !v_ring || !aligned16(k_ring) || !aligned16(v_ring)))
+      return RAT_ERR_INVALID_ARG;
+    ScanLayout L;
+    if (!scan_layout(B, H, T, hd, dtype, L)) return RAT_ERR_UNSUPPORTED;
+    if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < L.bytes)
+      return RAT_ERR_WORKSPACE;
+    if (L.nticket > INT32_MAX) return RAT_ERR_UNSUPPORTED;
+    char* ws = static_cast<char*>(workspace);
+    p.hdr = reinterpret_cast<uint32_t*>(ws);
+    p.flags = reinterpret_cast<uint32_t*>(ws + L.flags_off);
+    p.agg = reinterpret_cast<float*>(ws + L.agg_off);
+    p.nticket = (int)L.nticket;
+    p.nchunk = (int)L.nchunk;
+    p.nlevels = L.nlevels;
+    for (int l = 0; l < L.nlevels; ++l) {
+      p.nodes[l] = L.nodes[l];
+      p.lbase[l] = L.lbase[l];
+    }
+  }
+  p.B = B;
+  p.H = H;
+  p.T = (int)T;
+  p.nseq = B * H;
+  p.nclass = 1;
+  while (p.nclass < kScanMaxClasses && p.nseq % (2 * p.nclass) == 0) p.nclass *= 2;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.hk = hk;
+  p.hv = hv;
+  p.Kc = Kc;
+  p.Vc = Vc;
+  p.kr = k_ring;
+  p.vr = v_ring;
+  p.sk = state_k;
+  p.sv = state_v;
+  return map_hip(launch_scan(dtype, hd, p, stream));
+}
+
+int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* D,
+                             const int32_t* W, float scale, int64_t T_cap, const void* q,
+                             const void* hk, const void* hv, const void* Kc, const void* Vc,
+                             void* o, float* lse, void* stream) {
+  int st = check_common(dtype, B, H, hd, D, W);
+  if (st != RAT_OK) return st;
+  if (T < 0 || T_cap < T || T_cap > kMaxT) return T_cap < T ? RAT_ERR_CAPACITY : RAT_ERR_INVALID_ARG;
+  if (!(scale <= 0.f) && !std::isfinite(scale)) return RAT_ERR_INVALID_ARG;
+  if (B == 0 || H == 0 || T == 0) return RAT_OK;
+  AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  int64_t WS;
+  st = fill_tables(H, T_cap, D, W, p.ht, p.R, WS);
+  if (st != RAT_OK) return st;
+  if (!q || !hk || !hv || !o || !aligned16(q) || !aligned16(hk) || !aligned16(hv) || !aligned16(o))
+    return RAT_ERR_INVALID_ARG;
+  if (p.R > 0 && (!Kc || !Vc || !aligned16(Kc) || !aligned16(Vc))) return RAT_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return RAT_ERR_INVALID_ARG;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)hd);
+  p.B = B;
+  p.H = H;
+  p.T = (int)T;
+  p.nq = (int)((T + kAttnBM - 1) / kAttnBM);
+  p.np = (p.nq + 1) / 2;
+  if ((int64_t)H * B * p.np > INT32_MAX) return RAT_ERR_UNSUPPORTED;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.q = q;
+  p.hk = hk;
+  p.hv = hv;
+  p.Kc = Kc;
+  p.Vc = Vc;
+  p.o = o;
+  p.lse = lse;
+  // heads in descending cost of one pair-block (anchor tiles + band tiles of
+  // the heaviest and the lightest query tile), so heavy heads start first
+  const int bn = kAttnBN;
+  auto tiles = [&](int h, int qt) -> int64_t {
+    const int64_t t0 = (int64_t)qt * kAttnBM;
+    const int64_t tl = std::min<int64_t>(t0 + kAttnBM - 1, T - 1);
+    const int64_t na = std::max<int64_t>(0, tl - W[h]) / D[h];
+    int64_t n = (na + bn - 1) / bn + 1;
+    if (W[h] > 0) n += (tl - std::max<int64_t>(0, t0 - W[h]) + bn) / bn;
+    return n;
+  };
+  int64_t cost[RAT_MAX_HEADS];
+  for (int h = 0; h < H; ++h) {
+    cost[h] = tiles(h, p.nq - 1) + (p.nq > 1 ? tiles(h, 0) : 0);
+    p.perm[h] = h;
+  }
+  std::stable_sort(p.perm, p.perm + H, [&](int a, int b) { return cost[a] > cost[b]; });
+  return map_hip(launch_attn_prefill(dtype, hd, p, stream));
+}
+
+namespace {
+int decode_splits(int B, int H, int64_t T_cap, const int32_t* D, const int32_t* W, int requested) {
+  if (requested > 0) return requested;
+  int64_t maxk = 0;
+  for (int h = 0; h < H; ++h) maxk = std::max<int64_t>(maxk, T_cap / D[h] + W[h]);
+  const int64_t nbh = std::max<int64_t>(1, (int64_t)B * H);
+  // aim for >= 2048 workgroups (8 per CU), but keep >= 256 rows per split
+  int64_t s = (2048 + nbh - 1) / nbh;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, maxk / 256));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
+}  // namespace
+
+int64_t rat_decode_workspace_bytes(int B, int H, int hd, int64_t T_cap, const int32_t* D,
+                                   const int32_t* W, int num_splits) {
+  int st = check_common(RAT_DTYPE_BF16, B, H, hd, D, W);
+  if (st != RAT_OK) return st;
+  if (T_cap < 0 || T_cap > kMaxT || num_splits < 0) return RAT_ERR_INVALID_ARG;
+  const int s = decode_splits(B, H, T_cap, D, W, num_splits);
+  if (s <= 1) return 0;
+  return (int64_t)B * H * s * (hd + 2) * 4;
+}
+
+int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D, const int32_t* W,
+                    float scale, int64_t pos, int64_t T_cap, const void* q, const void* k,
+                    const void* v, const void* g, float* state_k, float* state_v, void* Kc,
+                    void* Vc, void* k_ring, void* v_ring, void* o, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(dtype, B, H, hd, D, W);
+  if (st != RAT_OK) return st;
+  if (T_cap < 0 || T_cap > kMaxT || pos < 0 || num_splits < 0 || num_splits > 1024)
+    return RAT_ERR_INVALID_ARG;
+  if (pos >= T_cap) return RAT_ERR_CAPACITY;
+  if (!(scale <= 0.f) && !std::isfinite(scale)) return RAT_ERR_INVALID_ARG;
+  if (B == 0 || H == 0) return RAT_OK;
+  DecodeParams p;
+  std::memset(&p, 0, sizeof(p));
+  st = fill_tables(H, T_cap, D, W, p.ht, p.R, p.WS);
+  if (st != RAT_OK) return st;
+  for (const void* ptr : {q, k, v, g, (const void*)o})
+    if (!ptr || !aligned16(ptr)) return RAT_ERR_INVALID_ARG;
+  if (!state_k || !state_v || !aligned16(state_k) || !aligned16(state_v)) return RAT_ERR_INVALID_ARG;
+  if (p.R > 0 && (!Kc || !Vc || !aligned16(Kc) || !aligned16(Vc))) return RAT_ERR_INVALID_ARG;
+  if (p.WS > 0 && (!k_ring || !v_ring || !aligned16(k_ring) || !aligned16(v_ring)))
+    return RAT_ERR_INVALID_ARG;
+  const int s = decode_splits(B, H, T_cap, D, W, num_splits);
+  if (s > 1) {
+    const int64_t need = (int64_t)B * H * s * (hd + 2) * 4;
+    if (!workspace || !aligned16(workspace) || (int64_t)workspace_bytes < need)
+      return RAT_ERR_WORKSPACE;
+  }
+  if ((int64_t)B * H > INT32_MAX / 2) return RAT_ERR_UNSUPPORTED;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)hd);
+  p.B = B;
+  p.H = H;
+  p.splits = s;
+  p.pos = (int)pos;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.sk = state_k;
+  p.sv = state_v;
+  p.Kc = Kc;
+  p.Vc = Vc;
+  p.kr = k_ring;
+  p.vr = v_ring;
+  p.o = o;
+  p.part = static_cast<float*>(workspace);
+  return map_hip(launch_decode(dtype, hd, p, stream));
+}
+
+}  // extern "C"

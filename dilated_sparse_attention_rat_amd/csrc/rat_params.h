@@ -1,0 +1,114 @@
+// Kernel parameter blocks, filled on the host by the C-ABI layer and passed
+// by value as kernel arguments (per-head tables included, so a head-wise
+// hybrid needs no device-side table and no extra copy).
+#pragma once
+
+#include <stdint.h>
+
+#include "rat.h"
+
+namespace rat {
+
+constexpr int kMaxHeads = RAT_MAX_HEADS;
+
+struct HeadTables {
+  int32_t D[kMaxHeads];     // dilation per head
+  int32_t W[kMaxHeads];     // window per head
+  int32_t aoff[kMaxHeads];  // first anchor-cache row of the head
+  int32_t roff[kMaxHeads];  // first ring slot of the head
+};
+
+// Scan workspace header: one 4 KB slot per ticket class (so the classes'
+// atomics do not contend on one address).  Slot x holds
+//   [0] ticket: next chunk ticket of class x in the running launch
+//   [1] epoch:  launches of class x completed on this workspace
+//   [2] error:  != 0 if a wait for an aggregate timed out
+constexpr int kScanMaxClasses = 8;
+constexpr int kScanClassStride = 1024;  // uint32 words (4 KB)
+constexpr int64_t kScanHeaderBytes = (int64_t)kScanMaxClasses * kScanClassStride * 4;
+
+constexpr int kScanRadix = 8;      // fan-in of the chunk-aggregate tree
+constexpr int kScanMaxLevels = 10;
+
+struct ScanParams {
+  int B, H, T;
+  int nseq;        // B * H
+  int nchunk;      // chunks per sequence
+  int nticket;     // nseq * nchunk (= grid size)
+  int nclass;      // ticket classes (a power of two dividing nseq, <= 8)
+  int nlevels;     // levels of the aggregate tree (top level has <= radix nodes)
+  int nodes[kScanMaxLevels];     // nodes per sequence at each level
+  int64_t lbase[kScanMaxLevels]; // first entry of each level in flags/agg
+  int64_t R;       // anchor rows per batch row
+  int64_t WS;      // ring slots per batch row
+  const void* k;
+  const void* v;
+  const void* g;
+  void* hk;        // nullable (cache-only mode)
+  void* hv;
+  void* Kc;
+  void* Vc;
+  void* kr;        // nullable iff all W == 0
+  void* vr;
+  float* sk;
+  float* sv;
+  uint32_t* hdr;    // kScanMaxClasses slots of kScanClassStride words
+  uint32_t* flags;  // [entries]: epoch tag of a published tree node
+  float* agg;       // [entries][3][hd]: A, Bk, Bv of the node's chunk range
+  HeadTables ht;
+};
+
+struct AttnParams {
+  int B, H, T;
+  int nq;            // query tiles per (b, h)
+  int np;            // pair-blocks per (b, h)
+  float scale_log2;  // scale * log2(e)
+  int64_t R;
+  const void* q;
+  const void* hk;
+  const void* hv;
+  const void* Kc;
+  const void* Vc;
+  void* o;
+  float* lse;        // nullable
+  int32_t perm[kMaxHeads];  // heads in descending per-block cost
+  HeadTables ht;
+};
+
+struct DecodeParams {
+  int B, H;
+  int splits;
+  int pos;
+  float scale_log2;
+  int64_t R;
+  int64_t WS;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  float* sk;
+  float* sv;
+  void* Kc;
+  void* Vc;
+  void* kr;
+  void* vr;
+  void* o;
+  float* part;       // [B*H][splits][2 + hd] (m, l, acc) when splits > 1
+  HeadTables ht;
+};
+
+// launchers (one per kernel family); return hipError_t as int
+int launch_scan(int dtype, int hd, const ScanParams& p, void* stream);
+int launch_attn_prefill(int dtype, int hd, const AttnParams& p, void* stream);
+int launch_decode(int dtype, int hd, const DecodeParams& p, void* stream);
+
+// sizes shared by the host layer and the kernels
+constexpr int kScanThreads = 256;
+constexpr int kScanRowsPerThread = 4;
+int scan_rows_per_chunk(int dtype, int hd);
+
+constexpr int kAttnBM = 128;   // queries per tile (4 waves x 32)
+constexpr int kAttnBN = 64;    // keys per LDS tile
+constexpr int kDecodeThreads = 256;
+
+}  // namespace rat

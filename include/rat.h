@@ -1,0 +1,184 @@
+/*
+ * rat.h -- C ABI of the RAT+ inference hot path on AMD MI355X (gfx950).
+ *
+ * The method ("RAT+: Train Dense, Infer Sparse -- Recurrence Augmented
+ * Attention for Dilated Inference", abstract; zhichai.net deep dive
+ * "RAT+ 深度拆解", sections 一, 2.1, 2.2 and 六):
+ *
+ *   1. a per-channel, input-gated recurrence over keys and values that runs
+ *      over the whole sequence (deep dive, section 2.1):
+ *          h_t = g_t * h_{t-1} + (1 - g_t) * x_t,   h_{-1} = 0,
+ *      the same gate for keys and values, computed in fp32;
+ *   2. causal softmax attention dilated by D (abstract; deep dive, section
+ *      一): query t attends to the recurrent states at the anchors
+ *      j = D-1 (mod D), j < t, to its own position t, and optionally to a
+ *      local window of the W positions before t (abstract: the window is an
+ *      option).  D = 1 and W = 0 is dense causal attention (deep
+ *      dive, section 2.2).  D and W are chosen per head at inference time
+ *      (abstract; deep dive, sections 六 and 7.1: head-wise hybrids).
+ *   3. the KV cache keeps only the anchors, floor(T_cap / D) rows per head,
+ *      which is the D-fold cache cut of the abstract, plus a ring of the
+ *      last W states for the window.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller (any allocator),
+ *    contiguous in the stated layout and 16-byte aligned.  The library never
+ *    allocates device memory, never synchronises and keeps no global mutable
+ *    state.  All GPU work is enqueued on `stream` (a hipStream_t; NULL is
+ *    the default stream) and completes asynchronously.
+ *  - Per-head tables D[H], W[H] are HOST int32 arrays, the same for every
+ *    batch row; 1 <= D[h], 0 <= W[h]; H <= RAT_MAX_HEADS.
+ *  - dtype is RAT_DTYPE_BF16 or RAT_DTYPE_F32: the storage type (ST) of
+ *    q, k, v, g, the states hk/hv, the caches and o.  Recurrent state
+ *    (state_k/state_v) and lse are always fp32.  hd (head dim) is 64 or 128.
+ *  - Layouts: activations [B, H, T, hd]; state [B, H, hd];
+ *    anchor cache Kc/Vc [B, R, hd] with head h's rows at
+ *    off[h] = sum_{h'<h} floor(T_cap / D[h']) (R = off[H]); anchor row a of
+ *    head h holds position a*D[h] + D[h] - 1;
+ *    window ring k_ring/v_ring [B, sum(W), hd] with head h's W[h] slots at
+ *    roff[h] = sum_{h'<h} W[h']; position p lives in slot p mod W[h].
+ *  - Every function validates all arguments on the host before enqueuing
+ *    anything; a call that fails validation writes nothing.  Return values:
+ *    RAT_OK (0) or a negative RAT_ERR_* code; no C++ exception crosses the
+ *    ABI.  RAT_ERR_HIP means a launch was rejected by the HIP runtime.
+ *  - Thread-safe and reentrant.  Calls that share a workspace or write the
+ *    same outputs must be ordered by the caller (same stream).
+ */
+#ifndef RAT_H_
+#define RAT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RAT_OK 0
+#define RAT_ERR_INVALID_ARG (-1)
+#define RAT_ERR_UNSUPPORTED (-2)
+#define RAT_ERR_CAPACITY (-3)
+#define RAT_ERR_WORKSPACE (-4)
+#define RAT_ERR_HIP (-5)
+
+#define RAT_DTYPE_BF16 0
+#define RAT_DTYPE_F32 1
+
+#define RAT_MAX_HEADS 128
+
+/* Library version string (static storage). */
+const char* rat_version(void);
+
+/* Static, human-readable message for a status code. */
+const char* rat_status_string(int status);
+
+/*
+ * Rows per batch row of the anchor-only cache for capacity T_cap (abstract:
+ * the cache shrinks by D).  R = sum_h floor(T_cap / D[h]).  If offsets_out
+ * is not NULL it receives H+1 values: off[h] and off[H] = R.
+ * Pure host function.  Returns R >= 0, or RAT_ERR_INVALID_ARG.
+ */
+int64_t rat_anchor_rows(int H, int64_t T_cap, const int32_t* D,
+                        int64_t* offsets_out);
+
+/*
+ * Slots per batch row of the window ring: sum_h W[h]; offsets_out (nullable)
+ * receives H+1 values roff[h], roff[H] = total.  Pure host function.
+ * Returns the total >= 0, or RAT_ERR_INVALID_ARG.
+ */
+int64_t rat_ring_rows(int H, const int32_t* W, int64_t* offsets_out);
+
+/*
+ * Bytes of device workspace rat_scan_prefill needs for (B, H, T, hd).
+ * The workspace carries the scan's chunk-to-chunk carries.  It must be
+ * zero-filled once before its first use; every call leaves it ready for the
+ * next call (after a call that returned an error, or a launch that was
+ * aborted, zero-fill it again).  One workspace must not be used by two calls
+ * that can run at the same time.  The first 32 KB are eight 4 KB counter
+ * slots; uint32 word 2 of the workspace is an error word: != 0 after a call
+ * means a chunk gave up waiting for a predecessor's aggregate (results of
+ * that call are invalid).  Pure host function; returns bytes (> 0) or a
+ * negative code.
+ */
+int64_t rat_scan_workspace_bytes(int B, int H, int64_t T, int hd);
+
+/*
+ * Prefill recurrence with fused anchor compaction (deep dive, section 2.1:
+ * full-sequence recurrence computed by an associative scan in prefill;
+ * abstract: anchor-only KV cache).
+ *
+ * Reads  k, v, g          [B, H, T, hd] ST (g in [0, 1])
+ * Writes hk, hv           [B, H, T, hd] ST: h_t of keys / values (both
+ *                         NULL = cache-only mode: only the outputs below)
+ *        Kc, Vc           [B, R(T_cap), hd] ST: rows a < floor(T / D[h]) of
+ *                         each head (other rows untouched)
+ *        k_ring, v_ring   [B, sum W, hd] ST: slots of positions
+ *                         max(0, T - W[h]) .. T-1 (NULL allowed iff all W = 0)
+ *        state_k, state_v [B, H, hd] fp32: h_{T-1} (zeros when T = 0)
+ * Requires 0 <= T <= T_cap.  Starts from the zero state at position 0.
+ * workspace: see rat_scan_workspace_bytes (RAT_ERR_WORKSPACE if too small).
+ */
+int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd,
+                     const int32_t* D, const int32_t* W, int64_t T_cap,
+                     const void* k, const void* v, const void* g, void* hk,
+                     void* hv, void* Kc, void* Vc, void* k_ring, void* v_ring,
+                     float* state_k, float* state_v, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill dilated attention (abstract; deep dive, sections 一, 2.2, 六).
+ * For each (b, h, t): keys S(t) = {t} U {j < t : j = D-1 mod D}
+ *                                 U {max(0, t-W) .. t-1},
+ *   o_t = sum_{j in S(t)} softmax_j(scale * q_t . hk_j) hv_j,
+ *   lse_t = log sum_{j in S(t)} exp(scale * q_t . hk_j)   (natural log).
+ * Anchors j < max(0, t-W) are read from the compact cache Kc/Vc (as written
+ * by rat_scan_prefill with the same D, T_cap); window and own positions are
+ * read from hk/hv.
+ * Reads  q, hk, hv [B, H, T, hd] ST; Kc, Vc [B, R(T_cap), hd] ST.
+ * Writes o [B, H, T, hd] ST; lse [B, H, T] fp32 (nullable).
+ * scale <= 0 selects 1/sqrt(hd).  Requires 0 <= T <= T_cap.
+ */
+int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd,
+                             const int32_t* D, const int32_t* W, float scale,
+                             int64_t T_cap, const void* q, const void* hk,
+                             const void* hv, const void* Kc, const void* Vc,
+                             void* o, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace rat_decode_step needs for any pos < T_cap with
+ * num_splits (0 = automatic choice).  0 means no workspace is needed
+ * (the single-split path).  Pure host function; negative on error.
+ */
+int64_t rat_decode_workspace_bytes(int B, int H, int hd, int64_t T_cap,
+                                   const int32_t* D, const int32_t* W,
+                                   int num_splits);
+
+/*
+ * One decode step at position pos for every batch row (the single-state
+ * update of the full-sequence recurrence, then dilated attention over the
+ * anchor-only cache; abstract: the cache is D times smaller).
+ *   s <- g*s + (1-g)*x  (fp32, x in {k, v});  hat = ST(s);
+ *   o = attention of q over anchors a < floor(max(0, pos-W)/D) from Kc/Vc,
+ *       the window positions max(0,pos-W) .. pos-1 from the ring, and hat.
+ * Then, after every read: state_k/state_v <- s; ring slot pos mod W <- hat
+ * (if W > 0); anchor row pos / D <- hat (if pos mod D = D-1).
+ * Reads  q, k, v, g [B, H, hd] ST.  Updates state_k, state_v [B, H, hd] fp32,
+ * Kc, Vc, k_ring, v_ring (layouts above).  Writes o [B, H, hd] ST.
+ * The cache must hold positions 0 .. pos-1 (rat_scan_prefill of T = pos,
+ * or earlier decode steps).  Requires 0 <= pos < T_cap, else
+ * RAT_ERR_CAPACITY.  num_splits: split-K factor (0 = automatic).
+ * workspace: rat_decode_workspace_bytes bytes (NULL if that is 0).
+ */
+int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D,
+                    const int32_t* W, float scale, int64_t pos, int64_t T_cap,
+                    const void* q, const void* k, const void* v, const void* g,
+                    float* state_k, float* state_v, void* Kc, void* Vc,
+                    void* k_ring, void* v_ring, void* o, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAT_H_ */

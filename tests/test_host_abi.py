@@ -1,0 +1,183 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+Every call here fails validation, or has an empty batch, before anything is
+enqueued, so only host code runs.  Fake device pointers are used only in
+calls that are rejected by validation.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from dilated_sparse_attention_rat_amd import binding as rb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rat.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rb.LIB_PATH):
+        from dilated_sparse_attention_rat_amd import build
+        build.build_library(verbose=False)
+    return rb.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rat_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(rb.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", rb.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in _declared():
+        assert name in syms, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert "gfx950" in rb.rat_version()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert rb.rat_status_string(code) not in ("", "unknown status")
+    assert rb.rat_status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_anchor_rows_match_oracle(L, seed):
+    rng = np.random.default_rng(seed)
+    H = int(rng.integers(1, 40))
+    D = rng.integers(1, 70, size=H).astype(np.int32)
+    T_cap = int(rng.integers(0, 100000))
+    R, off = rb.rat_anchor_rows(H, T_cap, D)
+    R2, off2 = oracle.anchor_offsets(H, T_cap, D)
+    assert R == R2
+    np.testing.assert_array_equal(off, off2)
+
+
+def test_ring_rows(L):
+    W = np.array([0, 5, 128, 0, 7], dtype=np.int32)
+    S, off = rb.rat_ring_rows(5, W)
+    assert S == 140
+    assert list(off) == [0, 0, 5, 133, 133, 140]
+
+
+def test_layout_functions_reject_bad_tables(L):
+    D = np.array([4, 0], dtype=np.int32)
+    assert L.rat_anchor_rows(2, 100, D.ctypes.data_as(ctypes.c_void_p), None) == rb.RAT_ERR_INVALID_ARG
+    W = np.array([4, -1], dtype=np.int32)
+    assert L.rat_ring_rows(2, W.ctypes.data_as(ctypes.c_void_p), None) == rb.RAT_ERR_INVALID_ARG
+    assert L.rat_anchor_rows(-1, 100, None, None) == rb.RAT_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(L):
+    assert rb.rat_scan_workspace_bytes(4, 16, 4096, 128) > 0
+    assert rb.rat_scan_workspace_bytes(1, 1, 0, 64) > 0
+    a = rb.rat_scan_workspace_bytes(1, 16, 16384, 128)
+    b = rb.rat_scan_workspace_bytes(2, 16, 16384, 128)
+    assert b > a
+    assert L.rat_scan_workspace_bytes(1, 1, 10, 96) == rb.RAT_ERR_UNSUPPORTED
+    D = np.full(32, 64, np.int32)
+    W = np.full(32, 128, np.int32)
+    assert rb.rat_decode_workspace_bytes(64, 32, 128, 33024, D, W) == 0  # one split
+    assert rb.rat_decode_workspace_bytes(1, 2, 128, 33024, D[:2], W[:2]) > 0
+    assert rb.rat_decode_workspace_bytes(1, 2, 128, 1000, D[:2], W[:2], num_splits=4) == 2 * 4 * 130 * 4
+
+
+# -------------------------------------------------------------------------
+# validation paths of the three compute entry points (rejected before any
+# launch; fake pointers are never dereferenced)
+# -------------------------------------------------------------------------
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced
+
+
+def _p(x=FAKE):
+    return ctypes.c_void_p(x)
+
+
+def _tables(H, D=4, W=0):
+    d = np.full(H, D, np.int32)
+    w = np.full(H, W, np.int32)
+    return d, w, d.ctypes.data_as(ctypes.c_void_p), w.ctypes.data_as(ctypes.c_void_p)
+
+
+def _scan(L, dtype=0, B=1, H=2, T=16, hd=64, D=4, W=0, T_cap=16, kptr=FAKE, ws=FAKE,
+          ws_bytes=1 << 30, state=FAKE, hk=FAKE, hv=FAKE, ring=FAKE):
+    d, w, dp, wp = _tables(H, D, W)
+    return L.rat_scan_prefill(dtype, B, H, T, hd, dp, wp, T_cap, _p(kptr), _p(), _p(), _p(hk),
+                              _p(hv), _p(), _p(), _p(ring), _p(ring), _p(state), _p(state),
+                              _p(ws), ws_bytes, None)
+
+
+def test_scan_validation(L):
+    assert _scan(L, dtype=7) == rb.RAT_ERR_UNSUPPORTED
+    assert _scan(L, hd=96) == rb.RAT_ERR_UNSUPPORTED
+    assert _scan(L, D=0) == rb.RAT_ERR_INVALID_ARG
+    assert _scan(L, W=-3) == rb.RAT_ERR_INVALID_ARG
+    assert _scan(L, T=17, T_cap=16) == rb.RAT_ERR_CAPACITY
+    assert _scan(L, kptr=FAKE + 8) == rb.RAT_ERR_INVALID_ARG       # misaligned
+    assert _scan(L, kptr=0) == rb.RAT_ERR_INVALID_ARG              # null input
+    assert _scan(L, state=0) == rb.RAT_ERR_INVALID_ARG
+    assert _scan(L, hk=0) == rb.RAT_ERR_INVALID_ARG                # hk without hv
+    assert _scan(L, W=4, ring=0) == rb.RAT_ERR_INVALID_ARG         # window needs a ring
+    assert _scan(L, ws=0) == rb.RAT_ERR_WORKSPACE
+    assert _scan(L, ws_bytes=64) == rb.RAT_ERR_WORKSPACE
+    assert _scan(L, H=129) == rb.RAT_ERR_UNSUPPORTED
+    assert _scan(L, B=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _scan(L, B=0) == rb.RAT_OK                              # empty batch: no-op
+
+
+def _attn(L, dtype=0, B=1, H=2, T=16, hd=64, D=4, W=0, T_cap=16, scale=0.0, q=FAKE, lse=0):
+    d, w, dp, wp = _tables(H, D, W)
+    return L.rat_dilated_attn_prefill(dtype, B, H, T, hd, dp, wp, scale, T_cap, _p(q), _p(), _p(),
+                                      _p(), _p(), _p(), _p(lse) if lse else None, None)
+
+
+def test_attention_validation(L):
+    assert _attn(L, dtype=3) == rb.RAT_ERR_UNSUPPORTED
+    assert _attn(L, hd=32) == rb.RAT_ERR_UNSUPPORTED
+    assert _attn(L, D=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _attn(L, T=20, T_cap=16) == rb.RAT_ERR_CAPACITY
+    assert _attn(L, q=0) == rb.RAT_ERR_INVALID_ARG
+    assert _attn(L, q=FAKE + 4) == rb.RAT_ERR_INVALID_ARG
+    assert _attn(L, lse=FAKE + 4) == rb.RAT_ERR_INVALID_ARG
+    assert _attn(L, scale=float("inf")) == rb.RAT_ERR_INVALID_ARG
+    assert _attn(L, T=0) == rb.RAT_OK
+    assert _attn(L, B=0) == rb.RAT_OK
+
+
+def _dec(L, dtype=0, B=1, H=2, hd=64, D=4, W=0, pos=5, T_cap=16, splits=0, ws=0, ws_bytes=0,
+         q=FAKE):
+    d, w, dp, wp = _tables(H, D, W)
+    return L.rat_decode_step(dtype, B, H, hd, dp, wp, 0.0, pos, T_cap, _p(q), _p(), _p(), _p(),
+                             _p(), _p(), _p(), _p(), _p(), _p(), _p(), splits,
+                             _p(ws) if ws else None, ws_bytes, None)
+
+
+def test_decode_validation(L):
+    assert _dec(L, pos=16, T_cap=16) == rb.RAT_ERR_CAPACITY
+    assert _dec(L, pos=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _dec(L, dtype=9) == rb.RAT_ERR_UNSUPPORTED
+    assert _dec(L, hd=256) == rb.RAT_ERR_UNSUPPORTED
+    assert _dec(L, q=0) == rb.RAT_ERR_INVALID_ARG
+    assert _dec(L, splits=4) == rb.RAT_ERR_WORKSPACE               # 4 splits need a workspace
+    assert _dec(L, splits=4, ws=FAKE, ws_bytes=16) == rb.RAT_ERR_WORKSPACE
+    assert _dec(L, splits=-2) == rb.RAT_ERR_INVALID_ARG
+    assert _dec(L, B=0) == rb.RAT_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(rb, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(rb, "_lib", None)
+    with pytest.raises(ImportError):
+        rb.lib()
