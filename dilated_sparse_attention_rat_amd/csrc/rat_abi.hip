@@ -53,15 +53,15 @@ int fill_tables(int H, int64_t T_cap, const int32_t* D, const int32_t* W, HeadTa
 
 int map_hip(int e) { return e == 0 ? RAT_OK : RAT_ERR_HIP; }
 
-// Workspace of the scan: header, then per tree node a tag (uint32) and an
-// aggregate (A, Bk, Bv: 3*hd fp32).  Level l has ceil(nchunk / 8^l) nodes per
+// Workspace of the scan: header, then per tree node an aggregate (A, Bk, Bv:
+// 3*hd values, each a 64-bit tagged word).  Level l has ceil(nchunk / 8^l) nodes per
 // sequence; levels are added until the top one has at most 8 nodes.
 struct ScanLayout {
   int64_t nchunk = 0, nticket = 0, entries = 0;
   int nlevels = 0;
   int nodes[kScanMaxLevels] = {};
   int64_t lbase[kScanMaxLevels] = {};
-  int64_t flags_off = 0, agg_off = 0, bytes = 0;
+  int64_t agg_off = 0, bytes = 0;
 };
 
 bool scan_layout(int B, int H, int64_t T, int hd, int dtype, ScanLayout& L) {
@@ -81,9 +81,8 @@ bool scan_layout(int B, int H, int64_t T, int hd, int dtype, ScanLayout& L) {
     n = (n + kScanRadix - 1) / kScanRadix;
   }
   auto up = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
-  L.flags_off = kScanHeaderBytes;
-  L.agg_off = up(L.flags_off + L.entries * 4);
-  L.bytes = up(L.agg_off + L.entries * 3 * hd * 4);
+  L.agg_off = kScanHeaderBytes;
+  L.bytes = up(L.agg_off + L.entries * 3 * hd * 8);
   return true;
 }
 
@@ -169,8 +168,7 @@ int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* 
     if (L.nticket > INT32_MAX) return RAT_ERR_UNSUPPORTED;
     char* ws = static_cast<char*>(workspace);
     p.hdr = reinterpret_cast<uint32_t*>(ws);
-    p.flags = reinterpret_cast<uint32_t*>(ws + L.flags_off);
-    p.agg = reinterpret_cast<float*>(ws + L.agg_off);
+    p.agg = reinterpret_cast<uint64_t*>(ws + L.agg_off);
     p.nticket = (int)L.nticket;
     p.nchunk = (int)L.nchunk;
     p.nlevels = L.nlevels;
@@ -183,8 +181,6 @@ int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* 
   p.H = H;
   p.T = (int)T;
   p.nseq = B * H;
-  p.nclass = 1;
-  while (p.nclass < kScanMaxClasses && p.nseq % (2 * p.nclass) == 0) p.nclass *= 2;
   p.k = k;
   p.v = v;
   p.g = g;
@@ -221,7 +217,16 @@ int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const i
   p.B = B;
   p.H = H;
   p.T = (int)T;
-  p.nq = (int)((T + kAttnBM - 1) / kAttnBM);
+  // 16-query blocks per wave: 2 when the average query attends to many keys
+  // (MFMA-bound: better operand reuse), else 1 (streaming-bound: fewer
+  // registers, more waves in flight)
+  double avg_keys = 0.0;
+  for (int h = 0; h < H; ++h)
+    avg_keys += (double)std::max<int64_t>(0, T - W[h]) / (2.0 * D[h]) + std::min<int64_t>(W[h], T);
+  avg_keys /= H;
+  p.qb = avg_keys >= 512.0 ? 2 : 1;
+  const int bm = 64 * p.qb;
+  p.nq = (int)((T + bm - 1) / bm);
   p.np = (p.nq + 1) / 2;
   if ((int64_t)H * B * p.np > INT32_MAX) return RAT_ERR_UNSUPPORTED;
   p.scale_log2 = sc * 1.4426950408889634f;
@@ -236,8 +241,8 @@ int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const i
   // the heaviest and the lightest query tile), so heavy heads start first
   const int bn = kAttnBN;
   auto tiles = [&](int h, int qt) -> int64_t {
-    const int64_t t0 = (int64_t)qt * kAttnBM;
-    const int64_t tl = std::min<int64_t>(t0 + kAttnBM - 1, T - 1);
+    const int64_t t0 = (int64_t)qt * bm;
+    const int64_t tl = std::min<int64_t>(t0 + bm - 1, T - 1);
     const int64_t na = std::max<int64_t>(0, tl - W[h]) / D[h];
     int64_t n = (na + bn - 1) / bn + 1;
     if (W[h] > 0) n += (tl - std::max<int64_t>(0, t0 - W[h]) + bn) / bn;

@@ -18,14 +18,10 @@ struct HeadTables {
   int32_t roff[kMaxHeads];  // first ring slot of the head
 };
 
-// Scan workspace header: one 4 KB slot per ticket class (so the classes'
-// atomics do not contend on one address).  Slot x holds
-//   [0] ticket: next chunk ticket of class x in the running launch
-//   [1] epoch:  launches of class x completed on this workspace
-//   [2] error:  != 0 if a wait for an aggregate timed out
-constexpr int kScanMaxClasses = 8;
-constexpr int kScanClassStride = 1024;  // uint32 words (4 KB)
-constexpr int64_t kScanHeaderBytes = (int64_t)kScanMaxClasses * kScanClassStride * 4;
+// Scan workspace header (32 KB): uint32 word 0 is the launch epoch, word 2
+// the error flag (a wait for an aggregate timed out), and 64 done counters
+// 256 bytes apart follow (see scan.hip).
+constexpr int64_t kScanHeaderBytes = 32 * 1024;
 
 constexpr int kScanRadix = 8;      // fan-in of the chunk-aggregate tree
 constexpr int kScanMaxLevels = 10;
@@ -35,7 +31,6 @@ struct ScanParams {
   int nseq;        // B * H
   int nchunk;      // chunks per sequence
   int nticket;     // nseq * nchunk (= grid size)
-  int nclass;      // ticket classes (a power of two dividing nseq, <= 8)
   int nlevels;     // levels of the aggregate tree (top level has <= radix nodes)
   int nodes[kScanMaxLevels];     // nodes per sequence at each level
   int64_t lbase[kScanMaxLevels]; // first entry of each level in flags/agg
@@ -52,14 +47,14 @@ struct ScanParams {
   void* vr;
   float* sk;
   float* sv;
-  uint32_t* hdr;    // kScanMaxClasses slots of kScanClassStride words
-  uint32_t* flags;  // [entries]: epoch tag of a published tree node
-  float* agg;       // [entries][3][hd]: A, Bk, Bv of the node's chunk range
+  uint32_t* hdr;    // workspace header (kScanHeaderBytes)
+  uint64_t* agg;    // [entries][3][hd]: (tag << 32 | fp32) of A, Bk, Bv
   HeadTables ht;
 };
 
 struct AttnParams {
   int B, H, T;
+  int qb;            // 16-query blocks per wave (1 or 2): tile = 64*qb queries
   int nq;            // query tiles per (b, h)
   int np;            // pair-blocks per (b, h)
   float scale_log2;  // scale * log2(e)
@@ -107,7 +102,6 @@ constexpr int kScanThreads = 256;
 constexpr int kScanRowsPerThread = 4;
 int scan_rows_per_chunk(int dtype, int hd);
 
-constexpr int kAttnBM = 128;   // queries per tile (4 waves x 32)
 constexpr int kAttnBN = 64;    // keys per LDS tile
 constexpr int kDecodeThreads = 256;
 

@@ -22,12 +22,20 @@
 //    of at most 7 nodes per level that precede it.  No chunk waits on a
 //    serial chain, and the composition order is fixed, so the scan is
 //    bitwise deterministic run to run;
-//  * chunks are handed out by an atomic ticket in sequence-interleaved
-//    order, so every node a block waits on belongs to a block already
-//    running (no deadlock); every wait is bounded;
+//  * the kernel is persistent and launched cooperatively (all workgroups
+//    resident); chunks are assigned statically in chunk-major order, so
+//    every node a workgroup waits on belongs to a smaller ticket of a
+//    running workgroup (no deadlock) and no atomic ticket counter is needed
+//    (same-address device-scope atomics serialise at about 10 ns each);
+//    every wait is bounded;
 //  * the second pass re-runs the sequential recurrence from the chunk's
 //    carry-in on the registers and streams hk/hv, anchor rows, ring slots
 //    and the final fp32 state out with 16-byte stores.
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "rat_device.h"
 
 namespace rat {
@@ -51,6 +59,17 @@ __device__ __forceinline__ void st_coherent_f32(float* p, float v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workspace header words (uint32): the launch epoch, the error flag, and the
+// done counters that let the last block advance the epoch.  Counters sit
+// 256 bytes apart so their atomics do not queue on one address.
+constexpr int kEpochWord = 0;
+constexpr int kErrorWord = 2;
+constexpr int kTopWord = 32;
+constexpr int kDoneBase = 64;
+constexpr int kDoneStride = 64;
+constexpr int kDoneSlots = 64;
+static_assert(kDoneBase + kDoneSlots * kDoneStride <= kScanHeaderBytes / 4, "header");
+
 constexpr int kScanRadixLog2 = 3;
 static_assert((1 << kScanRadixLog2) == kScanRadix, "radix");
 
@@ -63,117 +82,123 @@ static_assert((1 << kScanRadixLog2) == kScanRadix, "radix");
 // of the XCD on every call).
 __device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Publish one aggregate-tree node: data with coherent stores, then the tag.
-template <int HD, int CPL>
-__device__ __forceinline__ void publish_node(const ScanParams& p, int64_t e, const float* A,
-                                             const float* Bk, const float* Bv, uint32_t tag,
-                                             int lane) {
-  float* d = p.agg + e * 3 * HD;
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
-    st_coherent_f32(d + c, A[j]);
-    st_coherent_f32(d + HD + c, Bk[j]);
-    st_coherent_f32(d + 2 * HD + c, Bv[j]);
-  }
-  vm_drain();
-  if (lane == 0) st_relaxed_u32(p.flags + e, tag);
+// The hd channels are independent; the tree works on 64-channel halves, one
+// wave per half with one channel per lane.  Every published value is a 64-bit
+// word (launch tag << 32 | fp32 bits) written and read with single-copy
+// atomic 64-bit accesses, so a reader that sees the current tag in a word
+// also sees its value: no separate flag, no store drain, one round trip.
+__device__ __forceinline__ void st_tagged(uint64_t* p, uint32_t tag, float v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publish one half of a tree node (A, Bk, Bv of this lane's channel).
+template <int HD>
+__device__ __forceinline__ void publish_node(const ScanParams& p, int64_t e, int half, float A,
+                                             float Bk, float Bv, uint32_t tag, int lane) {
+  uint64_t* d = p.agg + e * 3 * HD + 64 * half + lane;
+  st_tagged(d, tag, A);
+  st_tagged(d + HD, tag, Bk);
+  st_tagged(d + 2 * HD, tag, Bv);
 }
 
 // Compose the n (< radix) consecutive nodes [e0, e0 + n), in order, after
-// the running map (A, Bk, Bv).  Lane j polls node e0 + j; every wait is
-// bounded.  All n aggregates are then loaded at once.
-template <int HD, int CPL>
-__device__ __forceinline__ void fold_nodes(const ScanParams& p, int64_t e0, int n, float* A,
-                                           float* Bk, float* Bv, uint32_t tag, int lane) {
+// the running map (A, Bk, Bv) of one channel.  All 3n words are loaded at
+// once and re-loaded until every tag in the wave is current; every wait is
+// bounded.
+template <int HD>
+__device__ __forceinline__ void fold_nodes(const ScanParams& p, int64_t e0, int n, int half,
+                                           float& A, float& Bk, float& Bv, uint32_t tag,
+                                           int lane) {
   if (n <= 0) return;
-  bool ready = lane >= n;
+  uint64_t w[kScanRadix - 1][3];
   uint32_t spins = 0;
   while (true) {
-    if (!ready) ready = ld_acquire_u32(p.flags + e0 + lane) == tag;
-    if (__all(ready)) break;
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < kScanRadix - 1; ++i) {
+      if (i < n) {
+        const uint64_t* d = p.agg + (e0 + i) * 3 * HD + 64 * half + lane;
+        w[i][0] = ld_tagged(d);
+        w[i][1] = ld_tagged(d + HD);
+        w[i][2] = ld_tagged(d + 2 * HD);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kScanRadix - 1; ++i)
+      if (i < n)
+        ok = ok && (uint32_t)(w[i][0] >> 32) == tag && (uint32_t)(w[i][1] >> 32) == tag &&
+             (uint32_t)(w[i][2] >> 32) == tag;
+    if (__all(ok)) break;
     if (++spins > kSpinLimit) {
-      if (lane == 0) st_relaxed_u32(p.hdr + 2, 1u);
+      if (lane == 0) st_relaxed_u32(p.hdr + kErrorWord, 1u);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  vm_drain();
-  float a[kScanRadix - 1][CPL], bk[kScanRadix - 1][CPL], bv[kScanRadix - 1][CPL];
 #pragma unroll
   for (int i = 0; i < kScanRadix - 1; ++i) {
     if (i < n) {
-      const float* d = p.agg + (e0 + i) * 3 * HD;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
-        a[i][j] = ld_coherent_f32(d + c);
-        bk[i][j] = ld_coherent_f32(d + HD + c);
-        bv[i][j] = ld_coherent_f32(d + 2 * HD + c);
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kScanRadix - 1; ++i) {
-    if (i < n) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        Bk[j] = a[i][j] * Bk[j] + bk[i][j];
-        Bv[j] = a[i][j] * Bv[j] + bv[i][j];
-        A[j] = A[j] * a[i][j];
-      }
+      const float a = __uint_as_float((uint32_t)w[i][0]);
+      Bk = a * Bk + __uint_as_float((uint32_t)w[i][1]);
+      Bv = a * Bv + __uint_as_float((uint32_t)w[i][2]);
+      A = A * a;
     }
   }
 }
 
 template <typename ST, int HD, int S>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(const ScanParams p) {
+struct ChunkRows {
+  u32x4 k[S], v[S], g[S];
+};
+
+// Issue the loads of this lane's S rows of chunk `ticket` (kept in registers
+// for both passes).  The loads are unconditional (rows at or past T re-read
+// row T-1 and are ignored) so the compiler can count outstanding loads
+// exactly and wait only for the ones it needs.
+template <typename ST, int HD, int S>
+__device__ __forceinline__ void load_rows(const ScanParams& p, uint32_t ticket,
+                                          ChunkRows<ST, HD, S>& rw) {
+  constexpr int VEC = StTraits<ST>::VEC;
+  constexpr int LPR = HD / VEC;
+  constexpr int RG = kScanThreads / LPR;
+  constexpr int LC = RG * S;
+  const int tid = threadIdx.x;
+  const int chunk = (int)(ticket / (uint32_t)p.nseq);
+  const int seq = (int)(ticket % (uint32_t)p.nseq);
+  const int r = tid / LPR;
+  const int c0 = (tid - r * LPR) * VEC;
+  const int tbase = chunk * LC + r * S;
+  const int64_t seq_base = (int64_t)seq * p.T * HD;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int t = min(tbase + s, p.T - 1);
+    const int64_t off = seq_base + (int64_t)t * HD + c0;
+    rw.k[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.k) + off);
+    rw.v[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.v) + off);
+    rw.g[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.g) + off);
+  }
+}
+
+// One chunk: pass 1, tree publication and carry, then pass 2.  `between`
+// runs after the carry is known and before pass 2: the caller issues the
+// next chunk's loads there, so that no tree load waits behind them (vector
+// memory counters complete in order) while pass 2 still overlaps them.
+template <typename ST, int HD, int S, typename F>
+__device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket, uint32_t tag,
+                                           const ChunkRows<ST, HD, S>& rw, float (*s_A)[HD],
+                                           float (*s_Bk)[HD], float (*s_Bv)[HD], float* s_hk,
+                                           float* s_hv, F&& between) {
   constexpr int VEC = StTraits<ST>::VEC;
   constexpr int LPR = HD / VEC;           // lanes per row
   constexpr int RG = kScanThreads / LPR;  // row-groups per chunk
   constexpr int LC = RG * S;              // rows per chunk
-  constexpr int CPL = HD / 64;            // channels per lane in the carry wave
-  static_assert(HD % 64 == 0 && LPR <= 64, "layout");
-
-  __shared__ float s_A[RG][HD];
-  __shared__ float s_Bk[RG][HD];
-  __shared__ float s_Bv[RG][HD];
-  __shared__ float s_hk[HD];
-  __shared__ float s_hv[HD];
-  __shared__ uint32_t s_ticket, s_tag;
-
-  // Tickets: blocks are split into nclass classes by blockIdx; class x owns
-  // the sequences s = x (mod nclass) and hands out their chunks in
-  // chunk-major order through its own counter.  A chunk only waits on
-  // earlier chunks of its own sequence, i.e. on smaller tickets of its own
-  // class, which blocks already running hold: no deadlock.  Every block reads
-  // the class epoch before taking its ticket, so the block that takes the
-  // class's last ticket can reset the counter and advance the epoch (the
-  // next launch's tag) without any further atomic.
   const int tid = threadIdx.x;
-  const int cls = (int)(blockIdx.x % (unsigned)p.nclass);
-  uint32_t* slot = p.hdr + cls * kScanClassStride;
-  const uint32_t per_class = (uint32_t)(p.nticket / p.nclass);
-  if (tid == 0) {
-    const uint32_t ep = ld_acquire_u32(slot + 1);
-    vm_drain();
-    const uint32_t tk = __hip_atomic_fetch_add(slot, 1u, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-    if (tk == per_class - 1) {
-      st_relaxed_u32(slot, 0u);
-      st_relaxed_u32(slot + 1, ep + 1u);
-    }
-    s_ticket = tk;
-    s_tag = (ep % 0x3FFFFFFFu) + 1u;
-  }
-  __syncthreads();
-  const uint32_t ticket = s_ticket;
-  const uint32_t tag = s_tag;
-  const bool valid_ticket = ticket < per_class;
-  const int nseq_c = p.nseq / p.nclass;  // sequences of this class
-
-  const int chunk = valid_ticket ? (int)(ticket / (uint32_t)nseq_c) : 0;
-  const int seq = valid_ticket ? cls + p.nclass * (int)(ticket % (uint32_t)nseq_c) : 0;
+  const int chunk = (int)(ticket / (uint32_t)p.nseq);
+  const int seq = (int)(ticket % (uint32_t)p.nseq);
   const int b = seq / p.H;
   const int h = seq - b * p.H;
   const int T = p.T;
@@ -182,23 +207,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const ScanParams p) 
   const int c0 = cl * VEC;
   const int tbase = chunk * LC + r * S;
   const int64_t seq_base = (int64_t)seq * T * HD;
-
-  const ST* __restrict__ kp = reinterpret_cast<const ST*>(p.k);
-  const ST* __restrict__ vp = reinterpret_cast<const ST*>(p.v);
-  const ST* __restrict__ gp = reinterpret_cast<const ST*>(p.g);
-
-  // ---- issue the loads of this lane's S rows (kept for both passes) ------
-  u32x4 rk[S], rv[S], rg[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int t = tbase + s;
-    if (valid_ticket && t < T) {
-      const int64_t off = seq_base + (int64_t)t * HD + c0;
-      rk[s] = ld_raw16_nt(kp + off);
-      rv[s] = ld_raw16_nt(vp + off);
-      rg[s] = ld_raw16_nt(gp + off);
-    }
-  }
+  const u32x4* rk = rw.k;
+  const u32x4* rv = rw.v;
+  const u32x4* rg = rw.g;
 
   // ---- pass 1: affine map of this lane's rows ----------------------------
   float A[VEC], Bk[VEC], Bv[VEC];
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const ScanParams p) 
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int t = tbase + s;
-    if (valid_ticket && t < T) {
+    if (t < T) {
       float gf[VEC], kf[VEC], vf[VEC];
       unpack16(rg[s], gf, (ST*)nullptr);
       unpack16(rk[s], kf, (ST*)nullptr);
@@ -232,13 +243,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const ScanParams p) 
   }
   __syncthreads();
 
-  // ---- wave 0: row-group scan, publish the chunk and completed parents ---
-  if (tid < 64) {
-    const int lane = tid;
-    float cA[CPL], cBk[CPL], cBv[CPL];  // chunk aggregate per channel
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
+  // ---- waves 0..NH-1: row-group scan of half j, publish chunk and parents -
+  // ---- waves 2..2+NH-1, concurrently: carry-in of half j -------------------
+  // Publication never waits on a carry, so no chain forms along the
+  // sequence: every tree node depends on input data only.  The carry is the
+  // in-order composition, top tree level first, of the complete nodes that
+  // precede this chunk (at most radix-1 per level): a fixed order, so the
+  // result is bitwise deterministic.
+  {
+    constexpr int NH = HD / 64;  // channel halves
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    if (wave < NH) {
+      const int half = wave;
+      const int c = 64 * half + lane;
       float ra = 1.f, rbk = 0.f, rbv = 0.f;
       for (int rr = 0; rr < RG; ++rr) {
         const float a = s_A[rr][c], bk = s_Bk[rr][c], bv = s_Bv[rr][c];
@@ -249,74 +267,40 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const ScanParams p) 
         rbv = a * rbv + bv;
         ra = ra * a;
       }
-      cA[j] = ra;
-      cBk[j] = rbk;
-      cBv[j] = rbv;
-    }
-    if (valid_ticket) {
       // A node of level l+1 is the in-order composition of its radix
       // children; the chunk that owns the last child computes and publishes
       // it.
       int64_t node = chunk;
       for (int lv = 0; lv < p.nlevels; ++lv) {
         const int64_t lvl0 = p.lbase[lv] + (int64_t)seq * p.nodes[lv];
-        publish_node<HD, CPL>(p, lvl0 + node, cA, cBk, cBv, tag, lane);
+        publish_node<HD>(p, lvl0 + node, half, ra, rbk, rbv, tag, lane);
         if (lv + 1 >= p.nlevels || (node % kScanRadix) != kScanRadix - 1) break;
-        float fA[CPL], fBk[CPL], fBv[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          fA[j] = 1.f;
-          fBk[j] = 0.f;
-          fBv[j] = 0.f;
-        }
-        fold_nodes<HD, CPL>(p, lvl0 + node - (kScanRadix - 1), kScanRadix - 1, fA, fBk, fBv, tag,
-                            lane);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {  // then this node itself
-          fBk[j] = cA[j] * fBk[j] + cBk[j];
-          fBv[j] = cA[j] * fBv[j] + cBv[j];
-          fA[j] = fA[j] * cA[j];
-          cA[j] = fA[j];
-          cBk[j] = fBk[j];
-          cBv[j] = fBv[j];
-        }
+        float fA = 1.f, fBk = 0.f, fBv = 0.f;
+        fold_nodes<HD>(p, lvl0 + node - (kScanRadix - 1), kScanRadix - 1, half, fA, fBk, fBv,
+                       tag, lane);
+        rbk = ra * fBk + rbk;  // then this node itself
+        rbv = ra * fBv + rbv;
+        ra = fA * ra;
         node /= kScanRadix;
       }
-    }
-  }
-
-  // ---- wave 1, concurrently: carry-in of this chunk ------------------------
-  // Compose, top tree level first, the complete nodes that precede this
-  // chunk (at most radix-1 per level).  The order is fixed, so the result is
-  // bitwise deterministic.  Publication (wave 0) never waits on a carry, so
-  // no chain forms along the sequence: every node depends on input data only.
-  if (tid >= 64 && tid < 128) {
-    const int lane = tid - 64;
-    float one[CPL], hin_k[CPL], hin_v[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      one[j] = 1.f;
-      hin_k[j] = 0.f;
-      hin_v[j] = 0.f;
-    }
-    if (valid_ticket) {
+    } else if (wave >= 2 && wave < 2 + NH) {
+      const int half = wave - 2;
+      float one = 1.f, hin_k = 0.f, hin_v = 0.f;
       for (int lv = p.nlevels - 1; lv >= 0; --lv) {
         const int64_t nd = (int64_t)chunk >> (kScanRadixLog2 * lv);
         const int64_t first = nd & ~(int64_t)(kScanRadix - 1);
         const int64_t lvl0 = p.lbase[lv] + (int64_t)seq * p.nodes[lv];
-        fold_nodes<HD, CPL>(p, lvl0 + first, (int)(nd - first), one, hin_k, hin_v, tag, lane);
+        fold_nodes<HD>(p, lvl0 + first, (int)(nd - first), half, one, hin_k, hin_v, tag, lane);
       }
-    }
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      s_hk[lane + 64 * j] = hin_k[j];
-      s_hv[lane + 64 * j] = hin_v[j];
+      s_hk[64 * half + lane] = hin_k;
+      s_hv[64 * half + lane] = hin_v;
     }
   }
   __syncthreads();
+  between();
 
   // ---- pass 2: sequential recurrence from the carry-in, stream outputs ---
-  if (valid_ticket) {
+  {
     float sk[VEC], sv[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
@@ -384,6 +368,74 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const ScanParams p) 
 
 }
 
+// Persistent kernel: the grid is sized to the number of workgroups that can
+// be resident at once and launched cooperatively, so every workgroup runs
+// concurrently.  Workgroup w processes tickets w, w + G, w + 2G, ... in
+// order; ticket t is chunk t / nseq of sequence t % nseq.  A chunk waits only
+// on nodes of earlier chunks of its own sequence, i.e. on smaller tickets, so
+// the smallest unfinished ticket can always proceed (no deadlock), and no
+// ticket counter (atomic) is needed.  Every workgroup reads the epoch first;
+// the last one to finish advances it, so the epoch is this launch's tag.
+template <typename ST, int HD, int S>
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void scan_kernel(const ScanParams p) {
+  constexpr int VEC = StTraits<ST>::VEC;
+  constexpr int LPR = HD / VEC;
+  constexpr int RG = kScanThreads / LPR;
+  static_assert(HD % 64 == 0 && LPR <= 64, "layout");
+  __shared__ float s_A[RG][HD];
+  __shared__ float s_Bk[RG][HD];
+  __shared__ float s_Bv[RG][HD];
+  __shared__ float s_hk[HD];
+  __shared__ float s_hv[HD];
+  __shared__ uint32_t s_epoch;
+
+  const int tid = threadIdx.x;
+  if (tid == 0) s_epoch = ld_acquire_u32(p.hdr + kEpochWord);
+  __syncthreads();
+  const uint32_t epoch = s_epoch;
+  const uint32_t tag = (epoch % 0x3FFFFFFFu) + 1u;
+  const uint32_t G = gridDim.x;
+
+  // Two register buffers: the rows of the next chunk are loaded while the
+  // current chunk streams its outputs.
+  const uint32_t n = (uint32_t)p.nticket;
+  ChunkRows<ST, HD, S> ra, rb;
+  uint32_t ticket = blockIdx.x;
+  if (ticket < n) load_rows<ST, HD, S>(p, ticket, ra);
+  while (ticket < n) {
+    const uint32_t t1 = ticket + G;
+    // (prefetches are unconditional -- past the end they re-load the last
+    // ticket and are ignored -- so outstanding loads are counted exactly)
+    scan_chunk<ST, HD, S>(p, ticket, tag, ra, s_A, s_Bk, s_Bv, s_hk, s_hv,
+                          [&] { load_rows<ST, HD, S>(p, min(t1, n - 1), rb); });
+    __syncthreads();  // LDS is reused by the next chunk
+    if (t1 >= n) break;
+    const uint32_t t2 = t1 + G;
+    scan_chunk<ST, HD, S>(p, t1, tag, rb, s_A, s_Bk, s_Bv, s_hk, s_hv,
+                          [&] { load_rows<ST, HD, S>(p, min(t2, n - 1), ra); });
+    __syncthreads();
+    ticket = t2;
+  }
+
+  // retire: two-level done count; the last workgroup advances the epoch
+  if (tid == 0) {
+    const uint32_t slot = blockIdx.x % kDoneSlots;
+    const uint32_t in_slot = (G - 1 - slot) / kDoneSlots + 1;
+    const uint32_t used = G < (uint32_t)kDoneSlots ? G : (uint32_t)kDoneSlots;
+    vm_drain();
+    uint32_t* ctr = p.hdr + kDoneBase + slot * kDoneStride;
+    if (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_slot - 1) {
+      st_relaxed_u32(ctr, 0u);
+      uint32_t* top = p.hdr + kTopWord;
+      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == used - 1) {
+        st_relaxed_u32(top, 0u);
+        st_relaxed_u32(p.hdr + kEpochWord, epoch + 1u);
+      }
+    }
+  }
+}
+
 // T = 0: the state is h_{-1} = 0
 __global__ void zero_state_kernel(float* sk, float* sv, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -391,6 +443,25 @@ __global__ void zero_state_kernel(float* sk, float* sv, int64_t n) {
     sk[i] = 0.f;
     sv[i] = 0.f;
   }
+}
+
+// Largest grid whose workgroups can all be resident at once (cached per
+// device and kernel; the cache is the library's only mutable state, written
+// once under a lock).
+int coop_grid_limit(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, kernel});
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  const int lim = per_cu * cus;
+  cache[{dev, kernel}] = lim;
+  return lim;
 }
 
 template <typename ST, int HD>
@@ -402,9 +473,13 @@ int launch_scan_t(const ScanParams& p, hipStream_t st) {
                        p.sk, p.sv, n);
     return (int)hipGetLastError();
   }
-  hipLaunchKernelGGL((scan_kernel<ST, HD, kScanRowsPerThread>), dim3(p.nticket),
-                     dim3(kScanThreads), 0, st, p);
-  return (int)hipGetLastError();
+  const void* kern = reinterpret_cast<const void*>(&scan_kernel<ST, HD, kScanRowsPerThread>);
+  const int lim = coop_grid_limit(kern, kScanThreads);
+  if (lim <= 0) return (int)hipErrorInvalidValue;
+  const unsigned grid = (unsigned)std::min<int64_t>(p.nticket, lim);
+  ScanParams pp = p;
+  void* args[] = {&pp};
+  return (int)hipLaunchCooperativeKernel(kern, dim3(grid), dim3(kScanThreads), args, 0, st);
 }
 
 }  // namespace
