@@ -1,7 +1,7 @@
 """Benchmark of the RAT+ hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
-                    [--no-cpu-baseline] [--no-decode-workload]
+                    [--no-cpu-baseline] [--no-decode-workload] [--calibration-copy MIB]
 
 A step is one pass of the whole hot path over one batch of the prefill
 workload (default: the 1.5B-like shape B=4, H=16, hd=128, T=4096, D=16, no
@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--no-decode-workload", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="before the steps, run three plain elementwise copies of MIB MiB "
+                         "(reads MIB, writes MIB): the known-size reference that scales "
+                         "hardware byte counters (FETCH_SIZE / WRITE_SIZE) to bytes")
     return ap.parse_args()
 
 
@@ -192,6 +196,15 @@ def main():
                             workspace=s["dws"])
         if ev is not None:
             ev[3].record(stream)
+
+    if args.calibration_copy > 0:
+        n = args.calibration_copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
 
     for i in range(args.warmup):
         step(sets[i % 2])

@@ -22,12 +22,13 @@
 //    of at most 7 nodes per level that precede it.  No chunk waits on a
 //    serial chain, and the composition order is fixed, so the scan is
 //    bitwise deterministic run to run;
-//  * the kernel is persistent and launched cooperatively (all workgroups
-//    resident); chunks are assigned statically in chunk-major order, so
-//    every node a workgroup waits on belongs to a smaller ticket of a
-//    running workgroup (no deadlock) and no atomic ticket counter is needed
-//    (same-address device-scope atomics serialise at about 10 ns each);
-//    every wait is bounded;
+//  * the kernel is persistent: its grid is at most the number of workgroups
+//    the device holds at once, so all of them are resident together;
+//    chunks are assigned statically in chunk-major order, so every node a
+//    workgroup waits on belongs to a smaller ticket of a resident workgroup
+//    (no deadlock) and no atomic ticket counter is needed (same-address
+//    device-scope atomics serialise at about 10 ns each); every wait is
+//    bounded;
 //  * the second pass re-runs the sequential recurrence from the chunk's
 //    carry-in on the registers and streams hk/hv, anchor rows, ring slots
 //    and the final fp32 state out with 16-byte stores.
@@ -369,8 +370,7 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
 }
 
 // Persistent kernel: the grid is sized to the number of workgroups that can
-// be resident at once and launched cooperatively, so every workgroup runs
-// concurrently.  Workgroup w processes tickets w, w + G, w + 2G, ... in
+// be resident at once, so every workgroup runs concurrently.  Workgroup w processes tickets w, w + G, w + 2G, ... in
 // order; ticket t is chunk t / nseq of sequence t % nseq.  A chunk waits only
 // on nodes of earlier chunks of its own sequence, i.e. on smaller tickets, so
 // the smallest unfinished ticket can always proceed (no deadlock), and no
@@ -476,10 +476,16 @@ int launch_scan_t(const ScanParams& p, hipStream_t st) {
   const void* kern = reinterpret_cast<const void*>(&scan_kernel<ST, HD, kScanRowsPerThread>);
   const int lim = coop_grid_limit(kern, kScanThreads);
   if (lim <= 0) return (int)hipErrorInvalidValue;
+  // A plain launch: with the grid within the device's capacity every
+  // workgroup is placed as soon as the stream reaches the kernel.  (A
+  // cooperative launch gives the same residency as a formal guarantee but
+  // costs about 20 us of queue drain per launch.)  If other streams hold
+  // CUs, the late workgroups start when those finish; a wait that outlasts
+  // the spin bound is reported in the workspace error word, never a hang.
   const unsigned grid = (unsigned)std::min<int64_t>(p.nticket, lim);
-  ScanParams pp = p;
-  void* args[] = {&pp};
-  return (int)hipLaunchCooperativeKernel(kern, dim3(grid), dim3(kScanThreads), args, 0, st);
+  hipLaunchKernelGGL((scan_kernel<ST, HD, kScanRowsPerThread>), dim3(grid), dim3(kScanThreads), 0,
+                     st, p);
+  return (int)hipGetLastError();
 }
 
 }  // namespace
