@@ -95,11 +95,15 @@ int64_t rat_ring_rows(int H, const int32_t* W, int64_t* offsets_out);
  * zero-filled once before its first use; every call leaves it ready for the
  * next call (after a call that returned an error, or a launch that was
  * aborted, zero-fill it again).  One workspace must not be used by two calls
- * that can run at the same time.  The first 32 KB are eight 4 KB counter
- * slots; uint32 word 2 of the workspace is an error word: != 0 after a call
- * means a chunk gave up waiting for a predecessor's aggregate (results of
- * that call are invalid).  Pure host function; returns bytes (> 0) or a
- * negative code.
+ * that can run at the same time.  The first 32 KB are a header (uint32
+ * word 0: launch epoch; word 2: error word; then completion counters), the
+ * rest holds the tagged chunk aggregates.  The error word is != 0 after a
+ * call in which a chunk gave up waiting for a predecessor's aggregate (the
+ * results of that call are invalid).  The scan kernel is persistent: its
+ * grid never exceeds what the device holds at once, and with the device to
+ * itself every workgroup is resident immediately; if other streams keep CUs
+ * busy past the (bounded) wait, the call reports it here instead of
+ * hanging.  Pure host function; returns bytes (> 0) or a negative code.
  */
 int64_t rat_scan_workspace_bytes(int B, int H, int64_t T, int hd);
 
