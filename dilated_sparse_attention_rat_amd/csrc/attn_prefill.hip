@@ -365,12 +365,11 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   }
 }
 
-// Occupancy target: with QB = 1, 2 waves per SIMD (two workgroups per CU) so
-// one workgroup's MFMAs overlap the other's staging and softmax; with QB = 2
-// the full register file (1 wave per SIMD, no spills), the prefetch pipeline
-// hiding the global latency.
+// Occupancy target: 2 waves per SIMD (two workgroups per CU) for both QB, so
+// one workgroup's MFMAs overlap the other's staging and softmax (QB = 2 fits
+// the resulting 256-register budget without spills).
 template <typename ST, int HD, int QB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_kernel(const AttnParams p) {
   using C = AttnCfg<ST, HD, QB>;
   __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::KSTR];
