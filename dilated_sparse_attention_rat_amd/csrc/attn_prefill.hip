@@ -25,9 +25,12 @@
 //    of O^T += V^T P^T (keys permuted identically on both operands);
 //  * the staircase mask of the anchors (a < floor(max(0,t-W)/D)) and the band
 //    mask of the window are applied only on the tiles that need them;
-//  * with no window the own position is a per-query dot product folded into
-//    the initial softmax state (no 1-of-64 wasted MFMA band tile);
-//  * online softmax in the log2 domain (exp2), fp32 accumulation, bf16 P.
+//  * the own position is a per-query dot product folded into the initial
+//    softmax state (with no window this saves a 1-of-64 MFMA band tile; with
+//    a window the band mask covers t-W .. t-1);
+//  * online softmax in the log2 domain: Q is pre-scaled by scale*log2(e) and
+//    the score accumulators start at -m, so the MFMA output is directly the
+//    exp2 argument (no per-score multiply-add); fp32 accumulation, bf16 P.
 #include "rat_device.h"
 
 namespace rat {
@@ -141,23 +144,73 @@ struct WaveState {
   int nlo[QB];             // anchors visible to each query
 };
 
+// Raw per-lane query inputs of a wave's 16*QB queries: q fragments, the own
+// key fragments and the own value row slice (4 elements per 16-row d-block).
+template <typename ST>
+struct Raw4;
+template <>
+struct Raw4<bf16> {
+  u32x2 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ f32x4 f32() const {
+    return f32x4{bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1])};
+  }
+};
+template <>
+struct Raw4<float> {
+  f32x4 u;
+  __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ f32x4 f32() const { return u; }
+};
+
+template <typename ST, int HD, int QB>
+struct QueryIn {
+  using C = AttnCfg<ST, HD, QB>;
+  Frag<ST> q[QB][C::NS];
+  Frag<ST> k[QB][C::NS];
+  Raw4<ST> v[QB][C::NDB];
+
+  // rows of the wave's queries tw0 + 16*nb + (lane % 16), clamped to T-1
+  __device__ __forceinline__ void load(const ST* qp, const ST* hkp, const ST* hvp, int tw0, int T) {
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15;
+    const int g = lane >> 4;
+#pragma unroll
+    for (int nb = 0; nb < QB; ++nb) {
+      const int64_t row = (int64_t)min(tw0 + 16 * nb + col, T - 1) * HD;
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) {
+        q[nb][s] = frag_ld8(qp + row + 32 * s + 8 * g);
+        k[nb][s] = frag_ld8(hkp + row + 32 * s + 8 * g);
+      }
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) v[nb][db].load(hvp + row + 16 * db + 4 * g);
+    }
+  }
+};
+
 // One staged tile against one wave's 16*QB queries.
 //  kind 0: anchors, key index = anchor index a, visible iff a < nlo(t)
 //  kind 1: band,    key index = position j,     visible iff t-W <= j <= t
-template <typename ST, int HD, int QB>
+template <typename ST, int HD, int QB, int VS = AttnCfg<ST, HD, QB>::VSTR>
 __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST* sK,
                                             const ST* sVt, int key0, int kind, bool need_mask,
-                                            int W, float scale_log2) {
+                                            int W) {
   using C = AttnCfg<ST, HD, QB>;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
 
+  // accumulators start at -m: with Q pre-scaled by scale*log2(e) the MFMA
+  // result is c*s - m, the exp2 argument of the running softmax
   f32x4 S[C::NMB][QB];
 #pragma unroll
   for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < QB; ++nb) S[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < QB; ++nb) {
+      const float mneg = -ws.m[nb];
+      S[mb][nb] = f32x4{mneg, mneg, mneg, mneg};
+    }
 
 #pragma unroll
   for (int s = 0; s < C::NS; ++s) {
@@ -169,17 +222,17 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
     }
   }
 
-  // Online softmax in the log2 domain, scores scaled by c = scale*log2(e).
-  // The running max m is raised only when a tile's max exceeds it by more
-  // than kRescaleSlack: every weight is then exp2(c*s - m) <= 2^kRescaleSlack
-  // (no overflow in fp32 or bf16), the result is the same softmax, and the
-  // accumulators are rescaled on few tiles (wave-uniform skip otherwise).
+  // Online softmax in the log2 domain.  The running max m is raised only
+  // when a tile's max exceeds it by more than kRescaleSlack: every weight is
+  // then exp2(c*s - m) <= 2^kRescaleSlack (no overflow in fp32 or bf16), the
+  // result is the same softmax, and the accumulators are rescaled on few
+  // tiles (wave-uniform skip otherwise).
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
     // visible keys of this lane's query: lo <= key <= hi
-    //   anchors: a < nlo(t);  band: t - W <= j <= t
+    //   anchors: a < nlo(t);  band: t - W <= j <= t - 1 (own position folded)
     const int lo = kind == 0 ? 0 : ws.tq[nb] - W;
-    const int hi = kind == 0 ? ws.nlo[nb] - 1 : ws.tq[nb];
+    const int hi = kind == 0 ? ws.nlo[nb] - 1 : ws.tq[nb] - 1;
     const int base = key0 + 4 * g - lo;
     const uint32_t span = (uint32_t)(hi - lo);
     float tmax = -INFINITY;
@@ -198,23 +251,23 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, S[mb][nb][i]);
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    const float mcand = tmax * scale_log2;
-    const bool grow = mcand > ws.m[nb] + kRescaleSlack;
+    const bool grow = tmax > kRescaleSlack;
     if (__any(grow)) {
-      const float mnew = grow ? mcand : ws.m[nb];
-      const float alpha = __builtin_amdgcn_exp2f(ws.m[nb] - mnew);
-      ws.m[nb] = mnew;
+      const float delta = grow ? tmax : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      ws.m[nb] += delta;
       ws.l[nb] *= alpha;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) S[mb][nb] -= delta;
     }
-    const float mneg = -ws.m[nb];
     float lsum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][nb][i], scale_log2, mneg));
+        const float pv = __builtin_amdgcn_exp2f(S[mb][nb][i]);
         S[mb][nb][i] = pv;
         lsum += pv;
       }
@@ -228,7 +281,7 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
     for (int nb = 0; nb < QB; ++nb) pb[nb] = frag_from(S[2 * kk][nb], S[2 * kk + 1][nb], (ST*)nullptr);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const ST* vrow = sVt + (16 * db + col) * C::VSTR + 32 * kk + 4 * g;
+      const ST* vrow = sVt + (16 * db + col) * VS + 32 * kk + 4 * g;
       const Frag<ST> va = frag_ld4x2(vrow, vrow + 16);
 #pragma unroll
       for (int nb = 0; nb < QB; ++nb) mma16(ws.acc[nb][db], va, pb[nb]);
@@ -236,9 +289,14 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
   }
 }
 
+// One query tile of 64*QB queries at t0.  `qin` holds this tile's query
+// inputs (already loaded); if `next_t0` >= 0, the inputs of the query tile at
+// next_t0 are loaded into `qnext` right after they are consumed here, so
+// their HBM latency overlaps this tile's key loop.
 template <typename ST, int HD, int QB>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, int t0, ST* sK,
-                                             ST* sVt) {
+                                             ST* sVt, const QueryIn<ST, HD, QB>& qin,
+                                             QueryIn<ST, HD, QB>& qnext, int next_t0) {
   using C = AttnCfg<ST, HD, QB>;
   constexpr int QW = 16 * QB;  // queries per wave
   const int tid = threadIdx.x;
@@ -289,35 +347,30 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
     pf.load(ks, vs, nv);
   }
 
+  // own position folded into the initial state (m = its score, from the
+  // unscaled q in fp32; l = 1; acc = its value row).  The MFMA operand is Q
+  // pre-scaled by c = scale*log2(e), so tile scores come out in log2 units
+  // (bf16: q*c is rounded once, a relative 2^-9 per element, the same order
+  // as the bf16 rounding of P).
   WaveState<ST, HD, QB> ws;
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
     ws.tq[nb] = tw0 + 16 * nb + col;
-    const int tcl = min(ws.tq[nb], T - 1);
-    ws.nlo[nb] = max(0, tcl - W) / D;
-    const ST* qrow = qp + (int64_t)tcl * HD;
+    ws.nlo[nb] = max(0, min(ws.tq[nb], T - 1) - W) / D;
+    float d = 0.f;
 #pragma unroll
-    for (int s = 0; s < C::NS; ++s) ws.qf[nb][s] = frag_ld8(qrow + 32 * s + 8 * g);
-    if (W == 0) {
-      // own position only: fold it into the initial state
-      const ST* krow = hkp + (int64_t)tcl * HD;
-      float d = 0.f;
-#pragma unroll
-      for (int s = 0; s < C::NS; ++s) d += frag_dot(ws.qf[nb][s], frag_ld8(krow + 32 * s + 8 * g));
-      d += shfl_xor_f(d, 16);
-      d += shfl_xor_f(d, 32);
-      ws.m[nb] = d * p.scale_log2;
-      ws.l[nb] = (g == 0) ? 1.f : 0.f;
-      const ST* vrow = hvp + (int64_t)tcl * HD;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] = ld4_f32(vrow + 16 * db + 4 * g);
-    } else {
-      ws.m[nb] = -1e30f;
-      ws.l[nb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < C::NS; ++s) {
+      d += frag_dot(qin.q[nb][s], qin.k[nb][s]);
+      ws.qf[nb][s] = frag_scale(qin.q[nb][s], p.scale_log2);
     }
+    d += shfl_xor_f(d, 16);
+    d += shfl_xor_f(d, 32);
+    ws.m[nb] = d * p.scale_log2;
+    ws.l[nb] = (g == 0) ? 1.f : 0.f;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] = qin.v[nb][db].f32();
   }
+  if (next_t0 >= 0) qnext.load(qp, hkp, hvp, next_t0 + QW * wave, T);
 
   const int w_end = wave_active ? max(0, tlast_w - W) / D : 0;
   const int w_full = wave_active ? max(0, tw0 - W) / D : 0;
@@ -341,10 +394,10 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
     } else {
       part = wave_active && key0 <= tlast_w && key0 + C::BN > wj0;
       // fully visible to all of the wave's queries iff
-      // tw0+QW-1 - W <= key0 and key0 + BN - 1 <= tw0 (and no clamped rows)
-      need_mask = !((tw0 + QW - 1 - W <= key0) && (key0 + C::BN - 1 <= tw0) && (tw0 + QW - 1 < T));
+      // tw0+QW-1 - W <= key0 and key0 + BN - 1 <= tw0 - 1 (and no clamped rows)
+      need_mask = !((tw0 + QW - 1 - W <= key0) && (key0 + C::BN <= tw0) && (tw0 + QW - 1 < T));
     }
-    if (part) tile_update<ST, HD, QB>(ws, sK, sVt, key0, kind, need_mask, W, p.scale_log2);
+    if (part) tile_update<ST, HD, QB>(ws, sK, sVt, key0, kind, need_mask, W);
   }
 
   // ---- normalise and store --------------------------------------------------
@@ -375,6 +428,9 @@ void attn_prefill_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::KSTR];
   __shared__ __attribute__((aligned(16))) ST sVt[HD * C::VSTR];
 
+  // block -> (head rank, batch row, pair): heads in cost order, so the
+  // heaviest blocks are dispatched first; consecutive blocks land on
+  // different XCDs, which spreads every head's work over the whole chip
   const int L = blockIdx.x;
   const int per_rank = p.B * p.np;
   const int rank = L / per_rank;
@@ -385,12 +441,183 @@ void attn_prefill_kernel(const AttnParams p) {
 
   const int qa = p.nq - 1 - pr;  // heavy tile first, then its partner
   const int ntiles = pr < qa ? 2 : 1;
-  for (int it = 0; it < ntiles; ++it)
-    process_tile<ST, HD, QB>(p, b, h, (it == 0 ? qa : pr) * C::BM, sK, sVt);
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t off = bh * p.T * HD;
+  const ST* qp = reinterpret_cast<const ST*>(p.q) + off;
+  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
+  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
+  const int wave = threadIdx.x >> 6;
+  QueryIn<ST, HD, QB> q0, q1;
+  q0.load(qp, hkp, hvp, qa * C::BM + 16 * QB * wave, p.T);
+  // QB = 1 (streaming-bound): the partner tile's query inputs are loaded
+  // while the first tile runs; QB = 2 has no registers to spare for that
+  const bool pre = QB == 1 && ntiles == 2;
+  process_tile<ST, HD, QB>(p, b, h, qa * C::BM, sK, sVt, q0, q1, pre ? pr * C::BM : -1);
+  if (ntiles == 2) {
+    if (!pre) q1.load(qp, hkp, hvp, pr * C::BM + 16 * QB * wave, p.T);
+    process_tile<ST, HD, QB>(p, b, h, pr * C::BM, sK, sVt, q1, q0, -1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Resident-anchor kernel: no window and at most kResidentAnchors anchors per
+// head (e.g. T = 4096 at D = 16), bf16.  A workgroup loads its head's anchor
+// rows into LDS once (K row-major, V transposed: 136 KB at hd = 128) and its
+// 8 waves then stream 16-query blocks independently -- no barrier and no
+// global K/V traffic per block.  Each wave keeps the query inputs (q, own
+// key, own value rows) of its next two blocks in flight, about 192 KB per
+// CU, which is what HBM latency needs at full bandwidth.  Blocks of a head
+// are dealt round-robin over its workgroups and waves, so every wave sees
+// the same mix of short (early) and long (late) query rows.
+// ---------------------------------------------------------------------------
+template <typename ST, int HD>
+__device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, int D, int tb,
+                                               const ST* sK, const ST* sVt,
+                                               QueryIn<ST, HD, 1>& qin, int next_tb) {
+  using C = AttnCfg<ST, HD, 1>;
+  constexpr int VS = kResidentAnchors + 4;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int T = p.T;
+  const int64_t off = bh * T * HD;
+  const ST* qp = reinterpret_cast<const ST*>(p.q) + off;
+  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
+  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
+
+  WaveState<ST, HD, 1> ws;
+  ws.tq[0] = tb + col;
+  ws.nlo[0] = min(ws.tq[0], T - 1) / D;
+  float d = 0.f;
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) {
+    d += frag_dot(qin.q[0][s], qin.k[0][s]);
+    ws.qf[0][s] = frag_scale(qin.q[0][s], p.scale_log2);
+  }
+  d += shfl_xor_f(d, 16);
+  d += shfl_xor_f(d, 32);
+  ws.m[0] = d * p.scale_log2;
+  ws.l[0] = (g == 0) ? 1.f : 0.f;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) ws.acc[0][db] = qin.v[0][db].f32();
+  if (next_tb >= 0) qin.load(qp, hkp, hvp, next_tb, T);  // registers free again
+
+  const int n_end = min(tb + 15, T - 1) / D;  // anchors any query of the block sees
+  const int w_full = tb / D;                  // anchors every query of the block sees
+  for (int key0 = 0; key0 < n_end; key0 += C::BN)
+    tile_update<ST, HD, 1, VS>(ws, sK + key0 * C::KSTR, sVt + key0, key0, 0, key0 + C::BN > w_full, 0);
+
+  float lt = ws.l[0];
+  lt += shfl_xor_f(lt, 16);
+  lt += shfl_xor_f(lt, 32);
+  const int t = ws.tq[0];
+  if (t < T) {
+    const float inv = 1.f / lt;
+    ST* orow = reinterpret_cast<ST*>(p.o) + off + (int64_t)t * HD;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) st4(orow + 16 * db + 4 * g, ws.acc[0][db] * inv);
+    if (p.lse != nullptr && g == 0) p.lse[bh * T + t] = (ws.m[0] + __log2f(lt)) * kLn2;
+  }
+}
+
+template <typename ST, int HD>
+__global__ __launch_bounds__(64 * kResidentWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_resident_kernel(const AttnParams p) {
+  using C = AttnCfg<ST, HD, 1>;
+  constexpr int VS = kResidentAnchors + 4;
+  constexpr int NT = 64 * kResidentWaves;
+  __shared__ __attribute__((aligned(16))) ST sK[kResidentAnchors * C::KSTR];
+  __shared__ __attribute__((aligned(16))) ST sVt[HD * VS];
+
+  const int L = blockIdx.x;
+  const int per_rank = p.B * p.nra;
+  const int rank = L / per_rank;
+  const int rem = L - rank * per_rank;
+  const int b = rem / p.nra;
+  const int r = rem - b * p.nra;
+  const int h = p.perm[rank];
+  const int T = p.T;
+  const int D = p.ht.D[h];
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int tid = threadIdx.x;
+
+  // ---- stage the anchors a < floor((T-1)/D) (<= kResidentAnchors) --------
+  const int nan = (T - 1) / D;
+  if (nan > 0) {
+    const ST* kcp = reinterpret_cast<const ST*>(p.Kc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;
+    const ST* vcp = reinterpret_cast<const ST*>(p.Vc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;
+    const int nt = (nan + C::BN - 1) / C::BN;
+    for (int j = 0; j < nt; ++j) {
+      // K: BN rows x CPR 16-byte chunks; rows at or past nan re-read row
+      // nan-1 (finite, always masked)
+#pragma unroll
+      for (int i = 0; i < (C::KITEMS + NT - 1) / NT; ++i) {
+        const int idx = tid + NT * i;
+        if (idx < C::KITEMS) {
+          const int row = idx / C::CPR;
+          const int c16 = idx - row * C::CPR;
+          const int a = min(C::BN * j + row, nan - 1);
+          st_raw16(sK + (C::BN * j + row) * C::KSTR + c16 * C::VEC,
+                   ld_raw16(kcp + (int64_t)a * HD + c16 * C::VEC));
+        }
+      }
+      // V transposed: work item = 4 anchors x VEC channels
+      for (int idx = tid; idx < C::VITEMS; idx += NT) {
+        const int dg = idx / (C::BN / 4);
+        const int kg = idx - dg * (C::BN / 4);
+        u32x4 v[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          v[rr] = ld_raw16(vcp + (int64_t)min(C::BN * j + 4 * kg + rr, nan - 1) * HD + dg * C::VEC);
+        ST* dst = sVt + (dg * C::VEC) * VS + C::BN * j + 4 * kg;
+#pragma unroll
+        for (int e = 0; e < C::VEC; ++e) {
+          const int w = e >> 1;
+          const int sh = (e & 1) * 16;
+          const uint32_t x0 = (v[0][w] >> sh) & 0xffffu, x1 = (v[1][w] >> sh) & 0xffffu;
+          const uint32_t x2 = (v[2][w] >> sh) & 0xffffu, x3 = (v[3][w] >> sh) & 0xffffu;
+          u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
+          *reinterpret_cast<u32x2*>(dst + e * VS) = pk;
+        }
+      }
+    }
+  }
+  __syncthreads();  // the only barrier: anchors are read-only from here on
+
+  // ---- 16-query blocks: block r + nra*(wave + 8k), two blocks prefetched --
+  const int wave = tid >> 6;
+  const int nblk = (T + 15) / 16;
+  const int stride = p.nra * kResidentWaves;
+  const int first = r + p.nra * wave;
+  const int64_t off = bh * T * HD;
+  const ST* qp = reinterpret_cast<const ST*>(p.q) + off;
+  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
+  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
+  QueryIn<ST, HD, 1> qa, qb;
+  if (first < nblk) qa.load(qp, hkp, hvp, 16 * first, T);
+  if (first + stride < nblk) qb.load(qp, hkp, hvp, 16 * (first + stride), T);
+  for (int bi = first; bi < nblk; bi += 2 * stride) {
+    const int n2 = bi + 2 * stride;
+    resident_block<ST, HD>(p, bh, D, 16 * bi, sK, sVt, qa, n2 < nblk ? 16 * n2 : -1);
+    const int b1 = bi + stride;
+    if (b1 >= nblk) break;
+    const int n3 = b1 + 2 * stride;
+    resident_block<ST, HD>(p, bh, D, 16 * b1, sK, sVt, qb, n3 < nblk ? 16 * n3 : -1);
+  }
 }
 
 template <typename ST, int HD>
 int launch_t(const AttnParams& p, hipStream_t st) {
+  if (p.mode == 1) {
+    if constexpr (sizeof(ST) == 2) {
+      const int64_t nwg = (int64_t)p.H * p.B * p.nra;
+      if (nwg == 0) return 0;
+      hipLaunchKernelGGL((attn_resident_kernel<ST, HD>), dim3((unsigned)nwg),
+                         dim3(64 * kResidentWaves), 0, st, p);
+      return (int)hipGetLastError();
+    }
+    return (int)hipErrorInvalidValue;
+  }
   const int64_t nblk = (int64_t)p.H * p.B * p.np;
   if (nblk == 0) return 0;
   if (p.qb == 2)

@@ -225,6 +225,23 @@ int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const i
     avg_keys += (double)std::max<int64_t>(0, T - W[h]) / (2.0 * D[h]) + std::min<int64_t>(W[h], T);
   avg_keys /= H;
   p.qb = avg_keys >= 512.0 ? 2 : 1;
+  // resident-anchor kernel: bf16, no window, every head's anchors fit in LDS
+  bool resident = dtype == RAT_DTYPE_BF16;
+  for (int h = 0; h < H && resident; ++h) resident = W[h] == 0 && (T - 1) / D[h] <= kResidentAnchors;
+  if (resident) {
+    // about one workgroup per CU, at least one 16-query block per wave
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return RAT_ERR_HIP;
+    const int64_t nbh = (int64_t)B * H;
+    const int64_t nblk16 = (T + 15) / 16;
+    int64_t nra = (std::max(cus, 1) + nbh - 1) / nbh;
+    nra = std::max<int64_t>(1, std::min<int64_t>(nra, (nblk16 + kResidentWaves - 1) / kResidentWaves));
+    if (nbh * nra > INT32_MAX) return RAT_ERR_UNSUPPORTED;
+    p.mode = 1;
+    p.nra = (int)nra;
+  }
   const int bm = 64 * p.qb;
   p.nq = (int)((T + bm - 1) / bm);
   p.np = (p.nq + 1) / 2;

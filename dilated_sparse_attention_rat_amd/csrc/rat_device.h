@@ -161,6 +161,22 @@ __device__ __forceinline__ Frag<float> frag_from(const f32x4& a, const f32x4& b,
   f.hi = b;
   return f;
 }
+// fragment scaled by c (bf16: rounded back to nearest even)
+__device__ __forceinline__ Frag<bf16> frag_scale(const Frag<bf16>& f, float c) {
+  f32x4 a, b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = (float)f.v[j] * c;
+    b[j] = (float)f.v[4 + j] * c;
+  }
+  return frag_from(a, b, (bf16*)nullptr);
+}
+__device__ __forceinline__ Frag<float> frag_scale(const Frag<float>& f, float c) {
+  Frag<float> r;
+  r.lo = f.lo * c;
+  r.hi = f.hi * c;
+  return r;
+}
 // dot product of two fragments (fp32 accumulate)
 __device__ __forceinline__ float frag_dot(const Frag<bf16>& a, const Frag<bf16>& b) {
   float s = 0.f;

@@ -52,8 +52,15 @@ struct ScanParams {
   HeadTables ht;
 };
 
+// Resident-anchor attention applies when no head has a window and every
+// head's anchors fit in LDS (bf16).
+constexpr int kResidentAnchors = 256;
+constexpr int kResidentWaves = 8;  // waves per resident-anchor workgroup
+
 struct AttnParams {
   int B, H, T;
+  int mode;          // 0: streamed K/V tiles; 1: resident anchors
+  int nra;           // mode 1: workgroups per (b, h)
   int qb;            // 16-query blocks per wave (1 or 2): tile = 64*qb queries
   int nq;            // query tiles per (b, h)
   int np;            // pair-blocks per (b, h)
