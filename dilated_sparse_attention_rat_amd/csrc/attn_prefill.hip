@@ -463,17 +463,17 @@ void attn_prefill_kernel(const AttnParams p) {
 // Resident-anchor kernel: no window and at most kResidentAnchors anchors per
 // head (e.g. T = 4096 at D = 16), bf16.  A workgroup loads its head's anchor
 // rows into LDS once (K row-major, V transposed: 136 KB at hd = 128) and its
-// 8 waves then stream 16-query blocks independently -- no barrier and no
-// global K/V traffic per block.  Each wave keeps the query inputs (q, own
-// key, own value rows) of its next two blocks in flight, about 192 KB per
-// CU, which is what HBM latency needs at full bandwidth.  Blocks of a head
-// are dealt round-robin over its workgroups and waves, so every wave sees
-// the same mix of short (early) and long (late) query rows.
+// 16 waves then stream 16-query blocks independently -- no barrier and no
+// global K/V traffic per block; with four waves per SIMD, the waves waiting
+// for their next block's query rows (q, own key, own value) overlap the
+// others' MFMAs.  Blocks of a head are dealt round-robin over its workgroups
+// and waves, so every wave sees the same mix of short (early) and long
+// (late) query rows.
 // ---------------------------------------------------------------------------
 template <typename ST, int HD>
 __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, int D, int tb,
                                                const ST* sK, const ST* sVt,
-                                               QueryIn<ST, HD, 1>& qin, int next_tb) {
+                                               const QueryIn<ST, HD, 1>& qin) {
   using C = AttnCfg<ST, HD, 1>;
   constexpr int VS = kResidentAnchors + 4;
   const int lane = threadIdx.x & 63;
@@ -500,8 +500,6 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   ws.l[0] = (g == 0) ? 1.f : 0.f;
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) ws.acc[0][db] = qin.v[0][db].f32();
-  if (next_tb >= 0) qin.load(qp, hkp, hvp, next_tb, T);  // registers free again
-
   const int n_end = min(tb + 15, T - 1) / D;  // anchors any query of the block sees
   const int w_full = tb / D;                  // anchors every query of the block sees
   for (int key0 = 0; key0 < n_end; key0 += C::BN)
@@ -511,17 +509,22 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   lt += shfl_xor_f(lt, 16);
   lt += shfl_xor_f(lt, 32);
   const int t = ws.tq[0];
-  if (t < T) {
-    const float inv = 1.f / lt;
-    ST* orow = reinterpret_cast<ST*>(p.o) + off + (int64_t)t * HD;
+  const float inv = 1.f / lt;
+  // buffer stores: lanes of rows past T (and the lse of lanes g > 0, or a
+  // null lse) use an offset outside the region, which the hardware drops
+  const auto orsrc = buffer_region(reinterpret_cast<ST*>(p.o) + off);
+  const auto lrsrc = buffer_region(p.lse != nullptr ? p.lse + bh * T : nullptr);
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) st4(orow + 16 * db + 4 * g, ws.acc[0][db] * inv);
-    if (p.lse != nullptr && g == 0) p.lse[bh * T + t] = (ws.m[0] + __log2f(lt)) * kLn2;
+  for (int db = 0; db < C::NDB; ++db) {
+    const uint32_t ob = t < T ? (uint32_t)(((int64_t)t * HD + 16 * db + 4 * g) * sizeof(ST)) : kDropOffset;
+    buffer_st4(orsrc, ob, ws.acc[0][db] * inv);
   }
+  const uint32_t lb = (t < T && g == 0 && p.lse != nullptr) ? (uint32_t)t * 4u : kDropOffset;
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((ws.m[0] + __log2f(lt)) * kLn2), lrsrc, lb, 0, 0);
 }
 
 template <typename ST, int HD>
-__global__ __launch_bounds__(64 * kResidentWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kResidentWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attn_resident_kernel(const AttnParams p) {
   using C = AttnCfg<ST, HD, 1>;
   constexpr int VS = kResidentAnchors + 4;
@@ -593,16 +596,12 @@ void attn_resident_kernel(const AttnParams p) {
   const ST* qp = reinterpret_cast<const ST*>(p.q) + off;
   const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
   const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
-  QueryIn<ST, HD, 1> qa, qb;
-  if (first < nblk) qa.load(qp, hkp, hvp, 16 * first, T);
-  if (first + stride < nblk) qb.load(qp, hkp, hvp, 16 * (first + stride), T);
-  for (int bi = first; bi < nblk; bi += 2 * stride) {
-    const int n2 = bi + 2 * stride;
-    resident_block<ST, HD>(p, bh, D, 16 * bi, sK, sVt, qa, n2 < nblk ? 16 * n2 : -1);
-    const int b1 = bi + stride;
-    if (b1 >= nblk) break;
-    const int n3 = b1 + 2 * stride;
-    resident_block<ST, HD>(p, bh, D, 16 * b1, sK, sVt, qb, n3 < nblk ? 16 * n3 : -1);
+  // the wave's blocks first + j*stride; sixteen waves per CU hide the load
+  // latency of each block's query inputs
+  for (int bi = first; bi < nblk; bi += stride) {
+    QueryIn<ST, HD, 1> qa;
+    qa.load(qp, hkp, hvp, 16 * bi, T);
+    resident_block<ST, HD>(p, bh, D, 16 * bi, sK, sVt, qa);
   }
 }
 

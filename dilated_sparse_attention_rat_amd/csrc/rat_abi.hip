@@ -226,7 +226,8 @@ int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const i
   avg_keys /= H;
   p.qb = avg_keys >= 512.0 ? 2 : 1;
   // resident-anchor kernel: bf16, no window, every head's anchors fit in LDS
-  bool resident = dtype == RAT_DTYPE_BF16;
+  // (per-(b,h) output rows are addressed with 32-bit byte offsets there)
+  bool resident = dtype == RAT_DTYPE_BF16 && T * hd * 2 <= INT32_MAX;
   for (int h = 0; h < H && resident; ++h) resident = W[h] == 0 && (T - 1) / D[h] <= kResidentAnchors;
   if (resident) {
     // about one workgroup per CU, at least one 16-query block per wave

@@ -223,6 +223,22 @@ __device__ __forceinline__ void st4(float* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// Buffer resource over one region of < 2^31 bytes.  A buffer access at byte
+// offset kDropOffset lies outside every such region: loads return 0 and
+// stores are discarded by the hardware, which lets masked accesses be issued
+// unconditionally (straight-line code, exact counts of outstanding memory
+// operations).  dword 3 = 0x00020000: raw 32-bit data format, the gfx9
+// buffer default.
+constexpr uint32_t kDropOffset = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_region(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)kDropOffset, 0x00020000);
+}
+// fp32 x4 -> 4 consecutive bf16 at byte offset `off` of a region
+__device__ __forceinline__ void buffer_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4& v) {
+  u32x2 u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+}
+
 // cross-lane helpers (wave64)
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 

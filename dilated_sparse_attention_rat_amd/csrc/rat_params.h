@@ -55,7 +55,7 @@ struct ScanParams {
 // Resident-anchor attention applies when no head has a window and every
 // head's anchors fit in LDS (bf16).
 constexpr int kResidentAnchors = 256;
-constexpr int kResidentWaves = 8;  // waves per resident-anchor workgroup
+constexpr int kResidentWaves = 16;  // waves per resident-anchor workgroup
 
 struct AttnParams {
   int B, H, T;
