@@ -9,8 +9,10 @@ from .binding import (RAT_DTYPE_BF16, RAT_DTYPE_F32, RAT_ERR_CAPACITY,  # noqa: 
                       RAT_ERR_WORKSPACE, RAT_MAX_HEADS, RAT_OK, RatError,
                       alloc_cache, decode_workspace, lib, rat_anchor_rows,
                       rat_decode_step, rat_decode_workspace_bytes,
-                      rat_dilated_attn_prefill, rat_ring_rows,
-                      rat_scan_prefill, rat_scan_workspace_bytes,
+                      rat_dilated_attn_prefill,
+                      rat_dilated_attn_prefill_continue, rat_ring_rows,
+                      rat_scan_prefill, rat_scan_prefill_continue,
+                      rat_scan_workspace_bytes,
                       rat_status_string, rat_version, scan_workspace)
 
 __version__ = "0.1.0"

@@ -31,6 +31,7 @@ RAT_MAX_HEADS = 128
 EXPORTED = [
     "rat_version", "rat_status_string", "rat_anchor_rows", "rat_ring_rows",
     "rat_scan_workspace_bytes", "rat_scan_prefill", "rat_dilated_attn_prefill",
+    "rat_scan_prefill_continue", "rat_dilated_attn_prefill_continue",
     "rat_decode_workspace_bytes", "rat_decode_step",
 ]
 
@@ -70,6 +71,13 @@ def lib() -> ctypes.CDLL:
         L.rat_dilated_attn_prefill.argtypes = [i32, i32, i32, i64, i32, P, P,
                                                f32, i64, P, P, P, P, P, P, P, P]
         L.rat_dilated_attn_prefill.restype = i32
+        L.rat_scan_prefill_continue.argtypes = [i32, i32, i32, i64, i32, P, P, i64, i64,
+                                                P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                                P, P, P, sz, P]
+        L.rat_scan_prefill_continue.restype = i32
+        L.rat_dilated_attn_prefill_continue.argtypes = [i32, i32, i32, i64, i32, P, P, f32,
+                                                        i64, i64, P, P, P, P, P, P, P, P, P, P]
+        L.rat_dilated_attn_prefill_continue.restype = i32
         L.rat_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, P, P, i32]
         L.rat_decode_workspace_bytes.restype = i64
         L.rat_decode_step.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64,
@@ -239,6 +247,67 @@ def rat_dilated_attn_prefill(q, hk, hv, Kc, Vc, D, W, T_cap: int, o, lse=None,
         _opt(lse, "lse", (B, H, T), torch.float32, dev), _stream(stream, dev),
     ]
     _check("rat_dilated_attn_prefill", lib().rat_dilated_attn_prefill(*args))
+
+
+def rat_scan_prefill_continue(k, v, g, D, W, T_cap: int, t0: int, state_k_in,
+                              state_v_in, Kc, Vc, state_k, state_v, workspace,
+                              hk=None, hv=None, k_ring_in=None, v_ring_in=None,
+                              k_ring=None, v_ring=None, stream=None):
+    """Recurrence of a chunk at positions t0 .. t0+T-1.  k, v, g: [B,H,T,hd]."""
+    torch = _torch()
+    B, H, T, hd = k.shape
+    st = k.dtype
+    dev = k.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    R, _ = rat_anchor_rows(H, T_cap, Dh)
+    WS, _ = rat_ring_rows(H, Wh)
+    args = [
+        _dtype_code(k), B, H, T, hd, _ptr(Dh), _ptr(Wh), T_cap, int(t0),
+        _dev(k, "k", (B, H, T, hd), st, dev), _dev(v, "v", (B, H, T, hd), st, dev),
+        _dev(g, "g", (B, H, T, hd), st, dev),
+        _dev(state_k_in, "state_k_in", (B, H, hd), torch.float32, dev),
+        _dev(state_v_in, "state_v_in", (B, H, hd), torch.float32, dev),
+        _opt(hk, "hk", (B, H, T, hd), st, dev), _opt(hv, "hv", (B, H, T, hd), st, dev),
+        _opt(Kc, "Kc", (B, R, hd), st, dev), _opt(Vc, "Vc", (B, R, hd), st, dev),
+        _opt(k_ring_in, "k_ring_in", (B, WS, hd), st, dev),
+        _opt(v_ring_in, "v_ring_in", (B, WS, hd), st, dev),
+        _opt(k_ring, "k_ring", (B, WS, hd), st, dev), _opt(v_ring, "v_ring", (B, WS, hd), st, dev),
+        _dev(state_k, "state_k", (B, H, hd), torch.float32, dev),
+        _dev(state_v, "state_v", (B, H, hd), torch.float32, dev),
+    ]
+    need = rat_scan_workspace_bytes(B, H, T, hd)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    args += [ctypes.c_void_p(workspace.data_ptr()),
+             workspace.numel() * workspace.element_size(), _stream(stream, dev)]
+    _check("rat_scan_prefill_continue", lib().rat_scan_prefill_continue(*args))
+
+
+def rat_dilated_attn_prefill_continue(q, hk, hv, Kc, Vc, D, W, T_cap: int, t0: int, o,
+                                      k_ring_prev=None, v_ring_prev=None, lse=None,
+                                      scale: float = 0.0, stream=None):
+    """Attention of a chunk's queries at positions t0 .. t0+T-1."""
+    torch = _torch()
+    B, H, T, hd = q.shape
+    st = q.dtype
+    dev = q.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    R, _ = rat_anchor_rows(H, T_cap, Dh)
+    WS, _ = rat_ring_rows(H, Wh)
+    args = [
+        _dtype_code(q), B, H, T, hd, _ptr(Dh), _ptr(Wh), float(scale), T_cap, int(t0),
+        _dev(q, "q", (B, H, T, hd), st, dev), _dev(hk, "hk", (B, H, T, hd), st, dev),
+        _dev(hv, "hv", (B, H, T, hd), st, dev),
+        _opt(Kc, "Kc", (B, R, hd), st, dev), _opt(Vc, "Vc", (B, R, hd), st, dev),
+        _opt(k_ring_prev, "k_ring_prev", (B, WS, hd), st, dev),
+        _opt(v_ring_prev, "v_ring_prev", (B, WS, hd), st, dev),
+        _dev(o, "o", (B, H, T, hd), st, dev),
+        _opt(lse, "lse", (B, H, T), torch.float32, dev), _stream(stream, dev),
+    ]
+    _check("rat_dilated_attn_prefill_continue",
+           lib().rat_dilated_attn_prefill_continue(*args))
 
 
 def rat_decode_step(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, o,

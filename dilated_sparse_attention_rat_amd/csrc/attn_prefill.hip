@@ -70,12 +70,12 @@ struct Prefetch {
   u32x4 k[C::KPT];
   u32x4 v[C::VPT][4];
 
-  // Rows [0, BN) of ksrc/vsrc (nvalid >= 1).  Rows at or beyond nvalid
-  // re-read row nvalid-1: such keys are always masked (weight exactly 0) and
-  // the duplicated V row is finite, so they contribute nothing, and the
-  // loads need no branches.
-  __device__ __forceinline__ void load(const ST* __restrict__ ksrc, const ST* __restrict__ vsrc,
-                                       int nvalid) {
+  // Rows [0, BN) of the tile (nvalid >= 1); rows(r) gives the K and V row
+  // pointers of tile row r.  Rows at or beyond nvalid re-read row nvalid-1:
+  // such keys are always masked (weight exactly 0) and the duplicated V row
+  // is finite, so they contribute nothing, and the loads need no branches.
+  template <typename Rows>
+  __device__ __forceinline__ void load(Rows rows, int nvalid) {
     const int tid = threadIdx.x;
     const int last = nvalid - 1;
 #pragma unroll
@@ -83,7 +83,7 @@ struct Prefetch {
       const int idx = min(tid + 256 * i, C::KITEMS - 1);
       const int row = idx / C::CPR;
       const int c16 = idx - row * C::CPR;
-      k[i] = ld_raw16(ksrc + (int64_t)min(row, last) * HD + c16 * C::VEC);
+      k[i] = ld_raw16(rows.k(min(row, last)) + c16 * C::VEC);
     }
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
@@ -92,7 +92,7 @@ struct Prefetch {
       const int kg = idx - dg * (C::BN / 4);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        v[i][rr] = ld_raw16(vsrc + (int64_t)min(4 * kg + rr, last) * HD + dg * C::VEC);
+        v[i][rr] = ld_raw16(rows.v(min(4 * kg + rr, last)) + dg * C::VEC);
     }
   }
 
@@ -289,14 +289,42 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
   }
 }
 
-// One query tile of 64*QB queries at t0.  `qin` holds this tile's query
-// inputs (already loaded); if `next_t0` >= 0, the inputs of the query tile at
-// next_t0 are loaded into `qnext` right after they are consumed here, so
-// their HBM latency overlaps this tile's key loop.
+// Key rows of one staged tile.  Anchor tiles read the anchor cache; band
+// tiles read the states of positions key0 .. key0+BN-1: rows of this call
+// (position >= t0) from hk/hv, earlier positions (a continuation's window
+// reaching before t0) from the ring of the previous call, slot p mod W.
+template <typename ST, int HD>
+struct TileRows {
+  const ST* ka;  // anchors: row r at ka + r*HD (key0 folded in)
+  const ST* va;
+  const ST* hk;  // band: states of this call, position p at (p - t0)
+  const ST* hv;
+  const ST* rk;  // band: ring of the previous call
+  const ST* rv;
+  int key0, t0, W;
+  bool band;
+  __device__ __forceinline__ const ST* k(int r) const {
+    if (!band) return ka + (int64_t)r * HD;
+    const int pos = key0 + r;
+    return pos >= t0 ? hk + (int64_t)(pos - t0) * HD : rk + (int64_t)(pos % W) * HD;
+  }
+  __device__ __forceinline__ const ST* v(int r) const {
+    if (!band) return va + (int64_t)r * HD;
+    const int pos = key0 + r;
+    return pos >= t0 ? hv + (int64_t)(pos - t0) * HD : rv + (int64_t)(pos % W) * HD;
+  }
+};
+
+// One query tile of 64*QB queries at local row lt0 (absolute position
+// p.t0 + lt0).  `qin` holds this tile's query inputs (already loaded); if
+// `next_lt0` >= 0, the inputs of the query tile at next_lt0 are loaded into
+// `qnext` right after they are consumed here, so their HBM latency overlaps
+// this tile's key loop.  Positions (queries, band keys, anchors) are
+// absolute; rows of q, hk, hv, o and lse are local to this call.
 template <typename ST, int HD, int QB>
-__device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, int t0, ST* sK,
+__device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, int lt0, ST* sK,
                                              ST* sVt, const QueryIn<ST, HD, QB>& qin,
-                                             QueryIn<ST, HD, QB>& qnext, int next_t0) {
+                                             QueryIn<ST, HD, QB>& qnext, int next_lt0) {
   using C = AttnCfg<ST, HD, QB>;
   constexpr int QW = 16 * QB;  // queries per wave
   const int tid = threadIdx.x;
@@ -305,6 +333,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   const int col = lane & 15;
   const int g = lane >> 4;
   const int T = p.T;
+  const int a0 = p.t0;  // absolute position of local row 0
   const int D = p.ht.D[h];
   const int W = p.ht.W[h];
   const int64_t bh = (int64_t)b * p.H + h;
@@ -313,38 +342,51 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   const ST* hvp = reinterpret_cast<const ST*>(p.hv) + bh * T * HD;
   const ST* kcp = reinterpret_cast<const ST*>(p.Kc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;
   const ST* vcp = reinterpret_cast<const ST*>(p.Vc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;
+  const int64_t rofs = ((int64_t)b * p.WS + p.ht.roff[h]) * HD;
+  const ST* rkp = p.kr != nullptr ? reinterpret_cast<const ST*>(p.kr) + rofs : nullptr;
+  const ST* rvp = p.vr != nullptr ? reinterpret_cast<const ST*>(p.vr) + rofs : nullptr;
 
-  const int tw0 = t0 + QW * wave;              // first query of this wave
+  const int tw0 = lt0 + QW * wave;             // first query of this wave (local)
   const bool wave_active = tw0 < T;
-  const int tlast_blk = min(t0 + C::BM - 1, T - 1);
-  const int tlast_w = min(tw0 + QW - 1, T - 1);
+  const int alast_blk = a0 + min(lt0 + C::BM - 1, T - 1);  // last query (absolute)
+  const int aw0 = a0 + tw0;                                // absolute
+  const int awlast = a0 + min(tw0 + QW - 1, T - 1);
 
-  // the tile's key tiles: anchors [0, n_end) then the band [jb0, tlast_blk]
-  const int n_end = max(0, tlast_blk - W) / D;
-  const int jb0 = max(0, t0 - W);
+  // the tile's key tiles: anchors [0, n_end) then the band [jb0, alast_blk]
+  const int n_end = max(0, alast_blk - W) / D;
+  const int jb0 = max(0, a0 + lt0 - W);
   const int na_t = (n_end + C::BN - 1) / C::BN;
-  const int nb_t = W > 0 ? (tlast_blk - jb0 + C::BN) / C::BN : 0;
+  const int nb_t = W > 0 ? (alast_blk - jb0 + C::BN) / C::BN : 0;
   const int n_items = na_t + nb_t;
-  auto item_src = [&](int i, const ST*& ks, const ST*& vs, int& nvalid, int& key0) {
+  auto item_src = [&](int i, TileRows<ST, HD>& rows, int& nvalid, int& key0) {
+    rows.hk = hkp;
+    rows.hv = hvp;
+    rows.rk = rkp;
+    rows.rv = rvp;
+    rows.t0 = a0;
+    rows.W = max(W, 1);
     if (i < na_t) {
       key0 = i * C::BN;
-      ks = kcp + (int64_t)key0 * HD;
-      vs = vcp + (int64_t)key0 * HD;
+      rows.band = false;
+      rows.ka = kcp + (int64_t)key0 * HD;
+      rows.va = vcp + (int64_t)key0 * HD;
       nvalid = n_end - key0;
     } else {
       key0 = jb0 + (i - na_t) * C::BN;
-      ks = hkp + (int64_t)key0 * HD;
-      vs = hvp + (int64_t)key0 * HD;
-      nvalid = tlast_blk + 1 - key0;
+      rows.band = true;
+      rows.ka = kcp;
+      rows.va = vcp;
+      nvalid = alast_blk + 1 - key0;
     }
+    rows.key0 = key0;
   };
 
   Prefetch<ST, HD, QB> pf;
   if (n_items > 0) {
-    const ST *ks, *vs;
+    TileRows<ST, HD> rows;
     int nv, k0;
-    item_src(0, ks, vs, nv, k0);
-    pf.load(ks, vs, nv);
+    item_src(0, rows, nv, k0);
+    pf.load(rows, nv);
   }
 
   // own position folded into the initial state (m = its score, from the
@@ -355,8 +397,8 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   WaveState<ST, HD, QB> ws;
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
-    ws.tq[nb] = tw0 + 16 * nb + col;
-    ws.nlo[nb] = max(0, min(ws.tq[nb], T - 1) - W) / D;
+    ws.tq[nb] = aw0 + 16 * nb + col;
+    ws.nlo[nb] = max(0, min(ws.tq[nb], a0 + T - 1) - W) / D;
     float d = 0.f;
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
@@ -370,32 +412,32 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] = qin.v[nb][db].f32();
   }
-  if (next_t0 >= 0) qnext.load(qp, hkp, hvp, next_t0 + QW * wave, T);
+  if (next_lt0 >= 0) qnext.load(qp, hkp, hvp, next_lt0 + QW * wave, T);
 
-  const int w_end = wave_active ? max(0, tlast_w - W) / D : 0;
-  const int w_full = wave_active ? max(0, tw0 - W) / D : 0;
-  const int wj0 = max(0, tw0 - W);
+  const int w_end = wave_active ? max(0, awlast - W) / D : 0;
+  const int w_full = wave_active ? max(0, aw0 - W) / D : 0;
+  const int wj0 = max(0, aw0 - W);
   for (int i = 0; i < n_items; ++i) {
     __syncthreads();  // every wave is done reading the previous tile
     pf.store(sK, sVt);
     __syncthreads();
-    const ST *ks, *vs;
+    TileRows<ST, HD> rows;
     int nv, key0;
     if (i + 1 < n_items) {  // next tile's loads overlap this tile's MFMAs
-      item_src(i + 1, ks, vs, nv, key0);
-      pf.load(ks, vs, nv);
+      item_src(i + 1, rows, nv, key0);
+      pf.load(rows, nv);
     }
-    item_src(i, ks, vs, nv, key0);
+    item_src(i, rows, nv, key0);
     const int kind = i < na_t ? 0 : 1;
     bool part, need_mask;
     if (kind == 0) {
       part = key0 < w_end;
       need_mask = key0 + C::BN > w_full;
     } else {
-      part = wave_active && key0 <= tlast_w && key0 + C::BN > wj0;
+      part = wave_active && key0 <= awlast && key0 + C::BN > wj0;
       // fully visible to all of the wave's queries iff
-      // tw0+QW-1 - W <= key0 and key0 + BN - 1 <= tw0 - 1 (and no clamped rows)
-      need_mask = !((tw0 + QW - 1 - W <= key0) && (key0 + C::BN <= tw0) && (tw0 + QW - 1 < T));
+      // aw0+QW-1 - W <= key0 and key0 + BN - 1 <= aw0 - 1 (and no clamped rows)
+      need_mask = !((aw0 + QW - 1 - W <= key0) && (key0 + C::BN <= aw0) && (tw0 + QW - 1 < T));
     }
     if (part) tile_update<ST, HD, QB>(ws, sK, sVt, key0, kind, need_mask, W);
   }
@@ -407,7 +449,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
     float lt = ws.l[nb];
     lt += shfl_xor_f(lt, 16);
     lt += shfl_xor_f(lt, 32);
-    const int t = ws.tq[nb];
+    const int t = ws.tq[nb] - a0;  // local row
     if (t < T) {
       const float inv = 1.f / lt;
       ST* orow = op + (int64_t)t * HD;
@@ -485,9 +527,10 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
   const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
 
+  const int a0 = p.t0;  // absolute position of local row 0
   WaveState<ST, HD, 1> ws;
-  ws.tq[0] = tb + col;
-  ws.nlo[0] = min(ws.tq[0], T - 1) / D;
+  ws.tq[0] = a0 + tb + col;
+  ws.nlo[0] = min(ws.tq[0], a0 + T - 1) / D;
   float d = 0.f;
 #pragma unroll
   for (int s = 0; s < C::NS; ++s) {
@@ -500,15 +543,15 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   ws.l[0] = (g == 0) ? 1.f : 0.f;
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) ws.acc[0][db] = qin.v[0][db].f32();
-  const int n_end = min(tb + 15, T - 1) / D;  // anchors any query of the block sees
-  const int w_full = tb / D;                  // anchors every query of the block sees
+  const int n_end = (a0 + min(tb + 15, T - 1)) / D;  // anchors any query of the block sees
+  const int w_full = (a0 + tb) / D;                  // anchors every query of the block sees
   for (int key0 = 0; key0 < n_end; key0 += C::BN)
     tile_update<ST, HD, 1, VS>(ws, sK + key0 * C::KSTR, sVt + key0, key0, 0, key0 + C::BN > w_full, 0);
 
   float lt = ws.l[0];
   lt += shfl_xor_f(lt, 16);
   lt += shfl_xor_f(lt, 32);
-  const int t = ws.tq[0];
+  const int t = ws.tq[0] - a0;  // local row
   const float inv = 1.f / lt;
   // buffer stores: lanes of rows past T (and the lse of lanes g > 0, or a
   // null lse) use an offset outside the region, which the hardware drops
@@ -544,8 +587,8 @@ void attn_resident_kernel(const AttnParams p) {
   const int64_t bh = (int64_t)b * p.H + h;
   const int tid = threadIdx.x;
 
-  // ---- stage the anchors a < floor((T-1)/D) (<= kResidentAnchors) --------
-  const int nan = (T - 1) / D;
+  // ---- stage the anchors a < floor((t0+T-1)/D) (<= kResidentAnchors) -----
+  const int nan = (p.t0 + T - 1) / D;
   if (nan > 0) {
     const ST* kcp = reinterpret_cast<const ST*>(p.Kc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;
     const ST* vcp = reinterpret_cast<const ST*>(p.Vc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;

@@ -139,14 +139,19 @@ int64_t rat_scan_workspace_bytes(int B, int H, int64_t T, int hd) {
   return std::max(a.bytes, b.bytes);
 }
 
-int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* D,
-                     const int32_t* W, int64_t T_cap, const void* k, const void* v, const void* g,
-                     void* hk, void* hv, void* Kc, void* Vc, void* k_ring, void* v_ring,
-                     float* state_k, float* state_v, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+namespace {
+// Scan of rows [0, T) at absolute positions t0 .. t0+T-1, from the state
+// (sk_in, sv_in) before row 0 (null: zero).  kr_in/vr_in: the ring before the
+// call (continuation; null or equal to the output ring: no carry copy).
+int scan_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, const int32_t* W,
+              int64_t T_cap, int64_t t0, const void* k, const void* v, const void* g,
+              const float* sk_in, const float* sv_in, void* hk, void* hv, void* Kc, void* Vc,
+              const void* kr_in, const void* vr_in, void* k_ring, void* v_ring, float* state_k,
+              float* state_v, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_common(dtype, B, H, hd, D, W);
   if (st != RAT_OK) return st;
-  if (T < 0 || T_cap < T || T_cap > kMaxT) return T_cap < T ? RAT_ERR_CAPACITY : RAT_ERR_INVALID_ARG;
+  if (T < 0 || t0 < 0 || T_cap > kMaxT) return RAT_ERR_INVALID_ARG;
+  if (t0 + T > T_cap) return RAT_ERR_CAPACITY;
   if (B == 0 || H == 0) return RAT_OK;
   ScanParams p;
   std::memset(&p, 0, sizeof(p));
@@ -154,13 +159,19 @@ int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* 
   if (st != RAT_OK) return st;
   if (state_k == nullptr || state_v == nullptr || !aligned16(state_k) || !aligned16(state_v))
     return RAT_ERR_INVALID_ARG;
+  if ((sk_in == nullptr) != (sv_in == nullptr)) return RAT_ERR_INVALID_ARG;
+  if (sk_in && (!aligned16(sk_in) || !aligned16(sv_in) || sk_in == state_k || sv_in == state_v ||
+                sk_in == state_v || sv_in == state_k))
+    return RAT_ERR_INVALID_ARG;  // the input state is read while the output is written
+  if (p.WS > 0 && (!k_ring || !v_ring || !aligned16(k_ring) || !aligned16(v_ring)))
+    return RAT_ERR_INVALID_ARG;
+  if ((kr_in == nullptr) != (vr_in == nullptr)) return RAT_ERR_INVALID_ARG;
+  if (kr_in && (!aligned16(kr_in) || !aligned16(vr_in))) return RAT_ERR_INVALID_ARG;
   if (T > 0) {
     if (!k || !v || !g || !aligned16(k) || !aligned16(v) || !aligned16(g)) return RAT_ERR_INVALID_ARG;
     if ((hk == nullptr) != (hv == nullptr)) return RAT_ERR_INVALID_ARG;
     if (hk && (!aligned16(hk) || !aligned16(hv))) return RAT_ERR_INVALID_ARG;
     if (p.R > 0 && (!Kc || !Vc || !aligned16(Kc) || !aligned16(Vc))) return RAT_ERR_INVALID_ARG;
-    if (p.WS > 0 && (!k_ring || !v_ring || !aligned16(k_ring) || !aligned16(v_ring)))
-      return RAT_ERR_INVALID_ARG;
     ScanLayout L;
     if (!scan_layout(B, H, T, hd, dtype, L)) return RAT_ERR_UNSUPPORTED;
     if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < L.bytes)
@@ -180,6 +191,7 @@ int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* 
   p.B = B;
   p.H = H;
   p.T = (int)T;
+  p.t0 = (int)t0;
   p.nseq = B * H;
   p.k = k;
   p.v = v;
@@ -192,16 +204,54 @@ int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* 
   p.vr = v_ring;
   p.sk = state_k;
   p.sv = state_v;
+  p.sk_in = sk_in;
+  p.sv_in = sv_in;
+  if (p.WS > 0 && t0 > 0 && kr_in != nullptr && kr_in != k_ring) {
+    // window positions before t0 that stay in the window: previous ring ->
+    // new ring (disjoint from the slots the scan writes)
+    st = map_hip(launch_ring_carry(dtype, hd, B, H, p.WS, p.ht, t0, T, kr_in, vr_in, k_ring,
+                                   v_ring, stream));
+    if (st != RAT_OK) return st;
+  }
   return map_hip(launch_scan(dtype, hd, p, stream));
 }
+}  // namespace
 
-int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* D,
-                             const int32_t* W, float scale, int64_t T_cap, const void* q,
-                             const void* hk, const void* hv, const void* Kc, const void* Vc,
-                             void* o, float* lse, void* stream) {
+int rat_scan_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* D,
+                     const int32_t* W, int64_t T_cap, const void* k, const void* v, const void* g,
+                     void* hk, void* hv, void* Kc, void* Vc, void* k_ring, void* v_ring,
+                     float* state_k, float* state_v, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return scan_impl(dtype, B, H, T, hd, D, W, T_cap, 0, k, v, g, nullptr, nullptr, hk, hv, Kc, Vc,
+                   nullptr, nullptr, k_ring, v_ring, state_k, state_v, workspace, workspace_bytes,
+                   stream);
+}
+
+int rat_scan_prefill_continue(int dtype, int B, int H, int64_t T, int hd, const int32_t* D,
+                              const int32_t* W, int64_t T_cap, int64_t t0, const void* k,
+                              const void* v, const void* g, const float* state_k_in,
+                              const float* state_v_in, void* hk, void* hv, void* Kc, void* Vc,
+                              const void* k_ring_in, const void* v_ring_in, void* k_ring,
+                              void* v_ring, float* state_k, float* state_v, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (state_k_in == nullptr || state_v_in == nullptr) return RAT_ERR_INVALID_ARG;
+  return scan_impl(dtype, B, H, T, hd, D, W, T_cap, t0, k, v, g, state_k_in, state_v_in, hk, hv,
+                   Kc, Vc, k_ring_in, v_ring_in, k_ring, v_ring, state_k, state_v, workspace,
+                   workspace_bytes, stream);
+}
+
+namespace {
+// Attention of queries [0, T) at absolute positions t0 .. t0+T-1.  Window
+// keys before t0 come from (kr_prev, vr_prev), the ring as it was before the
+// continuation's scan.
+int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, const int32_t* W,
+              float scale, int64_t T_cap, int64_t t0, const void* q, const void* hk,
+              const void* hv, const void* Kc, const void* Vc, const void* kr_prev,
+              const void* vr_prev, void* o, float* lse, void* stream) {
   int st = check_common(dtype, B, H, hd, D, W);
   if (st != RAT_OK) return st;
-  if (T < 0 || T_cap < T || T_cap > kMaxT) return T_cap < T ? RAT_ERR_CAPACITY : RAT_ERR_INVALID_ARG;
+  if (T < 0 || t0 < 0 || T_cap > kMaxT) return RAT_ERR_INVALID_ARG;
+  if (t0 + T > T_cap) return RAT_ERR_CAPACITY;
   if (!(scale <= 0.f) && !std::isfinite(scale)) return RAT_ERR_INVALID_ARG;
   if (B == 0 || H == 0 || T == 0) return RAT_OK;
   AttnParams p;
@@ -213,22 +263,27 @@ int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const i
     return RAT_ERR_INVALID_ARG;
   if (p.R > 0 && (!Kc || !Vc || !aligned16(Kc) || !aligned16(Vc))) return RAT_ERR_INVALID_ARG;
   if (lse && !aligned16(lse)) return RAT_ERR_INVALID_ARG;
+  if (t0 > 0 && WS > 0 && (!kr_prev || !vr_prev || !aligned16(kr_prev) || !aligned16(vr_prev)))
+    return RAT_ERR_INVALID_ARG;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)hd);
   p.B = B;
   p.H = H;
   p.T = (int)T;
+  p.t0 = (int)t0;
   // 16-query blocks per wave: 2 when the average query attends to many keys
   // (MFMA-bound: better operand reuse), else 1 (streaming-bound: fewer
   // registers, more waves in flight)
+  const int64_t tmid = t0 + T / 2;
   double avg_keys = 0.0;
   for (int h = 0; h < H; ++h)
-    avg_keys += (double)std::max<int64_t>(0, T - W[h]) / (2.0 * D[h]) + std::min<int64_t>(W[h], T);
+    avg_keys += (double)std::max<int64_t>(0, tmid - W[h]) / D[h] + std::min<int64_t>(W[h], tmid);
   avg_keys /= H;
   p.qb = avg_keys >= 512.0 ? 2 : 1;
   // resident-anchor kernel: bf16, no window, every head's anchors fit in LDS
   // (per-(b,h) output rows are addressed with 32-bit byte offsets there)
   bool resident = dtype == RAT_DTYPE_BF16 && T * hd * 2 <= INT32_MAX;
-  for (int h = 0; h < H && resident; ++h) resident = W[h] == 0 && (T - 1) / D[h] <= kResidentAnchors;
+  for (int h = 0; h < H && resident; ++h)
+    resident = W[h] == 0 && (t0 + T - 1) / D[h] <= kResidentAnchors;
   if (resident) {
     // about one workgroup per CU, at least one 16-query block per wave
     int dev = 0, cus = 0;
@@ -253,17 +308,20 @@ int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const i
   p.hv = hv;
   p.Kc = Kc;
   p.Vc = Vc;
+  p.kr = kr_prev;
+  p.vr = vr_prev;
+  p.WS = WS;
   p.o = o;
   p.lse = lse;
   // heads in descending cost of one pair-block (anchor tiles + band tiles of
   // the heaviest and the lightest query tile), so heavy heads start first
   const int bn = kAttnBN;
   auto tiles = [&](int h, int qt) -> int64_t {
-    const int64_t t0 = (int64_t)qt * bm;
-    const int64_t tl = std::min<int64_t>(t0 + bm - 1, T - 1);
+    const int64_t a0 = t0 + (int64_t)qt * bm;
+    const int64_t tl = t0 + std::min<int64_t>((int64_t)qt * bm + bm - 1, T - 1);
     const int64_t na = std::max<int64_t>(0, tl - W[h]) / D[h];
     int64_t n = (na + bn - 1) / bn + 1;
-    if (W[h] > 0) n += (tl - std::max<int64_t>(0, t0 - W[h]) + bn) / bn;
+    if (W[h] > 0) n += (tl - std::max<int64_t>(0, a0 - W[h]) + bn) / bn;
     return n;
   };
   int64_t cost[RAT_MAX_HEADS];
@@ -273,6 +331,25 @@ int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const i
   }
   std::stable_sort(p.perm, p.perm + H, [&](int a, int b) { return cost[a] > cost[b]; });
   return map_hip(launch_attn_prefill(dtype, hd, p, stream));
+}
+}  // namespace
+
+int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd, const int32_t* D,
+                             const int32_t* W, float scale, int64_t T_cap, const void* q,
+                             const void* hk, const void* hv, const void* Kc, const void* Vc,
+                             void* o, float* lse, void* stream) {
+  return attn_impl(dtype, B, H, T, hd, D, W, scale, T_cap, 0, q, hk, hv, Kc, Vc, nullptr, nullptr,
+                   o, lse, stream);
+}
+
+int rat_dilated_attn_prefill_continue(int dtype, int B, int H, int64_t T, int hd,
+                                      const int32_t* D, const int32_t* W, float scale,
+                                      int64_t T_cap, int64_t t0, const void* q, const void* hk,
+                                      const void* hv, const void* Kc, const void* Vc,
+                                      const void* k_ring_prev, const void* v_ring_prev, void* o,
+                                      float* lse, void* stream) {
+  return attn_impl(dtype, B, H, T, hd, D, W, scale, T_cap, t0, q, hk, hv, Kc, Vc, k_ring_prev,
+                   v_ring_prev, o, lse, stream);
 }
 
 namespace {

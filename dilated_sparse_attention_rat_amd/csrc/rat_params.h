@@ -28,6 +28,7 @@ constexpr int kScanMaxLevels = 10;
 
 struct ScanParams {
   int B, H, T;
+  int t0;          // absolute position of row 0 (continuation; 0 for a prefill)
   int nseq;        // B * H
   int nchunk;      // chunks per sequence
   int nticket;     // nseq * nchunk (= grid size)
@@ -47,6 +48,8 @@ struct ScanParams {
   void* vr;
   float* sk;
   float* sv;
+  const float* sk_in;  // state before row 0 (nullable: zero)
+  const float* sv_in;
   uint32_t* hdr;    // workspace header (kScanHeaderBytes)
   uint64_t* agg;    // [entries][3][hd]: (tag << 32 | fp32) of A, Bk, Bv
   HeadTables ht;
@@ -59,6 +62,7 @@ constexpr int kResidentWaves = 16;  // waves per resident-anchor workgroup
 
 struct AttnParams {
   int B, H, T;
+  int t0;            // absolute position of query / state row 0
   int mode;          // 0: streamed K/V tiles; 1: resident anchors
   int nra;           // mode 1: workgroups per (b, h)
   int qb;            // 16-query blocks per wave (1 or 2): tile = 64*qb queries
@@ -71,6 +75,9 @@ struct AttnParams {
   const void* hv;
   const void* Kc;
   const void* Vc;
+  const void* kr;    // ring of the positions before t0 (window keys < t0)
+  const void* vr;
+  int64_t WS;        // ring slots per batch row
   void* o;
   float* lse;        // nullable
   int32_t perm[kMaxHeads];  // heads in descending per-block cost
@@ -101,6 +108,11 @@ struct DecodeParams {
 
 // launchers (one per kernel family); return hipError_t as int
 int launch_scan(int dtype, int hd, const ScanParams& p, void* stream);
+// Continuation: copy the ring slots of positions [max(0, t0+T-W), t0) that
+// stay in the window from ring_in to ring_out (the scan writes the rest).
+int launch_ring_carry(int dtype, int hd, int B, int H, int64_t WS, const HeadTables& ht,
+                      int64_t t0, int64_t T, const void* kr_in, const void* vr_in, void* kr_out,
+                      void* vr_out, void* stream);
 int launch_attn_prefill(int dtype, int hd, const AttnParams& p, void* stream);
 int launch_decode(int dtype, int hd, const DecodeParams& p, void* stream);
 

@@ -286,7 +286,11 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
       }
     } else if (wave >= 2 && wave < 2 + NH) {
       const int half = wave - 2;
-      float one = 1.f, hin_k = 0.f, hin_v = 0.f;
+      // the state before row 0: zero for a prefill, the given state for a
+      // continuation; the nodes before this chunk are composed onto it
+      float one = 1.f;
+      float hin_k = p.sk_in != nullptr ? p.sk_in[(int64_t)seq * HD + 64 * half + lane] : 0.f;
+      float hin_v = p.sv_in != nullptr ? p.sv_in[(int64_t)seq * HD + 64 * half + lane] : 0.f;
       for (int lv = p.nlevels - 1; lv >= 0; --lv) {
         const int64_t nd = (int64_t)chunk >> (kScanRadixLog2 * lv);
         const int64_t first = nd & ~(int64_t)(kScanRadix - 1);
@@ -319,8 +323,9 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
     ST* vrp = reinterpret_cast<ST*>(p.vr);
     const int64_t arow0 = (int64_t)b * p.R + p.ht.aoff[h];
     const int64_t rrow0 = (int64_t)b * p.WS + p.ht.roff[h];
-    int aq = tbase / D;             // anchor index candidate of row tbase
-    int ar = tbase - aq * D;        // phase of row tbase
+    const int tabs = p.t0 + tbase;  // absolute position of row tbase
+    int aq = tabs / D;              // anchor index candidate of row tbase
+    int ar = tabs - aq * D;         // phase of row tbase
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int t = tbase + s;
@@ -347,7 +352,7 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
           st_raw16(Vcp + off, ov);
         }
         if (W > 0 && t >= T - W) {
-          const int64_t off = (rrow0 + (t % W)) * HD + c0;
+          const int64_t off = (rrow0 + ((p.t0 + t) % W)) * HD + c0;
           st_raw16(krp + off, ok);
           st_raw16(vrp + off, ov);
         }
@@ -436,13 +441,39 @@ void scan_kernel(const ScanParams p) {
   }
 }
 
-// T = 0: the state is h_{-1} = 0
-__global__ void zero_state_kernel(float* sk, float* sv, int64_t n) {
+// T = 0: the state is the state before row 0 (zero for a prefill)
+__global__ void state_init_kernel(float* sk, float* sv, const float* sk_in, const float* sv_in,
+                                  int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
-    sk[i] = 0.f;
-    sv[i] = 0.f;
+    sk[i] = sk_in != nullptr ? sk_in[i] : 0.f;
+    sv[i] = sv_in != nullptr ? sv_in[i] : 0.f;
   }
+}
+
+// Continuation ring carry: the slot of each position p in
+// [max(0, t0 + T - W), t0) -- still inside the window after the continuation
+// and not rewritten by it -- is copied from the previous ring to the new
+// one.  Grid: (chunks of one head's slots, H, B); one 16-byte chunk each.
+template <typename ST, int HD>
+__global__ void ring_carry_kernel(const ST* __restrict__ kin, const ST* __restrict__ vin, ST* kout,
+                                  ST* vout, HeadTables ht, int64_t WS, int64_t t0, int64_t T) {
+  constexpr int VEC = StTraits<ST>::VEC;
+  constexpr int CPR = HD / VEC;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t W = ht.W[h];
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= W * CPR) return;
+  const int64_t slot = idx / CPR;
+  const int c16 = (int)(idx - slot * CPR);
+  // the position held by this slot before the continuation: the last p < t0
+  // with p = slot (mod W)
+  const int64_t p = t0 - 1 - (((t0 - 1 - slot) % W) + W) % W;
+  if (p < 0 || p < t0 + T - W) return;
+  const int64_t off = ((int64_t)b * WS + ht.roff[h] + slot) * HD + c16 * VEC;
+  st_raw16(kout + off, ld_raw16(kin + off));
+  st_raw16(vout + off, ld_raw16(vin + off));
 }
 
 // Largest grid whose workgroups can all be resident at once (cached per
@@ -469,8 +500,8 @@ int launch_scan_t(const ScanParams& p, hipStream_t st) {
   if (p.T == 0) {
     const int64_t n = (int64_t)p.nseq * HD;
     if (n == 0) return 0;
-    hipLaunchKernelGGL(zero_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       p.sk, p.sv, n);
+    hipLaunchKernelGGL(state_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       p.sk, p.sv, p.sk_in, p.sv_in, n);
     return (int)hipGetLastError();
   }
   const void* kern = reinterpret_cast<const void*>(&scan_kernel<ST, HD, kScanRowsPerThread>);
@@ -494,6 +525,31 @@ int scan_rows_per_chunk(int dtype, int hd) {
   const int vec = dtype == RAT_DTYPE_BF16 ? 8 : 4;
   const int lpr = hd / vec;
   return (kScanThreads / lpr) * kScanRowsPerThread;
+}
+
+template <typename ST, int HD>
+int launch_ring_carry_t(int B, int H, int64_t WS, const HeadTables& ht, int64_t t0, int64_t T,
+                        const void* kin, const void* vin, void* kout, void* vout, hipStream_t st) {
+  constexpr int CPR = HD / StTraits<ST>::VEC;
+  int64_t wmax = 0;
+  for (int h = 0; h < H; ++h) wmax = std::max<int64_t>(wmax, ht.W[h]);
+  if (wmax == 0 || t0 == 0 || B == 0 || H == 0) return 0;
+  const dim3 grid((unsigned)((wmax * CPR + 255) / 256), (unsigned)H, (unsigned)B);
+  hipLaunchKernelGGL((ring_carry_kernel<ST, HD>), grid, dim3(256), 0, st,
+                     reinterpret_cast<const ST*>(kin), reinterpret_cast<const ST*>(vin),
+                     reinterpret_cast<ST*>(kout), reinterpret_cast<ST*>(vout), ht, WS, t0, T);
+  return (int)hipGetLastError();
+}
+
+int launch_ring_carry(int dtype, int hd, int B, int H, int64_t WS, const HeadTables& ht,
+                      int64_t t0, int64_t T, const void* kr_in, const void* vr_in, void* kr_out,
+                      void* vr_out, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == RAT_DTYPE_BF16)
+    return hd == 128 ? launch_ring_carry_t<bf16, 128>(B, H, WS, ht, t0, T, kr_in, vr_in, kr_out, vr_out, st)
+                     : launch_ring_carry_t<bf16, 64>(B, H, WS, ht, t0, T, kr_in, vr_in, kr_out, vr_out, st);
+  return hd == 128 ? launch_ring_carry_t<float, 128>(B, H, WS, ht, t0, T, kr_in, vr_in, kr_out, vr_out, st)
+                   : launch_ring_carry_t<float, 64>(B, H, WS, ht, t0, T, kr_in, vr_in, kr_out, vr_out, st);
 }
 
 int launch_scan(int dtype, int hd, const ScanParams& p, void* stream) {

@@ -150,6 +150,68 @@ int rat_dilated_attn_prefill(int dtype, int B, int H, int64_t T, int hd,
                              void* o, float* lse, void* stream);
 
 /*
+ * Chunked prefill: the recurrence of a chunk of T positions that follows
+ * t0 positions already processed (deep dive, section 2.1: the recurrent
+ * state is carried along the whole sequence; abstract: anchor-only cache).
+ * Position t of the chunk is absolute position t0 + t; the result equals
+ * rat_scan_prefill over the t0 + T positions, restricted to the chunk.
+ *
+ * Reads  k, v, g                [B, H, T, hd] ST: the chunk
+ *        state_k_in, state_v_in [B, H, hd] fp32: h_{t0-1} (the state after
+ *                               the previous chunk, or zeros when t0 = 0);
+ *                               must not alias state_k / state_v
+ *        k_ring_in, v_ring_in   [B, sum W, hd] ST: the ring after the
+ *                               previous chunk (nullable when all W = 0 or
+ *                               t0 = 0).  When it is not k_ring/v_ring, the
+ *                               slots of positions max(0, t0+T-W) .. t0-1
+ *                               are copied from it into k_ring/v_ring first.
+ * Writes hk, hv           [B, H, T, hd] ST: h of the chunk's positions (both
+ *                         NULL = cache-only mode)
+ *        Kc, Vc           rows a with t0 <= a*D + D-1 < t0 + T (other rows,
+ *                         from earlier chunks, untouched)
+ *        k_ring, v_ring   slots of positions max(0, t0+T-W) .. t0+T-1
+ *        state_k, state_v h_{t0+T-1} (the input state when T = 0)
+ * Requires t0 >= 0, T >= 0, t0 + T <= T_cap (else RAT_ERR_CAPACITY).
+ * Updating the ring in place (k_ring_in == k_ring) is valid for the scan,
+ * but it overwrites window positions before t0 that the chunk's attention
+ * reads: keep the previous ring in a second buffer for
+ * rat_dilated_attn_prefill_continue (two rings used alternately).
+ * workspace: rat_scan_workspace_bytes(B, H, T, hd), as for rat_scan_prefill.
+ */
+int rat_scan_prefill_continue(int dtype, int B, int H, int64_t T, int hd,
+                              const int32_t* D, const int32_t* W, int64_t T_cap,
+                              int64_t t0, const void* k, const void* v,
+                              const void* g, const float* state_k_in,
+                              const float* state_v_in, void* hk, void* hv,
+                              void* Kc, void* Vc, const void* k_ring_in,
+                              const void* v_ring_in, void* k_ring,
+                              void* v_ring, float* state_k, float* state_v,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Chunked prefill attention: queries of a chunk at absolute positions
+ * t0 .. t0+T-1 over the key sets of rat_dilated_attn_prefill (abstract;
+ * deep dive, sections 一, 2.2).  Anchors come from Kc/Vc (all chunks so far,
+ * after rat_scan_prefill_continue of this chunk); window positions >= t0
+ * and the own position from hk/hv of the chunk [B, H, T, hd]; window
+ * positions < t0 from k_ring_prev/v_ring_prev [B, sum W, hd], the ring as
+ * it was after the previous chunk (required when t0 > 0 and some W > 0,
+ * else nullable).  Writes o [B, H, T, hd] ST, lse [B, H, T] fp32
+ * (nullable).  Requires t0 + T <= T_cap (else RAT_ERR_CAPACITY).
+ */
+int rat_dilated_attn_prefill_continue(int dtype, int B, int H, int64_t T,
+                                      int hd, const int32_t* D,
+                                      const int32_t* W, float scale,
+                                      int64_t T_cap, int64_t t0,
+                                      const void* q, const void* hk,
+                                      const void* hv, const void* Kc,
+                                      const void* Vc,
+                                      const void* k_ring_prev,
+                                      const void* v_ring_prev, void* o,
+                                      float* lse, void* stream);
+
+/*
  * Bytes of device workspace rat_decode_step needs for any pos < T_cap with
  * num_splits (0 = automatic choice).  0 means no workspace is needed
  * (the single-split path).  Pure host function; negative on error.

@@ -156,6 +156,43 @@ def test_attention_validation(L):
     assert _attn(L, B=0) == rb.RAT_OK
 
 
+def _scan_c(L, B=1, H=2, T=8, hd=64, D=4, W=0, T_cap=16, t0=8, sin=FAKE + 4096, sout=FAKE,
+            rin=0, ring=FAKE):
+    d, w, dp, wp = _tables(H, D, W)
+    return L.rat_scan_prefill_continue(0, B, H, T, hd, dp, wp, T_cap, t0, _p(), _p(), _p(),
+                                       _p(sin), _p(sin), _p(), _p(), _p(), _p(),
+                                       _p(rin) if rin else None, _p(rin) if rin else None,
+                                       _p(ring), _p(ring), _p(sout), _p(sout), _p(), 1 << 30,
+                                       None)
+
+
+def test_scan_continue_validation(L):
+    assert _scan_c(L, t0=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _scan_c(L, t0=10) == rb.RAT_ERR_CAPACITY                # t0 + T > T_cap
+    assert _scan_c(L, sin=0) == rb.RAT_ERR_INVALID_ARG             # input state required
+    assert _scan_c(L, sin=FAKE) == rb.RAT_ERR_INVALID_ARG          # aliases the output state
+    assert _scan_c(L, sin=FAKE + 4100) == rb.RAT_ERR_INVALID_ARG   # misaligned
+    assert _scan_c(L, W=4, rin=FAKE + 8) == rb.RAT_ERR_INVALID_ARG
+    assert _scan_c(L, B=0) == rb.RAT_OK
+
+
+def _attn_c(L, B=1, H=2, T=8, hd=64, D=4, W=0, T_cap=16, t0=8, rprev=0):
+    d, w, dp, wp = _tables(H, D, W)
+    return L.rat_dilated_attn_prefill_continue(0, B, H, T, hd, dp, wp, 0.0, T_cap, t0, _p(),
+                                               _p(), _p(), _p(), _p(),
+                                               _p(rprev) if rprev else None,
+                                               _p(rprev) if rprev else None, _p(), None, None)
+
+
+def test_attention_continue_validation(L):
+    assert _attn_c(L, t0=-2) == rb.RAT_ERR_INVALID_ARG
+    assert _attn_c(L, t0=9) == rb.RAT_ERR_CAPACITY
+    assert _attn_c(L, W=4) == rb.RAT_ERR_INVALID_ARG               # window keys before t0
+    assert _attn_c(L, W=4, rprev=FAKE + 2) == rb.RAT_ERR_INVALID_ARG
+    assert _attn_c(L, T=0) == rb.RAT_OK
+    assert _attn_c(L, B=0) == rb.RAT_OK
+
+
 def _dec(L, dtype=0, B=1, H=2, hd=64, D=4, W=0, pos=5, T_cap=16, splits=0, ws=0, ws_bytes=0,
          q=FAKE):
     d, w, dp, wp = _tables(H, D, W)
