@@ -70,12 +70,13 @@ struct Prefetch {
   u32x4 k[C::KPT];
   u32x4 v[C::VPT][4];
 
-  // Rows [0, BN) of the tile (nvalid >= 1); rows(r) gives the K and V row
-  // pointers of tile row r.  Rows at or beyond nvalid re-read row nvalid-1:
-  // such keys are always masked (weight exactly 0) and the duplicated V row
-  // is finite, so they contribute nothing, and the loads need no branches.
+  // Rows [0, BN) of the tile (nvalid >= 1); rows.k(r) / rows.v(r) give the
+  // K and V row pointers of tile row r.  Rows at or beyond nvalid re-read row
+  // nvalid-1: such keys are always masked (weight exactly 0) and the
+  // duplicated V row is finite, so they contribute nothing, and the loads
+  // need no branches.
   template <typename Rows>
-  __device__ __forceinline__ void load(Rows rows, int nvalid) {
+  __device__ __forceinline__ void load(const Rows& rows, int nvalid) {
     const int tid = threadIdx.x;
     const int last = nvalid - 1;
 #pragma unroll
@@ -289,30 +290,26 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
   }
 }
 
-// Key rows of one staged tile.  Anchor tiles read the anchor cache; band
-// tiles read the states of positions key0 .. key0+BN-1: rows of this call
-// (position >= t0) from hk/hv, earlier positions (a continuation's window
-// reaching before t0) from the ring of the previous call, slot p mod W.
+// Key rows of one staged tile.  Anchor tiles, and band tiles at positions
+// >= t0, are linear: row r at kh + r*HD (n2 = 0).  A band tile that starts
+// before t0 (a continuation's window reaching into the previous call) reads
+// its first n2 = t0 - key0 rows (at most W) from the previous call's ring,
+// slot = position mod W: row r < n2 at kr + r*HD, where kr points at the
+// slot of key0, minus W rows once the slot wraps (r >= n1); rows r >= n2 at
+// kh + r*HD (kh = this call's row 0 minus n2 rows).  The selection is
+// branch-free on scalars, so every tile issues the same global loads.
 template <typename ST, int HD>
-struct TileRows {
-  const ST* ka;  // anchors: row r at ka + r*HD (key0 folded in)
-  const ST* va;
-  const ST* hk;  // band: states of this call, position p at (p - t0)
-  const ST* hv;
-  const ST* rk;  // band: ring of the previous call
-  const ST* rv;
-  int key0, t0, W;
-  bool band;
-  __device__ __forceinline__ const ST* k(int r) const {
-    if (!band) return ka + (int64_t)r * HD;
-    const int pos = key0 + r;
-    return pos >= t0 ? hk + (int64_t)(pos - t0) * HD : rk + (int64_t)(pos % W) * HD;
+struct RowMap {
+  const ST* kh;
+  const ST* vh;
+  const ST* kr;
+  const ST* vr;
+  int n1, n2, W;
+  __device__ __forceinline__ int64_t row(int r) const {
+    return (int64_t)(r >= n1 && r < n2 ? r - W : r) * HD;
   }
-  __device__ __forceinline__ const ST* v(int r) const {
-    if (!band) return va + (int64_t)r * HD;
-    const int pos = key0 + r;
-    return pos >= t0 ? hv + (int64_t)(pos - t0) * HD : rv + (int64_t)(pos % W) * HD;
-  }
+  __device__ __forceinline__ const ST* k(int r) const { return (r < n2 ? kr : kh) + row(r); }
+  __device__ __forceinline__ const ST* v(int r) const { return (r < n2 ? vr : vh) + row(r); }
 };
 
 // One query tile of 64*QB queries at local row lt0 (absolute position
@@ -321,7 +318,7 @@ struct TileRows {
 // `qnext` right after they are consumed here, so their HBM latency overlaps
 // this tile's key loop.  Positions (queries, band keys, anchors) are
 // absolute; rows of q, hk, hv, o and lse are local to this call.
-template <typename ST, int HD, int QB>
+template <typename ST, int HD, int QB, bool RING>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, int lt0, ST* sK,
                                              ST* sVt, const QueryIn<ST, HD, QB>& qin,
                                              QueryIn<ST, HD, QB>& qnext, int next_lt0) {
@@ -343,8 +340,9 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   const ST* kcp = reinterpret_cast<const ST*>(p.Kc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;
   const ST* vcp = reinterpret_cast<const ST*>(p.Vc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;
   const int64_t rofs = ((int64_t)b * p.WS + p.ht.roff[h]) * HD;
-  const ST* rkp = p.kr != nullptr ? reinterpret_cast<const ST*>(p.kr) + rofs : nullptr;
-  const ST* rvp = p.vr != nullptr ? reinterpret_cast<const ST*>(p.vr) + rofs : nullptr;
+  // previous call's ring (only read when t0 > 0 and W > 0, where it is set)
+  const ST* rkp = reinterpret_cast<const ST*>(p.kr) + rofs;
+  const ST* rvp = reinterpret_cast<const ST*>(p.vr) + rofs;
 
   const int tw0 = lt0 + QW * wave;             // first query of this wave (local)
   const bool wave_active = tw0 < T;
@@ -358,36 +356,40 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   const int na_t = (n_end + C::BN - 1) / C::BN;
   const int nb_t = W > 0 ? (alast_blk - jb0 + C::BN) / C::BN : 0;
   const int n_items = na_t + nb_t;
-  auto item_src = [&](int i, TileRows<ST, HD>& rows, int& nvalid, int& key0) {
-    rows.hk = hkp;
-    rows.hv = hvp;
-    rows.rk = rkp;
-    rows.rv = rvp;
-    rows.t0 = a0;
-    rows.W = max(W, 1);
+  // key tile i: its rows, first key position and number of valid rows
+  auto item_src = [&](int i, RowMap<ST, HD>& rows, int& nvalid, int& key0) {
+    rows.n1 = rows.n2 = 0;
+    rows.W = W;
     if (i < na_t) {
       key0 = i * C::BN;
-      rows.band = false;
-      rows.ka = kcp + (int64_t)key0 * HD;
-      rows.va = vcp + (int64_t)key0 * HD;
+      rows.kh = kcp + (int64_t)key0 * HD;
+      rows.vh = vcp + (int64_t)key0 * HD;
       nvalid = n_end - key0;
     } else {
       key0 = jb0 + (i - na_t) * C::BN;
-      rows.band = true;
-      rows.ka = kcp;
-      rows.va = vcp;
+      rows.kh = hkp + (int64_t)(key0 - a0) * HD;  // rows before t0: ring
+      rows.vh = hvp + (int64_t)(key0 - a0) * HD;
       nvalid = alast_blk + 1 - key0;
     }
-    rows.key0 = key0;
+    rows.kr = rows.kh;
+    rows.vr = rows.vh;
+    if (RING && i >= na_t && key0 < a0) {
+      const int s0 = key0 % W;
+      rows.n2 = a0 - key0;
+      rows.n1 = min(rows.n2, W - s0);
+      rows.kr = rkp + (int64_t)s0 * HD;
+      rows.vr = rvp + (int64_t)s0 * HD;
+    }
+  };
+  auto load_item = [&](Prefetch<ST, HD, QB>& pf, int i) {
+    RowMap<ST, HD> rows;
+    int nv, k0;
+    item_src(i, rows, nv, k0);
+    pf.load(rows, nv);
   };
 
   Prefetch<ST, HD, QB> pf;
-  if (n_items > 0) {
-    TileRows<ST, HD> rows;
-    int nv, k0;
-    item_src(0, rows, nv, k0);
-    pf.load(rows, nv);
-  }
+  if (n_items > 0) load_item(pf, 0);
 
   // own position folded into the initial state (m = its score, from the
   // unscaled q in fp32; l = 1; acc = its value row).  The MFMA operand is Q
@@ -421,12 +423,9 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
     __syncthreads();  // every wave is done reading the previous tile
     pf.store(sK, sVt);
     __syncthreads();
-    TileRows<ST, HD> rows;
+    if (i + 1 < n_items) load_item(pf, i + 1);  // overlaps this tile's MFMAs
+    RowMap<ST, HD> rows;
     int nv, key0;
-    if (i + 1 < n_items) {  // next tile's loads overlap this tile's MFMAs
-      item_src(i + 1, rows, nv, key0);
-      pf.load(rows, nv);
-    }
     item_src(i, rows, nv, key0);
     const int kind = i < na_t ? 0 : 1;
     bool part, need_mask;
@@ -462,8 +461,10 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
 
 // Occupancy target: 2 waves per SIMD (two workgroups per CU) for both QB, so
 // one workgroup's MFMAs overlap the other's staging and softmax (QB = 2 fits
-// the resulting 256-register budget without spills).
-template <typename ST, int HD, int QB>
+// the resulting 256-register budget without spills).  RING: a continuation
+// whose window reaches before t0 (band rows from the previous call's ring);
+// without it the band tiles are plain linear reads.
+template <typename ST, int HD, int QB, bool RING>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_kernel(const AttnParams p) {
   using C = AttnCfg<ST, HD, QB>;
@@ -494,10 +495,10 @@ void attn_prefill_kernel(const AttnParams p) {
   // QB = 1 (streaming-bound): the partner tile's query inputs are loaded
   // while the first tile runs; QB = 2 has no registers to spare for that
   const bool pre = QB == 1 && ntiles == 2;
-  process_tile<ST, HD, QB>(p, b, h, qa * C::BM, sK, sVt, q0, q1, pre ? pr * C::BM : -1);
+  process_tile<ST, HD, QB, RING>(p, b, h, qa * C::BM, sK, sVt, q0, q1, pre ? pr * C::BM : -1);
   if (ntiles == 2) {
     if (!pre) q1.load(qp, hkp, hvp, pr * C::BM + 16 * QB * wave, p.T);
-    process_tile<ST, HD, QB>(p, b, h, pr * C::BM, sK, sVt, q1, q0, -1);
+    process_tile<ST, HD, QB, RING>(p, b, h, pr * C::BM, sK, sVt, q1, q0, -1);
   }
 }
 
@@ -662,10 +663,20 @@ int launch_t(const AttnParams& p, hipStream_t st) {
   }
   const int64_t nblk = (int64_t)p.H * p.B * p.np;
   if (nblk == 0) return 0;
-  if (p.qb == 2)
-    hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 2>), dim3((unsigned)nblk), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 1>), dim3((unsigned)nblk), dim3(256), 0, st, p);
+  // the ring-reading variant only where a window reaches before t0
+  const bool ring = p.t0 > 0 && p.WS > 0;
+  const dim3 grid((unsigned)nblk), block(256);
+  if (p.qb == 2) {
+    if (ring)
+      hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 2, true>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 2, false>), grid, block, 0, st, p);
+  } else {
+    if (ring)
+      hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 1, true>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 1, false>), grid, block, 0, st, p);
+  }
   return (int)hipGetLastError();
 }
 
