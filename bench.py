@@ -1,6 +1,6 @@
 """Benchmark of the RAT+ hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--graph]
                     [--no-cpu-baseline] [--no-decode-workload] [--calibration-copy MIB]
 
 A step is one pass of the whole hot path over one batch of the prefill
@@ -12,10 +12,18 @@ timed region, and alternate between two copies so no step re-reads the
 previous step's data from the 256 MB last-level cache.
 
 Printed: ONE JSON line.  ``value`` is prefill tokens per second of the whole
-step, B*T / (time of scan + attention + decode step).  Per-kernel times come
-from HIP events recorded on the stream the kernels are launched on.  The
+step, B*T / (wall time of K steps / K), the K steps bracketed by device
+synchronisations; the three launches of a step are enqueued one by one
+(``--graph``: captured once into a HIP graph per input copy and replayed,
+which measured slightly slower here).
+Per-kernel times come from a second, instrumented pass of K eager steps with
+HIP events recorded between the kernels on the stream they are launched on
+(the event markers themselves cost a few microseconds per step, which is why
+they are kept out of the pass that gives ``value``).  The
 decode-step time of the metric is measured on the decode workload (batch 64,
-32 heads, context 32768, D=64, W=128, 256 steps) and reported beside it.
+32 heads, context 32768, D=64, W=128, 256 steps) and reported beside it, as
+is a chunked prefill (the long-prefill workload in four chunks through the
+continuation entry points, against the same sequence in one call).
 ``roofline`` is for the kernel that takes the most time in the step;
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
 """
@@ -44,8 +52,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph instead of three launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-workload", action="store_true")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked-prefill measurement (long-prefill workload in chunks)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -210,14 +222,40 @@ def main():
         step(sets[i % 2])
     torch.cuda.synchronize()
 
+    # one graph per input copy: the step's three launches, replayed as a unit
+    graphs = None
+    if args.graph:
+        graphs = []
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(s)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
+
+    # ---- timed pass: K steps, no instrumentation --------------------------
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(sets[i % 2], evs[i])
+        if graphs is not None:
+            graphs[i % 2].replay()
+        else:
+            step(sets[i % 2])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # ---- instrumented pass: K eager steps with HIP events between kernels --
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % 2], evs[i])
+    torch.cuda.synchronize()
+    wall_instr = time.perf_counter() - t1
+    del graphs
     scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
@@ -242,7 +280,7 @@ def main():
                     kernel="scan_kernel", traffic=traffic_from_profiles("scan.hip", f"scan_w{args.workload}"))
     else:
         roof = dict(bound="hbm", achieved=kernels["attention"]["gbs"], peak=HBM_PEAK_GBS,
-                    unit="GB/s", kernel="attn_prefill_kernel",
+                    unit="GB/s", kernel=attn_kernel_name(w),
                     traffic=traffic_from_profiles("attn_prefill.hip", f"attn_w{args.workload}"))
     roof["frac"] = roof["achieved"] / roof["peak"]
     kernels["attention"]["mfma_frac_useful"] = kernels["attention"]["tflops"] / MFMA_BF16_PEAK_TFLOPS
@@ -253,6 +291,9 @@ def main():
     decode_info = None
     if not args.no_decode_workload:
         decode_info = bench_decode_workload(rat, synth, torch, np)
+    chunked_info = None
+    if not args.no_chunked:
+        chunked_info = bench_chunked(rat, synth, torch, np)
 
     del sets
     torch.cuda.empty_cache()
@@ -270,6 +311,8 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_instrumented": wall_instr * 1e3 / K,
+        "launch": "hip graph per step" if args.graph else "eager",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -288,10 +331,20 @@ def main():
         "decode_us_per_step": decode_info["us_mean"] if decode_info else None,
         "kernels": kernels,
         "decode_workload": decode_info,
+        "chunked_prefill": chunked_info,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def attn_kernel_name(w) -> str:
+    """The attention kernel the library picks for this workload: the
+    resident-anchor kernel for bf16 windowless heads whose anchors fit in LDS
+    (at most 256 per head), else the streaming kernel."""
+    resident = (w.dtype == "bf16" and w.T * w.hd * 2 <= 2 ** 31 - 1
+                and all(wh == 0 and (w.T - 1) // d <= 256 for d, wh in zip(w.D, w.W)))
+    return "attn_resident_kernel" if resident else "attn_prefill_kernel"
 
 
 def bench_decode_workload(rat, synth, torch, np):
@@ -329,6 +382,86 @@ def bench_decode_workload(rat, synth, torch, np):
                bytes_mean=float(nbytes.mean()), gbs_mean=float(gbs.mean()),
                hbm_frac=float(gbs.mean() / HBM_PEAK_GBS), steps=steps)
     del cache, inputs
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_chunked(rat, synth, torch, np, reps=5, nchunks=4):
+    """Chunked prefill of the long-prefill workload (T=16384, D=64, W=256):
+    the sequence in nchunks equal chunks through the continuation entry
+    points (two rings used alternately), against the same sequence in one
+    call.  Times are HIP-event medians over reps repetitions."""
+    w = synth.WORKLOADS[2]
+    B, H, T, hd = w.B, w.H, w.T, w.hd
+    D, W = list(w.D), list(w.W)
+    x = synth.prefill_inputs(w)
+    t = {n: torch.from_numpy(x[n]).to("cuda").to(torch.bfloat16) for n in "qkvg"}
+    del x
+    Tc = T // nchunks
+    ch = [{n: t[n][:, :, i * Tc:(i + 1) * Tc].contiguous() for n in "qkvg"} for i in range(nchunks)]
+    c = rat.alloc_cache(B, H, hd, T, D, W, torch.bfloat16, "cuda")
+    rings = [(c["k_ring"], c["v_ring"]), (torch.empty_like(c["k_ring"]), torch.empty_like(c["v_ring"]))]
+    states = [(c["state_k"], c["state_v"]), (torch.zeros_like(c["state_k"]), torch.zeros_like(c["state_v"]))]
+    hk, hv = torch.empty_like(ch[0]["k"]), torch.empty_like(ch[0]["v"])
+    o = torch.empty_like(ch[0]["q"])
+    ws = rat.scan_workspace(B, H, Tc, hd, "cuda")
+    hk_f, hv_f, o_f = torch.empty_like(t["k"]), torch.empty_like(t["v"]), torch.empty_like(t["q"])
+    ws_f = rat.scan_workspace(B, H, T, hd, "cuda")
+    stream = torch.cuda.current_stream()
+
+    def chunked(ev=None):
+        for i in range(nchunks):
+            cur, prev = rings[i % 2], rings[1 - i % 2]
+            sc, sp = states[i % 2], states[1 - i % 2]
+            if ev is not None:
+                ev[2 * i].record(stream)
+            if i == 0:
+                rat.rat_scan_prefill(ch[0]["k"], ch[0]["v"], ch[0]["g"], D, W, T, c["Kc"], c["Vc"],
+                                     sc[0], sc[1], ws, hk=hk, hv=hv, k_ring=cur[0], v_ring=cur[1])
+                rat.rat_dilated_attn_prefill(ch[0]["q"], hk, hv, c["Kc"], c["Vc"], D, W, T, o)
+            else:
+                rat.rat_scan_prefill_continue(ch[i]["k"], ch[i]["v"], ch[i]["g"], D, W, T, i * Tc,
+                                              sp[0], sp[1], c["Kc"], c["Vc"], sc[0], sc[1], ws,
+                                              hk=hk, hv=hv, k_ring_in=prev[0], v_ring_in=prev[1],
+                                              k_ring=cur[0], v_ring=cur[1])
+                rat.rat_dilated_attn_prefill_continue(ch[i]["q"], hk, hv, c["Kc"], c["Vc"], D, W, T,
+                                                      i * Tc, o, k_ring_prev=prev[0],
+                                                      v_ring_prev=prev[1])
+            if ev is not None:
+                ev[2 * i + 1].record(stream)
+
+    def whole():
+        rat.rat_scan_prefill(t["k"], t["v"], t["g"], D, W, T, c["Kc"], c["Vc"], c["state_k"],
+                             c["state_v"], ws_f, hk=hk_f, hv=hv_f, k_ring=c["k_ring"],
+                             v_ring=c["v_ring"])
+        rat.rat_dilated_attn_prefill(t["q"], hk_f, hv_f, c["Kc"], c["Vc"], D, W, T, o_f)
+
+    chunked()
+    whole()
+    torch.cuda.synchronize()
+    per_chunk = []
+    tot_chunked, tot_whole = [], []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nchunks)]
+        chunked(ev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        whole()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = [ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(nchunks)]
+        per_chunk.append(us)
+        tot_chunked.append(sum(us))
+        tot_whole.append(e0.elapsed_time(e1) * 1e3)
+    med = lambda a: float(np.median(a))
+    res = dict(workload=f"{w.name}: B={B} H={H} hd={hd} T={T} D={D[0]} W={W[0]} in {nchunks} "
+                        f"chunks of {Tc}",
+               us_per_chunk=[med([r[i] for r in per_chunk]) for i in range(nchunks)],
+               us_chunked=med(tot_chunked), us_whole=med(tot_whole),
+               tok_s_chunked=B * T / (med(tot_chunked) * 1e-6),
+               tok_s_whole=B * T / (med(tot_whole) * 1e-6))
+    assert int(ws[2].item()) == 0 and int(ws_f[2].item()) == 0, "scan wait timed out"
+    del t, ch, c, rings, states, hk, hv, o, hk_f, hv_f, o_f
     torch.cuda.empty_cache()
     return res
 
