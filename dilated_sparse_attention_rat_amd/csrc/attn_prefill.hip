@@ -250,8 +250,7 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
     for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, S[mb][nb][i]);
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+    tmax = xor16_32_max(tmax);
     const bool grow = tmax > kRescaleSlack;
     if (__any(grow)) {
       const float delta = grow ? tmax : 0.f;
@@ -407,8 +406,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
       d += frag_dot(qin.q[nb][s], qin.k[nb][s]);
       ws.qf[nb][s] = frag_scale(qin.q[nb][s], p.scale_log2);
     }
-    d += shfl_xor_f(d, 16);
-    d += shfl_xor_f(d, 32);
+    d = xor16_32_sum(d);
     ws.m[nb] = d * p.scale_log2;
     ws.l[nb] = (g == 0) ? 1.f : 0.f;
 #pragma unroll
@@ -445,9 +443,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   ST* op = reinterpret_cast<ST*>(p.o) + bh * T * HD;
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
-    float lt = ws.l[nb];
-    lt += shfl_xor_f(lt, 16);
-    lt += shfl_xor_f(lt, 32);
+    const float lt = xor16_32_sum(ws.l[nb]);
     const int t = ws.tq[nb] - a0;  // local row
     if (t < T) {
       const float inv = 1.f / lt;
@@ -538,8 +534,7 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
     d += frag_dot(qin.q[0][s], qin.k[0][s]);
     ws.qf[0][s] = frag_scale(qin.q[0][s], p.scale_log2);
   }
-  d += shfl_xor_f(d, 16);
-  d += shfl_xor_f(d, 32);
+  d = xor16_32_sum(d);
   ws.m[0] = d * p.scale_log2;
   ws.l[0] = (g == 0) ? 1.f : 0.f;
 #pragma unroll
@@ -549,9 +544,7 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   for (int key0 = 0; key0 < n_end; key0 += C::BN)
     tile_update<ST, HD, 1, VS>(ws, sK + key0 * C::KSTR, sVt + key0, key0, 0, key0 + C::BN > w_full, 0);
 
-  float lt = ws.l[0];
-  lt += shfl_xor_f(lt, 16);
-  lt += shfl_xor_f(lt, 32);
+  const float lt = xor16_32_sum(ws.l[0]);
   const int t = ws.tq[0] - a0;  // local row
   const float inv = 1.f / lt;
   // buffer stores: lanes of rows past T (and the lse of lanes g > 0, or a

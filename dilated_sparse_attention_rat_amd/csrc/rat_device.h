@@ -242,4 +242,24 @@ __device__ __forceinline__ void buffer_st4(__amdgpu_buffer_rsrc_t r, uint32_t of
 // cross-lane helpers (wave64)
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Max / sum of v over lanes {i, i^16, i^32, i^48} on the VALU, no LDS round
+// trip: with both operands equal to x, v_permlane16_swap returns x at lanes
+// i and i^16 in its two outputs, and v_permlane32_swap x at i and i^32.
+__device__ __forceinline__ float xor16_32_max(float v) {
+  const uint32_t a = __float_as_uint(v);
+  const u32x2 r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const uint32_t b = __float_as_uint(v);
+  const u32x2 t = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float xor16_32_sum(float v) {
+  const uint32_t a = __float_as_uint(v);
+  const u32x2 r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const uint32_t b = __float_as_uint(v);
+  const u32x2 t = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 }  // namespace rat
