@@ -8,6 +8,6 @@ Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, brute force and library routines; nothing in it is
 "parity unpinned".
 """
-from .oracle import (anchor_offsets, attention, attention_rows, build,  # noqa: F401
+from .oracle import (anchor_offsets, attention, attention_rows, backward, build,  # noqa: F401
                      build_cache, decode_step, in_keyset, keyset_size, lib,
                      num_threads, prefill, round_bf16, scan)

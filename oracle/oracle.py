@@ -61,6 +61,8 @@ def load(path: str) -> ctypes.CDLL:
     L.rat_oracle_decode_step.argtypes = [i32, i32, i32, P, P, f64, i64,
                                          P, P, P, P, P, P, P, P, i32,
                                          P, P, P]
+    L.rat_oracle_backward.argtypes = [i32, i32, i32, i32, P, P, f64, P, P, P,
+                                      P, P, i32, P, P, P, P]
     L.rat_oracle_num_threads.restype = i32
     return L
 
@@ -68,7 +70,7 @@ def load(path: str) -> ctypes.CDLL:
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = load(_LIB)
     return _lib
@@ -226,3 +228,15 @@ def decode_step(q, k, v, g, state_k, state_v, hk_hist, hv_hist, D, W, scale,
                                  _p(hk_hist), _p(hv_hist), int(st_bf16), _p(o),
                                  _p(hk_new), _p(hv_new))
     return o, sk, sv, hk_new, hv_new
+
+
+def backward(q, k, v, g, dO, D, W, scale, st_bf16: bool):
+    """Gradients (dq, dk, dv, dg) of a loss whose gradient with respect to
+    the prefill output o is dO; all [B,H,T,hd].  See rat_oracle_backward."""
+    q, k, v, g, dO = _f64(q), _f64(k), _f64(v), _f64(g), _f64(dO)
+    B, H, T, hd = q.shape
+    D, W = _i32(D), _i32(W)
+    out = [np.empty_like(q) for _ in range(4)]
+    lib().rat_oracle_backward(B, H, T, hd, _p(D), _p(W), float(scale), _p(q), _p(k),
+                              _p(v), _p(g), _p(dO), int(st_bf16), *[_p(a) for a in out])
+    return dict(dq=out[0], dk=out[1], dv=out[2], dg=out[3])

@@ -293,3 +293,111 @@ int rat_oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------ */
+/* Backward of the prefill (reverse-mode derivative of the definitions  */
+/* above), for a loss L whose gradient with respect to o is dO.  The    */
+/* pages train RAT+ densely with active recurrence learning and adapt   */
+/* it to a dilation ([Z22], [Z23]); this is the gradient that training  */
+/* path needs.  Steps, per (b, h):                                     */
+/*  1. the forward recurrence of keys and values ([Z21]); the attention */
+/*     reads the states rounded to the storage type when st_bf16, and   */
+/*     the rounding is taken as the identity in the derivative;         */
+/*  2. per query t, over its key set S(t): p_j = softmax_j(scale q.hk_j),*/
+/*     dP_j = dO_t . hv_j, delta = sum_j p_j dP_j, dS_j = p_j (dP_j -    */
+/*     delta); dq_t = scale sum_j dS_j hk_j; dhk_j += scale dS_j q_t;    */
+/*     dhv_j += p_j dO_t;                                               */
+/*  3. the recurrence in reverse: lambda_t = dh_t + g_{t+1} lambda_{t+1} */
+/*     (lambda_T = 0); dx_t = (1 - g_t) lambda_t; dg_t accumulates      */
+/*     lambda_t (h_{t-1} - x_t) over keys and values (h_{-1} = 0).      */
+/* q, k, v, g, dO, dq, dk, dv, dg: [B,H,T,hd].                           */
+/* ------------------------------------------------------------------ */
+void rat_oracle_backward(int B, int H, int T, int hd, const int32_t* D,
+                         const int32_t* W, double scale, const double* q,
+                         const double* k, const double* v, const double* g,
+                         const double* dO, int st_bf16, double* dq, double* dk,
+                         double* dv, double* dg) {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      const int64_t base = IDX4(b, h, 0, 0, H, T, hd);
+      const int64_t n = (int64_t)T * hd;
+      double* hk = (double*)malloc(sizeof(double) * n);
+      double* hv = (double*)malloc(sizeof(double) * n);
+      double* hkr = (double*)malloc(sizeof(double) * n);
+      double* hvr = (double*)malloc(sizeof(double) * n);
+      double* dhk = (double*)calloc(n, sizeof(double));
+      double* dhv = (double*)calloc(n, sizeof(double));
+      double* p = (double*)malloc(sizeof(double) * T);
+      double* dp = (double*)malloc(sizeof(double) * T);
+      /* 1. forward recurrence */
+      for (int c = 0; c < hd; ++c) {
+        double sk = 0.0, sv = 0.0;
+        for (int t = 0; t < T; ++t) {
+          const int64_t i = base + (int64_t)t * hd + c;
+          sk = g[i] * sk + (1.0 - g[i]) * k[i];
+          sv = g[i] * sv + (1.0 - g[i]) * v[i];
+          hk[(int64_t)t * hd + c] = sk;
+          hv[(int64_t)t * hd + c] = sv;
+        }
+      }
+      for (int64_t i = 0; i < n; ++i) {
+        hkr[i] = st_bf16 ? rat_oracle_round_bf16(hk[i]) : hk[i];
+        hvr[i] = st_bf16 ? rat_oracle_round_bf16(hv[i]) : hv[i];
+      }
+      /* 2. attention backward, query by query */
+      for (int t = 0; t < T; ++t) {
+        const double* qt = q + base + (int64_t)t * hd;
+        const double* dot = dO + base + (int64_t)t * hd;
+        double m = -INFINITY;
+        for (int j = 0; j <= t; ++j) {
+          p[j] = -INFINITY;
+          if (!rat_oracle_in_keyset(t, j, D[h], W[h])) continue;
+          double e = 0.0;
+          for (int c = 0; c < hd; ++c) e += qt[c] * hkr[(int64_t)j * hd + c];
+          p[j] = scale * e;
+          if (p[j] > m) m = p[j];
+        }
+        double l = 0.0;
+        for (int j = 0; j <= t; ++j) {
+          p[j] = (p[j] == -INFINITY) ? 0.0 : exp(p[j] - m);
+          l += p[j];
+        }
+        double delta = 0.0;
+        for (int j = 0; j <= t; ++j) {
+          p[j] /= l;
+          dp[j] = 0.0;
+          if (p[j] == 0.0) continue;
+          for (int c = 0; c < hd; ++c) dp[j] += dot[c] * hvr[(int64_t)j * hd + c];
+          delta += p[j] * dp[j];
+        }
+        double* dqt = dq + base + (int64_t)t * hd;
+        for (int c = 0; c < hd; ++c) dqt[c] = 0.0;
+        for (int j = 0; j <= t; ++j) {
+          if (p[j] == 0.0) continue;
+          const double ds = p[j] * (dp[j] - delta);
+          for (int c = 0; c < hd; ++c) {
+            dqt[c] += scale * ds * hkr[(int64_t)j * hd + c];
+            dhk[(int64_t)j * hd + c] += scale * ds * qt[c];
+            dhv[(int64_t)j * hd + c] += p[j] * dot[c];
+          }
+        }
+      }
+      /* 3. the recurrence in reverse */
+      for (int c = 0; c < hd; ++c) {
+        double lk = 0.0, lv = 0.0;
+        for (int t = T - 1; t >= 0; --t) {
+          const int64_t i = base + (int64_t)t * hd + c;
+          const double gn = (t + 1 < T) ? g[i + hd] : 0.0;
+          lk = dhk[(int64_t)t * hd + c] + gn * lk;
+          lv = dhv[(int64_t)t * hd + c] + gn * lv;
+          dk[i] = (1.0 - g[i]) * lk;
+          dv[i] = (1.0 - g[i]) * lv;
+          const double pk = t > 0 ? hk[(int64_t)(t - 1) * hd + c] : 0.0;
+          const double pv = t > 0 ? hv[(int64_t)(t - 1) * hd + c] : 0.0;
+          dg[i] = lk * (pk - k[i]) + lv * (pv - v[i]);
+        }
+      }
+      free(hk); free(hv); free(hkr); free(hvr); free(dhk); free(dhv); free(p); free(dp);
+    }
+}

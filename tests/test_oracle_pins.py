@@ -339,7 +339,104 @@ def test_pages_claim_dfold_reduction():
 # --------------------------------------------------------------------------
 # planted mistakes: the pins above must catch them
 # --------------------------------------------------------------------------
+# --------------------------------------------------------------------------
+# backward: gradient of a loss L with dL/do = dO
+# --------------------------------------------------------------------------
+def _bwd_case(B, H, T, hd, seed):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((B, H, T, hd)) for _ in range(3))
+    g = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, T, hd)) - 1.0))
+    dO = rng.standard_normal((B, H, T, hd))
+    return q, k, v, g, dO
+
+
+BWD_FD_CASES = [
+    # B, H, T, hd, D, W, scale, seed
+    (1, 2, 40, 8, [3, 1], [0, 5], 0.35, 1),       # anchors, dense head, window
+    (2, 1, 33, 4, [7], [2], 0.6, 2),              # sparse anchors + short window
+    (1, 1, 10, 4, [16], [0], 0.5, 3),             # D > T: own position only
+]
+
+
+def _backward_fd(B, H, T, hd, D, W, scale, seed, n=8):
+    """Central differences of the pinned forward (oracle.prefill) against
+    oracle.backward at sampled elements of q, k, v and g; every sample set
+    includes t = 0 (the longest reverse-recurrence chain)."""
+    q, k, v, g, dO = _bwd_case(B, H, T, hd, seed)
+    grads = oracle.backward(q, k, v, g, dO, D, W, scale, False)
+    rng = np.random.default_rng(seed + 100)
+
+    def loss(xs):
+        return float((oracle.prefill(*xs, D, W, scale, False)["o"] * dO).sum())
+
+    eps = 1e-6
+    for i, name in enumerate(("q", "k", "v", "g")):
+        idxs = [(0, 0, 0, 0)] + [tuple(int(rng.integers(0, s)) for s in (B, H, T, hd))
+                                 for _ in range(n)]
+        for idx in idxs:
+            xs = [q.copy(), k.copy(), v.copy(), g.copy()]
+            xs[i][idx] += eps
+            lp = loss(xs)
+            xs[i][idx] -= 2 * eps
+            lm = loss(xs)
+            fd = (lp - lm) / (2 * eps)
+            an = grads["d" + name][idx]
+            assert abs(fd - an) <= 1e-6 + 1e-5 * abs(fd), (name, idx, fd, an)
+
+
+@pytest.mark.parametrize("case", BWD_FD_CASES)
+def test_backward_matches_finite_differences(case):
+    """The backward is the derivative of the forward: central differences of
+    the oracle's own (separately pinned) prefill, loss sum(o * dO)."""
+    _backward_fd(*case)
+
+
+def test_backward_dense_zero_gate_equals_sdpa_autograd():
+    """D = 1 with no window and g = 0 (states equal the inputs) is dense
+    causal attention over k and v: gradients equal torch autograd of
+    scaled_dot_product_attention (fp64, CPU); dg follows from the recurrence
+    with h_{t-1} = x_{t-1}."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    B, H, T, hd = 1, 2, 37, 8
+    q, k, v, _, dO = _bwd_case(B, H, T, hd, 9)
+    g = np.zeros_like(q)
+    scale = 0.4
+    r = oracle.backward(q, k, v, g, dO, [1] * H, [0] * H, scale, False)
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+    o.backward(torch.from_numpy(dO))
+    np.testing.assert_allclose(r["dq"], tq.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(r["dk"], tk.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(r["dv"], tv.grad.numpy(), rtol=1e-9, atol=1e-11)
+    kp = np.concatenate([np.zeros_like(k[:, :, :1]), k[:, :, :-1]], axis=2)
+    vp = np.concatenate([np.zeros_like(v[:, :, :1]), v[:, :, :-1]], axis=2)
+    dg = tk.grad.numpy() * (kp - k) + tv.grad.numpy() * (vp - v)
+    np.testing.assert_allclose(r["dg"], dg, rtol=1e-9, atol=1e-11)
+
+
+def test_backward_storage_rounding_is_straight_through():
+    """With g = 0 and inputs that are exact in bf16 the rounded states equal
+    the exact ones, so the bf16-storage backward equals the exact one (the
+    rounding enters the derivative as the identity)."""
+    B, H, T, hd = 1, 2, 24, 8
+    q, k, v, _, dO = _bwd_case(B, H, T, hd, 4)
+    k, v = oracle.round_bf16(k), oracle.round_bf16(v)
+    g = np.zeros_like(q)
+    a = oracle.backward(q, k, v, g, dO, [3, 1], [2, 0], 0.3, True)
+    b = oracle.backward(q, k, v, g, dO, [3, 1], [2, 0], 0.3, False)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n])
+
+
 MUTANTS = [
+    ("backward drops the softmax mean", "const double ds = p[j] * (dp[j] - delta);",
+     "const double ds = p[j] * dp[j];", ["backward"]),
+    ("reverse recurrence uses the current gate", "const double gn = (t + 1 < T) ? g[i + hd] : 0.0;",
+     "const double gn = g[i];", ["backward"]),
+    ("gate gradient sign", "dg[i] = lk * (pk - k[i]) + lv * (pv - v[i]);",
+     "dg[i] = lk * (k[i] - pk) + lv * (v[i] - pv);", ["backward"]),
+    ("input gradient misses 1-g", "dk[i] = (1.0 - g[i]) * lk;", "dk[i] = lk;", ["backward"]),
     # (description, original text, mutated text, pins expected to fail)
     ("anchor phase 0 instead of D-1", "if (j % D == D - 1) return 1;",
      "if (j % D == 0) return 1;", ["keyset", "readback"]),
@@ -370,6 +467,7 @@ PIN_GROUPS = {
                         for D, W, T in [(2, 0, 61), (4, 5, 64)]],
     "bf16": test_round_bf16_matches_torch,
     "layout": test_anchor_offsets_and_cache_layout,
+    "backward": lambda: [_backward_fd(*c, n=3) for c in BWD_FD_CASES[:2]],
 }
 
 
