@@ -23,7 +23,8 @@ they are kept out of the pass that gives ``value``).  The
 decode-step time of the metric is measured on the decode workload (batch 64,
 32 heads, context 32768, D=64, W=128, 256 steps) and reported beside it, as
 is a chunked prefill (the long-prefill workload in four chunks through the
-continuation entry points, against the same sequence in one call).
+continuation entry points, against the same sequence in one call) and the
+prefill backward (dq, dk, dv, dg) of the step's workload.
 ``roofline`` is for the kernel that takes the most time in the step;
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
 """
@@ -56,6 +57,8 @@ def parse():
                     help="replay each step as a captured HIP graph instead of three launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-workload", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the prefill-backward measurement")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-prefill measurement (long-prefill workload in chunks)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -103,6 +106,24 @@ def attn_flops(w):
         if key not in cache:
             cache[key] = keyset_total(w.T, *key)
         tot += 4 * w.hd * cache[key]
+    return w.B * tot
+
+
+def backward_bytes(w, es=2):
+    # read q, k, v, g, dO, hk, hv, o and lse; write dq, dk, dv, dg
+    return w.B * w.H * w.T * (12 * w.hd * es + 4)
+
+
+def backward_flops(w):
+    # per attended key: scores, dP and dq (query side), scores, dP, dV and dK
+    # (key side): 7 products of 2*hd flops; the own position is VALU work
+    tot = 0
+    cache = {}
+    for h in range(w.H):
+        key = (w.D[h], w.W[h])
+        if key not in cache:
+            cache[key] = keyset_total(w.T, *key) - w.T  # own positions excluded
+        tot += 14 * w.hd * cache[key]
     return w.B * tot
 
 
@@ -294,6 +315,9 @@ def main():
     chunked_info = None
     if not args.no_chunked:
         chunked_info = bench_chunked(rat, synth, torch, np)
+    backward_info = None
+    if not args.no_backward:
+        backward_info = bench_backward(rat, synth, torch, np, w)
 
     del sets
     torch.cuda.empty_cache()
@@ -332,6 +356,7 @@ def main():
         "kernels": kernels,
         "decode_workload": decode_info,
         "chunked_prefill": chunked_info,
+        "backward": backward_info,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -462,6 +487,57 @@ def bench_chunked(rat, synth, torch, np, reps=5, nchunks=4):
                tok_s_whole=B * T / (med(tot_whole) * 1e-6))
     assert int(ws[2].item()) == 0 and int(ws_f[2].item()) == 0, "scan wait timed out"
     del t, ch, c, rings, states, hk, hv, o, hk_f, hv_f, o_f
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_backward(rat, synth, torch, np, w, reps=10):
+    """Prefill backward (dq, dk, dv, dg for a random dO) of workload w after
+    its forward; HIP-event time of the whole rat_prefill_backward call."""
+    x = synth.prefill_inputs(w)
+    st = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {n: torch.from_numpy(x[n]).to("cuda").to(st) for n in "qkvg"}
+    del x
+    B, H, T, hd = w.B, w.H, w.T, w.hd
+    D, W = list(w.D), list(w.W)
+    c = rat.alloc_cache(B, H, hd, T, D, W, st, "cuda")
+    hk, hv = torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    ws = rat.scan_workspace(B, H, T, hd, "cuda")
+    rat.rat_scan_prefill(t["k"], t["v"], t["g"], D, W, T, c["Kc"], c["Vc"], c["state_k"],
+                         c["state_v"], ws, hk=hk, hv=hv, k_ring=c["k_ring"], v_ring=c["v_ring"])
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    rat.rat_dilated_attn_prefill(t["q"], hk, hv, c["Kc"], c["Vc"], D, W, T, o, lse)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 99)
+    dO = torch.randn(t["q"].shape, generator=gen, device="cuda").to(st)
+    grads = [torch.empty_like(t["q"]) for _ in range(4)]
+    bws = rat.backward_workspace(B, H, T, hd, D, "cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        rat.rat_prefill_backward(t["q"], t["k"], t["v"], t["g"], hk, hv, o, lse, dO, D, W,
+                                 *grads, bws)
+
+    run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+    es = 2 if w.dtype == "bf16" else 4
+    nb, nf = backward_bytes(w, es), backward_flops(w)
+    med = us[reps // 2]
+    res = dict(workload=f"{w.name}: B={B} H={H} hd={hd} T={T} D={D[0]} W={W[0]}",
+               us_median=med, us_min=us[0], bytes=nb, flops=nf, gbs=nb / (med * 1e-6) / 1e9,
+               hbm_frac=nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
+               tflops=nf / (med * 1e-6) / 1e12,
+               mfma_frac_useful=nf / (med * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+               tok_s=B * T / (med * 1e-6))
+    del t, c, hk, hv, o, lse, dO, grads, bws
     torch.cuda.empty_cache()
     return res
 

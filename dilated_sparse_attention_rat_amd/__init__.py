@@ -7,7 +7,9 @@ of ``include/rat.h``); :mod:`.binding` is its argument-marshalling layer and
 from .binding import (RAT_DTYPE_BF16, RAT_DTYPE_F32, RAT_ERR_CAPACITY,  # noqa: F401
                       RAT_ERR_HIP, RAT_ERR_INVALID_ARG, RAT_ERR_UNSUPPORTED,
                       RAT_ERR_WORKSPACE, RAT_MAX_HEADS, RAT_OK, RatError,
-                      alloc_cache, decode_workspace, lib, rat_anchor_rows,
+                      alloc_cache, backward_workspace, decode_workspace, lib,
+                      rat_anchor_rows, rat_prefill_backward,
+                      rat_prefill_backward_workspace_bytes,
                       rat_decode_step, rat_decode_workspace_bytes,
                       rat_dilated_attn_prefill,
                       rat_dilated_attn_prefill_continue, rat_ring_rows,

@@ -33,6 +33,7 @@ EXPORTED = [
     "rat_scan_workspace_bytes", "rat_scan_prefill", "rat_dilated_attn_prefill",
     "rat_scan_prefill_continue", "rat_dilated_attn_prefill_continue",
     "rat_decode_workspace_bytes", "rat_decode_step",
+    "rat_prefill_backward_workspace_bytes", "rat_prefill_backward",
 ]
 
 
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.rat_dilated_attn_prefill_continue.argtypes = [i32, i32, i32, i64, i32, P, P, f32,
                                                         i64, i64, P, P, P, P, P, P, P, P, P, P]
         L.rat_dilated_attn_prefill_continue.restype = i32
+        L.rat_prefill_backward_workspace_bytes.argtypes = [i32, i32, i64, i32, P]
+        L.rat_prefill_backward_workspace_bytes.restype = i64
+        L.rat_prefill_backward.argtypes = [i32, i32, i32, i64, i32, P, P, f32] + [P] * 14 + [sz, P]
+        L.rat_prefill_backward.restype = i32
         L.rat_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, P, P, i32]
         L.rat_decode_workspace_bytes.restype = i64
         L.rat_decode_step.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64,
@@ -344,6 +349,40 @@ def rat_decode_step(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, o,
     _check("rat_decode_step", lib().rat_decode_step(*args))
 
 
+def rat_prefill_backward_workspace_bytes(B: int, H: int, T: int, hd: int, D) -> int:
+    r = lib().rat_prefill_backward_workspace_bytes(B, H, T, hd, _ptr(_heads(D, H)))
+    if r < 0:
+        raise RatError("rat_prefill_backward_workspace_bytes", int(r))
+    return int(r)
+
+
+def rat_prefill_backward(q, k, v, g, hk, hv, o, lse, dO, D, W, dq, dk, dv, dg, workspace,
+                         scale: float = 0.0, stream=None):
+    """Gradients dq, dk, dv, dg of the prefill for dL/do = dO.  All [B,H,T,hd]
+    except lse [B,H,T] fp32."""
+    torch = _torch()
+    B, H, T, hd = q.shape
+    st = q.dtype
+    dev = q.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    shp = (B, H, T, hd)
+    args = [_dtype_code(q), B, H, T, hd, _ptr(Dh), _ptr(Wh), float(scale)]
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (hk, "hk"), (hv, "hv"), (o, "o")):
+        args.append(_dev(t, n, shp, st, dev))
+    args.append(_dev(lse, "lse", (B, H, T), torch.float32, dev))
+    args.append(_dev(dO, "dO", shp, st, dev))
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (dg, "dg")):
+        args.append(_dev(t, n, shp, st, dev))
+    need = rat_prefill_backward_workspace_bytes(B, H, T, hd, Dh)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    args += [ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+             _stream(stream, dev)]
+    _check("rat_prefill_backward", lib().rat_prefill_backward(*args))
+
+
 # ---------------------------------------------------------------------------
 # allocation helpers (plumbing: device buffers in the layouts of rat.h)
 # ---------------------------------------------------------------------------
@@ -381,4 +420,10 @@ def decode_workspace(B: int, H: int, hd: int, T_cap: int, D, W, device,
     n = rat_decode_workspace_bytes(B, H, hd, T_cap, D, W, num_splits)
     if n == 0:
         return None
+    return torch.empty(((n + 15) // 16) * 4, dtype=torch.int32, device=device)
+
+
+def backward_workspace(B: int, H: int, T: int, hd: int, D, device):
+    torch = _torch()
+    n = rat_prefill_backward_workspace_bytes(B, H, T, hd, D)
     return torch.empty(((n + 15) // 16) * 4, dtype=torch.int32, device=device)

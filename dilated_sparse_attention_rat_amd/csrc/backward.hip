@@ -1,0 +1,592 @@
+// Prefill backward: gradients of q, k, v and g for a loss whose gradient
+// with respect to the attention output o is dO (the training path of RAT+:
+// dense pretraining with active recurrence learning and a short adaptation
+// to a dilation, zhichai.net deep dive, sections 2.2 and 2.3).  The
+// recurrence (section 2.1) and the dilated attention (abstract; section 一)
+// are the forward of csrc/scan.hip and csrc/attn_prefill.hip.
+//
+// Kernels, in stream order:
+//  1. bwd_dq_kernel (query-parallel, MFMA): per query t over its key set
+//     (anchors j = D-1 mod D before the window, the window t-W..t-1, t):
+//     P = exp2(c*q.hk - lse*log2 e) from the forward's lse, dP = dO.hv,
+//     delta = dO.o, dS = P (dP - delta); dq = scale sum dS hk.  The own
+//     position is handled per lane: its dq term, and its dh terms
+//     (scale dS q and P dO) written as the first contribution to the fp32
+//     gradient of each state; delta is kept for kernel 2.
+//  2. bwd_dkv_kernel (key-parallel, MFMA): for each tile of 64 keys -- a
+//     tile of anchors (rows of hk/hv at positions aD+D-1) or a tile of
+//     window positions -- over the query tiles that see them:
+//     dhv += P^T dO, dhk += scale dS^T q.  Anchor gradients go to their own
+//     fp32 rows; window gradients are added to the state gradients.
+//  3. bwd_rscan_{agg,carry,apply}: the recurrence in reverse,
+//     lambda_t = dh_t + g_{t+1} lambda_{t+1} (lambda_T = 0), where dh_t adds
+//     the anchor gradient at anchor positions; dk = (1-g) lambda_k,
+//     dv = (1-g) lambda_v, dg = lambda_k (h^k_{t-1} - k) + lambda_v
+//     (h^v_{t-1} - v) with the stored states (h_{-1} = 0).  Chunks of 64
+//     positions: per-chunk affine maps, a carry pass over chunks, then the
+//     chunks again from their carries.
+// The storage rounding of the states enters the derivative as the identity.
+#include "rat_device.h"
+
+namespace rat {
+
+namespace {
+
+template <typename ST, int HD>
+struct BwdCfg {
+  static constexpr int BN = 64;          // keys (or queries) per staged tile
+  static constexpr int NS = HD / 32;     // K=32 slabs over channels
+  static constexpr int NDB = HD / 16;    // 16-channel blocks of the transposed accumulators
+  static constexpr int NMB = BN / 16;    // 16-row blocks of a score tile
+  static constexpr int NKK = BN / 32;    // K=32 slabs over the tile's rows
+  static constexpr int VEC = StTraits<ST>::VEC;
+  static constexpr int CPR = HD / VEC;   // 16-byte chunks per row
+  // padded strides (as in the forward): row-major rows 68 dwords apart
+  // (bf16), transposed rows 34 dwords apart
+  static constexpr int RSTR = HD + 16 / (int)sizeof(ST);
+  static constexpr int TSTR = BN + 4;
+  static constexpr int G4 = (BN / 4) * CPR;       // items of 4 rows x VEC channels
+  static constexpr int G4PT = (G4 + 255) / 256;   // per thread
+};
+
+// A tile of BN rows staged through registers into LDS: items of 4
+// consecutive rows x VEC channels, stored row-major and, with TRANS, also
+// transposed (rows contiguous per channel, the layout of an A operand whose
+// K dimension runs over the tile's rows).  Rows at or beyond nvalid re-read
+// row nvalid-1 (finite; every use of them is masked).
+template <typename ST, int HD, bool TRANS>
+struct Stage4 {
+  using C = BwdCfg<ST, HD>;
+  u32x4 r[C::G4PT][4];
+
+  template <typename RowPtr>
+  __device__ __forceinline__ void load(RowPtr row, int nvalid) {
+    const int tid = threadIdx.x;
+    const int last = nvalid - 1;
+#pragma unroll
+    for (int i = 0; i < C::G4PT; ++i) {
+      const int idx = min(tid + 256 * i, C::G4 - 1);
+      const int dg = idx / (C::BN / 4);
+      const int kg = idx - dg * (C::BN / 4);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) r[i][rr] = ld_raw16(row(min(4 * kg + rr, last)) + dg * C::VEC);
+    }
+  }
+
+  __device__ __forceinline__ void store(ST* sRow, ST* sT) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::G4PT; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx >= C::G4) continue;
+      const int dg = idx / (C::BN / 4);
+      const int kg = idx - dg * (C::BN / 4);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) st_raw16(sRow + (4 * kg + rr) * C::RSTR + dg * C::VEC, r[i][rr]);
+      if constexpr (TRANS) {
+        ST* dst = sT + (dg * C::VEC) * C::TSTR + 4 * kg;
+        if constexpr (sizeof(ST) == 2) {
+#pragma unroll
+          for (int e = 0; e < C::VEC; ++e) {
+            const int w = e >> 1;
+            const int sh = (e & 1) * 16;
+            const uint32_t x0 = (r[i][0][w] >> sh) & 0xffffu, x1 = (r[i][1][w] >> sh) & 0xffffu;
+            const uint32_t x2 = (r[i][2][w] >> sh) & 0xffffu, x3 = (r[i][3][w] >> sh) & 0xffffu;
+            u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
+            *reinterpret_cast<u32x2*>(dst + e * C::TSTR) = pk;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < C::VEC; ++e) {
+            u32x4 pk = {r[i][0][e], r[i][1][e], r[i][2][e], r[i][3][e]};
+            *reinterpret_cast<u32x4*>(dst + e * C::TSTR) = pk;
+          }
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// 1. dq, delta and the own-position state gradients
+// ---------------------------------------------------------------------------
+// Workgroup: 4 waves x 16 queries of one (b, h), query tile qt (heaviest
+// first).  Key tiles as in the forward: anchors [0, n_end) then the window
+// positions [jb0, last query].  K is staged row-major (scores) and
+// transposed (dq), V row-major (dP).
+template <typename ST, int HD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(const BwdParams p) {
+  using C = BwdCfg<ST, HD>;
+  __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::RSTR];
+  __shared__ __attribute__((aligned(16))) ST sV[C::BN * C::RSTR];
+  __shared__ __attribute__((aligned(16))) ST sKt[HD * C::TSTR];
+
+  const int nq = (p.T + C::BN - 1) / C::BN;
+  const int qt = nq - 1 - (int)blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int T = p.T;
+  const int D = p.ht.D[h];
+  const int W = p.ht.W[h];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t base = bh * T * HD;
+  const ST* qp = reinterpret_cast<const ST*>(p.q) + base;
+  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + base;
+  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + base;
+  const ST* op = reinterpret_cast<const ST*>(p.o) + base;
+  const ST* dop = reinterpret_cast<const ST*>(p.dO) + base;
+
+  const int tq0 = qt * C::BN;
+  const int tw0 = tq0 + 16 * wave;
+  const int tq = tw0 + col;
+  const bool valid = tq < T;
+  const int64_t row = (int64_t)min(tq, T - 1) * HD;
+
+  // ---- the lane's query: fragments, own position, delta ------------------
+  Frag<ST> qf[C::NS], dof[C::NS];
+  float s_own = 0.f, dp_own = 0.f, delta = 0.f;
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) {
+    qf[s] = frag_ld8(qp + row + 32 * s + 8 * g);
+    dof[s] = frag_ld8(dop + row + 32 * s + 8 * g);
+    s_own += frag_dot(qf[s], frag_ld8(hkp + row + 32 * s + 8 * g));
+    dp_own += frag_dot(dof[s], frag_ld8(hvp + row + 32 * s + 8 * g));
+    delta += frag_dot(dof[s], frag_ld8(op + row + 32 * s + 8 * g));
+  }
+  s_own = xor16_32_sum(s_own);
+  dp_own = xor16_32_sum(dp_own);
+  delta = xor16_32_sum(delta);
+  const float lse2 = p.lse[bh * T + min(tq, T - 1)] * kLog2e;
+  const float p_own = __builtin_amdgcn_exp2f(s_own * p.scale_log2 - lse2);
+  const float ds_own = p_own * (dp_own - delta);
+  if (valid) {
+    float* dhk = p.dhk + base + (int64_t)tq * HD;
+    float* dhv = p.dhv + base + (int64_t)tq * HD;
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+      float qv[8], dv[8];
+      frag_to_f32(qf[s], qv);
+      frag_to_f32(dof[s], dv);
+      f32x4 a0, a1, c0, c1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a0[j] = p.scale * ds_own * qv[j];
+        a1[j] = p.scale * ds_own * qv[4 + j];
+        c0[j] = p_own * dv[j];
+        c1[j] = p_own * dv[4 + j];
+      }
+      *reinterpret_cast<f32x4*>(dhk + 32 * s + 8 * g) = a0;
+      *reinterpret_cast<f32x4*>(dhk + 32 * s + 8 * g + 4) = a1;
+      *reinterpret_cast<f32x4*>(dhv + 32 * s + 8 * g) = c0;
+      *reinterpret_cast<f32x4*>(dhv + 32 * s + 8 * g + 4) = c1;
+    }
+    if (g == 0) p.delta[bh * T + tq] = delta;
+  }
+  // dq^T accumulators start at the own term ds_own * hk_t (unscaled)
+  f32x4 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) acc[db] = ds_own * ld4_f32(hkp + row + 16 * db + 4 * g);
+  Frag<ST> qs[C::NS];
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) qs[s] = frag_scale(qf[s], p.scale_log2);
+
+  // ---- key tiles ----------------------------------------------------------
+  const int tlast = min(tq0 + C::BN - 1, T - 1);   // last query of the tile
+  const int wlast = min(tw0 + 15, T - 1);          // last query of the wave
+  const int n_end = max(0, tlast - W) / D;
+  const int jb0 = max(0, tq0 - W);
+  const int na_t = (n_end + C::BN - 1) / C::BN;
+  const int nb_t = W > 0 ? (tlast - jb0 + C::BN) / C::BN : 0;
+  const int n_items = na_t + nb_t;
+  const int nlo = max(0, min(tq, T - 1) - W) / D;  // anchors visible to the lane's query
+  const int w_end = tw0 < T ? max(0, wlast - W) / D : 0;
+  const int w_full = tw0 < T ? max(0, tw0 - W) / D : 0;
+  const int wj0 = max(0, tw0 - W);
+  const ST* kcp = hkp;  // anchor a is the state at position a*D + D - 1
+  const ST* vcp = hvp;
+  auto item = [&](int i, int& key0, int& nvalid, bool& anchor) {
+    anchor = i < na_t;
+    if (anchor) {
+      key0 = i * C::BN;
+      nvalid = n_end - key0;
+    } else {
+      key0 = jb0 + (i - na_t) * C::BN;
+      nvalid = tlast + 1 - key0;
+    }
+  };
+  Stage4<ST, HD, true> pk;
+  Stage4<ST, HD, false> pv;
+  auto load = [&](int i) {
+    int key0, nv;
+    bool anchor;
+    item(i, key0, nv, anchor);
+    // one load path for both kinds (a branch between two would make the
+    // compiler wait for the loads at the join)
+    const int stride = anchor ? D : 1;
+    const int first = anchor ? key0 * D + D - 1 : key0;
+    pk.load([&](int r) { return kcp + ((int64_t)first + (int64_t)r * stride) * HD; }, nv);
+    pv.load([&](int r) { return vcp + ((int64_t)first + (int64_t)r * stride) * HD; }, nv);
+  };
+  if (n_items > 0) load(0);
+  for (int i = 0; i < n_items; ++i) {
+    __syncthreads();
+    pk.store(sK, sKt);
+    pv.store(sV, nullptr);
+    __syncthreads();
+    if (i + 1 < n_items) load(i + 1);
+    int key0, nv;
+    bool anchor;
+    item(i, key0, nv, anchor);
+    bool part, need_mask;
+    if (anchor) {
+      part = key0 < w_end;
+      need_mask = key0 + C::BN > w_full;
+    } else {
+      part = tw0 < T && key0 <= wlast && key0 + C::BN > wj0;
+      need_mask = !((tw0 + 15 - W <= key0) && (key0 + C::BN <= tw0) && (tw0 + 15 < T));
+    }
+    if (!part) continue;
+    f32x4 S[C::NMB], dP[C::NMB];
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb) {
+      S[mb] = f32x4{-lse2, -lse2, -lse2, -lse2};
+      dP[mb] = f32x4{-delta, -delta, -delta, -delta};
+    }
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) {
+        mma16(S[mb], frag_ld8(sK + (16 * mb + col) * C::RSTR + 32 * s + 8 * g), qs[s]);
+        mma16(dP[mb], frag_ld8(sV + (16 * mb + col) * C::RSTR + 32 * s + 8 * g), dof[s]);
+      }
+    // visible keys of the lane's query: anchors a < nlo; window t-W..t-1
+    const int lo = anchor ? 0 : tq - W;
+    const int hi = anchor ? nlo - 1 : tq - 1;
+    const int kb = key0 + 4 * g - lo;
+    const uint32_t span = (uint32_t)(hi - lo);
+    f32x4 dS[C::NMB];
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool vis = !need_mask || (valid && (uint32_t)(kb + 16 * mb + e) <= span && hi >= lo);
+        const float pe = vis ? __builtin_amdgcn_exp2f(S[mb][e]) : 0.f;
+        dS[mb][e] = pe * dP[mb][e];
+      }
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      const Frag<ST> bfr = frag_from(dS[2 * kk], dS[2 * kk + 1], (ST*)nullptr);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const ST* kr = sKt + (16 * db + col) * C::TSTR + 32 * kk + 4 * g;
+        mma16(acc[db], frag_ld4x2(kr, kr + 16), bfr);
+      }
+    }
+  }
+
+  if (valid) {
+    ST* dqp = reinterpret_cast<ST*>(p.dq) + base + (int64_t)tq * HD;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) st4(dqp + 16 * db + 4 * g, p.scale * acc[db]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. state gradients from the keys' side
+// ---------------------------------------------------------------------------
+// Workgroup: one tile of 64 keys of one (b, h), 16 per wave (the wave's keys
+// are the B operand, held in registers).  Tile x < na_t: anchors
+// [64x, 64x+64), seen by queries t >= (a+1)D + W; next nb_t tiles: window
+// positions [64y, 64y+64), seen by queries j+1 .. j+W.  Per query tile of 64:
+// Q and dO staged row-major and transposed, lse and delta beside them.
+template <typename ST, int HD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_kernel(const BwdParams p) {
+  using C = BwdCfg<ST, HD>;
+  __shared__ __attribute__((aligned(16))) ST sQ[C::BN * C::RSTR];
+  __shared__ __attribute__((aligned(16))) ST sO[C::BN * C::RSTR];
+  __shared__ __attribute__((aligned(16))) ST sQt[HD * C::TSTR];
+  __shared__ __attribute__((aligned(16))) ST sOt[HD * C::TSTR];
+  __shared__ __attribute__((aligned(16))) float sL[C::BN];
+  __shared__ __attribute__((aligned(16))) float sDl[C::BN];
+
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int T = p.T;
+  const int D = p.ht.D[h];
+  const int W = p.ht.W[h];
+  const int na = T / D;                              // anchors of the head
+  const int na_t = (na + C::BN - 1) / C::BN;
+  const int nb_t = W > 0 ? (T + C::BN - 1) / C::BN : 0;
+  const int x = blockIdx.x;
+  if (x >= na_t + nb_t) return;
+  const bool anchor = x < na_t;
+  const int key0 = anchor ? x * C::BN : (x - na_t) * C::BN;
+  const int nkeys = anchor ? na : T;                 // valid key indices < nkeys
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t base = bh * T * HD;
+  const ST* qp = reinterpret_cast<const ST*>(p.q) + base;
+  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + base;
+  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + base;
+  const ST* dop = reinterpret_cast<const ST*>(p.dO) + base;
+  const float* lsep = p.lse + bh * T;
+  const float* dlp = p.delta + bh * T;
+
+  // the lane's key (B-operand column): index key and its state row
+  const int key = key0 + 16 * wave + col;
+  const int keyc = min(key, nkeys - 1);
+  const int kpos = anchor ? keyc * D + D - 1 : keyc;  // position of its state
+  Frag<ST> kf[C::NS], vf[C::NS];
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) {
+    kf[s] = frag_scale(frag_ld8(hkp + (int64_t)kpos * HD + 32 * s + 8 * g), p.scale_log2);
+    vf[s] = frag_ld8(hvp + (int64_t)kpos * HD + 32 * s + 8 * g);
+  }
+  f32x4 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[db] = dk[db];
+  }
+
+  // queries that see the tile: anchors from (key0+1)D + W on; window
+  // positions from key0+1 to the tile's last key + W
+  int t_lo, t_hi;
+  if (anchor) {
+    t_lo = (int)min<int64_t>((int64_t)(key0 + 1) * D + W, T);
+    t_hi = T - 1;
+  } else {
+    t_lo = key0 + 1;
+    t_hi = (int)min<int64_t>(T - 1, (int64_t)min(key0 + C::BN, nkeys) - 1 + W);
+  }
+  const int qt0 = t_lo / C::BN;
+  const int qt1 = t_lo <= t_hi ? t_hi / C::BN : qt0 - 1;
+
+  Stage4<ST, HD, true> pq, po;
+  float lpre = 0.f, dpre = 0.f;
+  auto load = [&](int qt) {
+    const int tq0 = qt * C::BN;
+    const int nv = min(C::BN, T - tq0);
+    pq.load([&](int r) { return qp + (int64_t)(tq0 + r) * HD; }, nv);
+    po.load([&](int r) { return dop + (int64_t)(tq0 + r) * HD; }, nv);
+    if (tid < C::BN) {
+      const int t = min(tq0 + tid, T - 1);
+      lpre = lsep[t] * kLog2e;
+      dpre = dlp[t];
+    }
+  };
+  if (qt0 <= qt1) load(qt0);
+  for (int qt = qt0; qt <= qt1; ++qt) {
+    __syncthreads();
+    pq.store(sQ, sQt);
+    po.store(sO, sOt);
+    if (tid < C::BN) {
+      sL[tid] = lpre;
+      sDl[tid] = dpre;
+    }
+    __syncthreads();
+    if (qt < qt1) load(qt + 1);
+    const int tq0 = qt * C::BN;
+    f32x4 S[C::NMB], dP[C::NMB];
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + 16 * mb + 4 * g);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDl + 16 * mb + 4 * g);
+      S[mb] = -l4;
+      dP[mb] = -d4;
+    }
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) {
+        mma16(S[mb], frag_ld8(sQ + (16 * mb + col) * C::RSTR + 32 * s + 8 * g), kf[s]);
+        mma16(dP[mb], frag_ld8(sO + (16 * mb + col) * C::RSTR + 32 * s + 8 * g), vf[s]);
+      }
+    // element (query t = tq0 + 16mb + 4g + e, the lane's key)
+    f32x4 P[C::NMB], dS[C::NMB];
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = tq0 + 16 * mb + 4 * g + e;
+        bool vis = t < T && key < nkeys;
+        if (anchor)
+          vis = vis && (int64_t)(key + 1) * D + W <= t;
+        else
+          vis = vis && key <= t - 1 && key >= t - W;
+        const float pe = vis ? __builtin_amdgcn_exp2f(S[mb][e]) : 0.f;
+        P[mb][e] = pe;
+        dS[mb][e] = pe * dP[mb][e];
+      }
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      const Frag<ST> bp = frag_from(P[2 * kk], P[2 * kk + 1], (ST*)nullptr);
+      const Frag<ST> bs = frag_from(dS[2 * kk], dS[2 * kk + 1], (ST*)nullptr);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const ST* orow = sOt + (16 * db + col) * C::TSTR + 32 * kk + 4 * g;
+        const ST* qrow = sQt + (16 * db + col) * C::TSTR + 32 * kk + 4 * g;
+        mma16(dv[db], frag_ld4x2(orow, orow + 16), bp);
+        mma16(dk[db], frag_ld4x2(qrow, qrow + 16), bs);
+      }
+    }
+  }
+
+  if (key < nkeys) {
+    if (anchor) {
+      const int64_t r = ((int64_t)b * p.R + p.ht.aoff[h] + key) * HD;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        *reinterpret_cast<f32x4*>(p.dKc + r + 16 * db + 4 * g) = p.scale * dk[db];
+        *reinterpret_cast<f32x4*>(p.dVc + r + 16 * db + 4 * g) = dv[db];
+      }
+    } else {
+      float* dhk = p.dhk + base + (int64_t)key * HD;
+      float* dhv = p.dhv + base + (int64_t)key * HD;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        f32x4* a = reinterpret_cast<f32x4*>(dhk + 16 * db + 4 * g);
+        f32x4* c = reinterpret_cast<f32x4*>(dhv + 16 * db + 4 * g);
+        *a = *a + p.scale * dk[db];
+        *c = *c + dv[db];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. the recurrence in reverse (one thread per channel, chunks of 64)
+// ---------------------------------------------------------------------------
+constexpr int kRChunk = 64;
+
+template <typename ST>
+__device__ __forceinline__ float ld1(const ST* p) {
+  return (float)*p;
+}
+
+// state gradient of position t, channel c: the query-side and window terms
+// plus, at an anchor position, the anchor's own gradient
+__device__ __forceinline__ void dh_at(const BwdParams& p, int b, int h, int64_t bh, int t, int c,
+                                      int HD, float& k, float& v) {
+  const int64_t i = (bh * p.T + t) * HD + c;
+  k = p.dhk[i];
+  v = p.dhv[i];
+  const int D = p.ht.D[h];
+  if (t % D == D - 1) {
+    const int64_t r = ((int64_t)b * p.R + p.ht.aoff[h] + t / D) * HD + c;
+    k += p.dKc[r];
+    v += p.dVc[r];
+  }
+}
+
+template <typename ST, int HD>
+__global__ __launch_bounds__(HD) void bwd_rscan_agg_kernel(const BwdParams p) {
+  const int ch = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int c = threadIdx.x;
+  const int T = p.T;
+  const int64_t bh = (int64_t)b * p.H + h;
+  const ST* gp = reinterpret_cast<const ST*>(p.g) + bh * T * HD + c;
+  const int s = ch * kRChunk;
+  const int e = min(T, s + kRChunk) - 1;
+  float A = 1.f, lk = 0.f, lv = 0.f;
+  for (int t = e; t >= s; --t) {
+    const float gn = t + 1 < T ? ld1(gp + (int64_t)(t + 1) * HD) : 0.f;
+    float dk, dv;
+    dh_at(p, b, h, bh, t, c, HD, dk, dv);
+    lk = dk + gn * lk;
+    lv = dv + gn * lv;
+    A *= gn;
+  }
+  float* a = p.agg + ((bh * p.nchunk + ch) * 3) * HD + c;
+  a[0] = A;
+  a[HD] = lk;
+  a[2 * HD] = lv;
+}
+
+template <int HD>
+__global__ __launch_bounds__(HD) void bwd_rscan_carry_kernel(const BwdParams p) {
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x;
+  float lk = 0.f, lv = 0.f;  // lambda at the position after the chunk
+  for (int ch = p.nchunk - 1; ch >= 0; --ch) {
+    float* cr = p.carry + ((bh * p.nchunk + ch) * 2) * HD + c;
+    cr[0] = lk;
+    cr[HD] = lv;
+    const float* a = p.agg + ((bh * p.nchunk + ch) * 3) * HD + c;
+    lk = a[0] * lk + a[HD];
+    lv = a[0] * lv + a[2 * HD];
+  }
+}
+
+template <typename ST, int HD>
+__global__ __launch_bounds__(HD) void bwd_rscan_apply_kernel(const BwdParams p) {
+  const int ch = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int c = threadIdx.x;
+  const int T = p.T;
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t off = bh * T * HD + c;
+  const ST* gp = reinterpret_cast<const ST*>(p.g) + off;
+  const ST* kp = reinterpret_cast<const ST*>(p.k) + off;
+  const ST* vp = reinterpret_cast<const ST*>(p.v) + off;
+  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
+  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
+  ST* dkp = reinterpret_cast<ST*>(p.dk) + off;
+  ST* dvp = reinterpret_cast<ST*>(p.dv) + off;
+  ST* dgp = reinterpret_cast<ST*>(p.dg) + off;
+  const int s = ch * kRChunk;
+  const int e = min(T, s + kRChunk) - 1;
+  const float* cr = p.carry + ((bh * p.nchunk + ch) * 2) * HD + c;
+  float lk = cr[0], lv = cr[HD];
+  for (int t = e; t >= s; --t) {
+    const int64_t r = (int64_t)t * HD;
+    const float gn = t + 1 < T ? ld1(gp + r + HD) : 0.f;
+    float dhk, dhv;
+    dh_at(p, b, h, bh, t, c, HD, dhk, dhv);
+    lk = dhk + gn * lk;
+    lv = dhv + gn * lv;
+    const float gt = ld1(gp + r);
+    const float pk = t > 0 ? ld1(hkp + r - HD) : 0.f;
+    const float pv = t > 0 ? ld1(hvp + r - HD) : 0.f;
+    dkp[r] = (ST)((1.f - gt) * lk);
+    dvp[r] = (ST)((1.f - gt) * lv);
+    dgp[r] = (ST)(lk * (pk - ld1(kp + r)) + lv * (pv - ld1(vp + r)));
+  }
+}
+
+template <typename ST, int HD>
+int launch_t(const BwdParams& p, hipStream_t st) {
+  const int nq = (p.T + 63) / 64;
+  hipLaunchKernelGGL((bwd_dq_kernel<ST, HD>), dim3(nq, p.H, p.B), dim3(256), 0, st, p);
+  if (p.nkt > 0)
+    hipLaunchKernelGGL((bwd_dkv_kernel<ST, HD>), dim3(p.nkt, p.H, p.B), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((bwd_rscan_agg_kernel<ST, HD>), dim3(p.nchunk, p.H, p.B), dim3(HD), 0, st, p);
+  hipLaunchKernelGGL((bwd_rscan_carry_kernel<HD>), dim3(p.B * p.H), dim3(HD), 0, st, p);
+  hipLaunchKernelGGL((bwd_rscan_apply_kernel<ST, HD>), dim3(p.nchunk, p.H, p.B), dim3(HD), 0, st, p);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_backward(int dtype, int hd, const BwdParams& p, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == RAT_DTYPE_BF16) return hd == 128 ? launch_t<bf16, 128>(p, st) : launch_t<bf16, 64>(p, st);
+  return hd == 128 ? launch_t<float, 128>(p, st) : launch_t<float, 64>(p, st);
+}
+
+}  // namespace rat

@@ -426,3 +426,118 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D, const int
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// prefill backward
+// ---------------------------------------------------------------------------
+namespace {
+
+// Backward workspace (fp32 throughout), each part 256-byte aligned:
+// delta [B,H,T], dhk and dhv [B,H,T,hd], dKc and dVc [B,R,hd],
+// chunk maps [B*H][nchunk][3][hd], carries [B*H][nchunk][2][hd].
+struct BwdLayout {
+  int64_t R = 0, nchunk = 0;
+  int64_t off_delta = 0, off_dhk = 0, off_dhv = 0, off_dkc = 0, off_dvc = 0, off_agg = 0,
+          off_carry = 0, bytes = 0;
+};
+
+bool bwd_layout(int B, int H, int64_t T, int hd, const int32_t* D, BwdLayout& L) {
+  L.R = 0;
+  for (int h = 0; h < H; ++h) L.R += T / D[h];
+  L.nchunk = (T + 63) / 64;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t bh = (int64_t)B * H;
+  int64_t o = 0;
+  L.off_delta = o; o = up(o + bh * T * 4);
+  L.off_dhk = o; o = up(o + bh * T * hd * 4);
+  L.off_dhv = o; o = up(o + bh * T * hd * 4);
+  L.off_dkc = o; o = up(o + (int64_t)B * L.R * hd * 4);
+  L.off_dvc = o; o = up(o + (int64_t)B * L.R * hd * 4);
+  L.off_agg = o; o = up(o + bh * L.nchunk * 3 * hd * 4);
+  L.off_carry = o; o = up(o + bh * L.nchunk * 2 * hd * 4);
+  L.bytes = std::max<int64_t>(o, 256);
+  return L.R <= INT32_MAX && bh * T * hd < ((int64_t)1 << 62);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t rat_prefill_backward_workspace_bytes(int B, int H, int64_t T, int hd, const int32_t* D) {
+  if (B < 0 || H < 0 || T < 0 || T > kMaxT || D == nullptr) return RAT_ERR_INVALID_ARG;
+  if (H > RAT_MAX_HEADS) return RAT_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 128) return RAT_ERR_UNSUPPORTED;
+  for (int h = 0; h < H; ++h)
+    if (D[h] < 1) return RAT_ERR_INVALID_ARG;
+  BwdLayout L;
+  if (!bwd_layout(B, H, T, hd, D, L)) return RAT_ERR_UNSUPPORTED;
+  return L.bytes;
+}
+
+int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32_t* D,
+                         const int32_t* W, float scale, const void* q, const void* k,
+                         const void* v, const void* g, const void* hk, const void* hv,
+                         const void* o, const float* lse, const void* dO, void* dq, void* dk,
+                         void* dv, void* dg, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int st = check_common(dtype, B, H, hd, D, W);
+  if (st != RAT_OK) return st;
+  if (T < 0 || T > kMaxT) return RAT_ERR_INVALID_ARG;
+  if (!(scale <= 0.f) && !std::isfinite(scale)) return RAT_ERR_INVALID_ARG;
+  if (B == 0 || H == 0 || T == 0) return RAT_OK;
+  const void* in[] = {q, k, v, g, hk, hv, o, lse, dO};
+  void* out[] = {dq, dk, dv, dg};
+  for (const void* ptr : in)
+    if (ptr == nullptr || !aligned16(ptr)) return RAT_ERR_INVALID_ARG;
+  for (void* ptr : out)
+    if (ptr == nullptr || !aligned16(ptr)) return RAT_ERR_INVALID_ARG;
+  BwdLayout L;
+  if (!bwd_layout(B, H, T, hd, D, L)) return RAT_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < L.bytes)
+    return RAT_ERR_WORKSPACE;
+  BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  int64_t R, WS;
+  st = fill_tables(H, T, D, W, p.ht, R, WS);
+  if (st != RAT_OK) return st;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)hd);
+  p.B = B;
+  p.H = H;
+  p.T = (int)T;
+  p.scale = sc;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.R = R;
+  p.nchunk = (int)L.nchunk;
+  int64_t nkt = 0;
+  for (int h = 0; h < H; ++h) {
+    const int64_t na_t = (T / D[h] + 63) / 64;
+    const int64_t nb_t = W[h] > 0 ? (T + 63) / 64 : 0;
+    nkt = std::max(nkt, na_t + nb_t);
+  }
+  if ((int64_t)B * H * L.nchunk > INT32_MAX || nkt > INT32_MAX) return RAT_ERR_UNSUPPORTED;
+  p.nkt = (int)nkt;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.hk = hk;
+  p.hv = hv;
+  p.o = o;
+  p.lse = lse;
+  p.dO = dO;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dg = dg;
+  char* ws = static_cast<char*>(workspace);
+  p.delta = reinterpret_cast<float*>(ws + L.off_delta);
+  p.dhk = reinterpret_cast<float*>(ws + L.off_dhk);
+  p.dhv = reinterpret_cast<float*>(ws + L.off_dhv);
+  p.dKc = reinterpret_cast<float*>(ws + L.off_dkc);
+  p.dVc = reinterpret_cast<float*>(ws + L.off_dvc);
+  p.agg = reinterpret_cast<float*>(ws + L.off_agg);
+  p.carry = reinterpret_cast<float*>(ws + L.off_carry);
+  return map_hip(launch_backward(dtype, hd, p, stream));
+}
+
+}  // extern "C"

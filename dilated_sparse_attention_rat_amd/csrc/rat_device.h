@@ -177,6 +177,18 @@ __device__ __forceinline__ Frag<float> frag_scale(const Frag<float>& f, float c)
   r.hi = f.hi * c;
   return r;
 }
+// fragment -> its 8 values in k-slot order (j = 0..7)
+__device__ __forceinline__ void frag_to_f32(const Frag<bf16>& f, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)f.v[j];
+}
+__device__ __forceinline__ void frag_to_f32(const Frag<float>& f, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = f.lo[j];
+    x[4 + j] = f.hi[j];
+  }
+}
 // dot product of two fragments (fp32 accumulate)
 __device__ __forceinline__ float frag_dot(const Frag<bf16>& a, const Frag<bf16>& b) {
   float s = 0.f;

@@ -106,6 +106,36 @@ struct DecodeParams {
   HeadTables ht;
 };
 
+struct BwdParams {
+  int B, H, T;
+  float scale;       // score scale
+  float scale_log2;  // scale * log2(e)
+  int64_t R;         // anchor rows per batch row (floor(T / D_h) summed over heads)
+  int nchunk;        // reverse-scan chunks of 64 positions per sequence
+  int nkt;           // key tiles per head in the key-side grid (max over heads)
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* hk;    // forward states (stored)
+  const void* hv;
+  const void* o;     // forward output
+  const float* lse;  // forward lse (natural log)
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dg;
+  float* delta;      // workspace: [B,H,T] dO . o
+  float* dhk;        // workspace: [B,H,T,hd] state gradients (query side + window)
+  float* dhv;
+  float* dKc;        // workspace: [B,R,hd] anchor gradients
+  float* dVc;
+  float* agg;        // workspace: [B*H][nchunk][3][hd] reverse-scan chunk maps
+  float* carry;      // workspace: [B*H][nchunk][2][hd] lambda after each chunk
+  HeadTables ht;
+};
+
 // launchers (one per kernel family); return hipError_t as int
 int launch_scan(int dtype, int hd, const ScanParams& p, void* stream);
 // Continuation: copy the ring slots of positions [max(0, t0+T-W), t0) that
@@ -115,6 +145,7 @@ int launch_ring_carry(int dtype, int hd, int B, int H, int64_t WS, const HeadTab
                       void* vr_out, void* stream);
 int launch_attn_prefill(int dtype, int hd, const AttnParams& p, void* stream);
 int launch_decode(int dtype, int hd, const DecodeParams& p, void* stream);
+int launch_backward(int dtype, int hd, const BwdParams& p, void* stream);
 
 // sizes shared by the host layer and the kernels
 constexpr int kScanThreads = 256;

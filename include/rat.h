@@ -243,6 +243,45 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D,
                     void* k_ring, void* v_ring, void* o, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace rat_prefill_backward needs for (B, H, T, hd, D).
+ * Pure host function; returns bytes (> 0) or a negative code.
+ */
+int64_t rat_prefill_backward_workspace_bytes(int B, int H, int64_t T, int hd,
+                                             const int32_t* D);
+
+/*
+ * Backward of the prefill (scan + dilated attention) for a loss L with
+ * dL/do = dO: the gradient the training path needs (deep dive, sections 2.2
+ * and 2.3: dense pretraining with active recurrence learning and a short
+ * adaptation to a dilation; section 2.1: the recurrence).
+ *   attention, per query t over its key set S(t): P = softmax(scale q.hk),
+ *     delta_t = dO_t . o_t, dS = P (dO_t . hv - delta_t);
+ *     dq_t = scale sum_j dS_j hk_j;  dh^k_j += scale dS_j q_t;
+ *     dh^v_j += P_j dO_t;
+ *   recurrence in reverse: lambda_t = dh_t + g_{t+1} lambda_{t+1}
+ *     (lambda_T = 0); dk = (1-g) lambda^k, dv = (1-g) lambda^v,
+ *     dg = lambda^k (h^k_{t-1} - k) + lambda^v (h^v_{t-1} - v), h_{-1} = 0.
+ * The storage rounding of the states is taken as the identity; h_{t-1} in
+ * dg is the stored state.
+ * Reads  q, k, v, g, dO       [B, H, T, hd] ST (the prefill's inputs)
+ *        hk, hv, o            [B, H, T, hd] ST (rat_scan_prefill's states and
+ *                             rat_dilated_attn_prefill's output, same D, W,
+ *                             scale)
+ *        lse                  [B, H, T] fp32 (rat_dilated_attn_prefill's lse)
+ * Writes dq, dk, dv, dg       [B, H, T, hd] ST
+ * workspace: rat_prefill_backward_workspace_bytes bytes (fp32 intermediates;
+ * no initialisation needed).  scale <= 0 selects 1/sqrt(hd).
+ */
+int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd,
+                         const int32_t* D, const int32_t* W, float scale,
+                         const void* q, const void* k, const void* v,
+                         const void* g, const void* hk, const void* hv,
+                         const void* o, const float* lse, const void* dO,
+                         void* dq, void* dk, void* dv, void* dg,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

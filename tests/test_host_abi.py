@@ -193,6 +193,26 @@ def test_attention_continue_validation(L):
     assert _attn_c(L, B=0) == rb.RAT_OK
 
 
+def test_backward_validation(L):
+    d, w, dp, wp = _tables(2, 4, 0)
+    assert L.rat_prefill_backward_workspace_bytes(1, 2, 100, 128, dp) > 0
+    assert L.rat_prefill_backward_workspace_bytes(1, 2, 100, 96, dp) == rb.RAT_ERR_UNSUPPORTED
+    assert L.rat_prefill_backward_workspace_bytes(1, 2, -1, 128, dp) == rb.RAT_ERR_INVALID_ARG
+
+    def bwd(dtype=0, T=16, hd=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30, B=1):
+        return L.rat_prefill_backward(dtype, B, 2, T, hd, dp, wp, 0.0, *([_p(ptr)] * 13),
+                                      _p(ws), ws_bytes, None)
+
+    assert bwd(dtype=5) == rb.RAT_ERR_UNSUPPORTED
+    assert bwd(hd=32) == rb.RAT_ERR_UNSUPPORTED
+    assert bwd(ptr=0) == rb.RAT_ERR_INVALID_ARG
+    assert bwd(ptr=FAKE + 2) == rb.RAT_ERR_INVALID_ARG
+    assert bwd(ws=0) == rb.RAT_ERR_WORKSPACE
+    assert bwd(ws_bytes=64) == rb.RAT_ERR_WORKSPACE
+    assert bwd(T=0) == rb.RAT_OK
+    assert bwd(B=0) == rb.RAT_OK
+
+
 def _dec(L, dtype=0, B=1, H=2, hd=64, D=4, W=0, pos=5, T_cap=16, splits=0, ws=0, ws_bytes=0,
          q=FAKE):
     d, w, dp, wp = _tables(H, D, W)
