@@ -512,7 +512,7 @@ def bench_backward(rat, synth, torch, np, w, reps=10):
     gen.manual_seed(w.seed + 99)
     dO = torch.randn(t["q"].shape, generator=gen, device="cuda").to(st)
     grads = [torch.empty_like(t["q"]) for _ in range(4)]
-    bws = rat.backward_workspace(B, H, T, hd, D, "cuda")
+    bws = rat.backward_workspace(B, H, T, hd, D, W, "cuda")
     stream = torch.cuda.current_stream()
 
     def run():

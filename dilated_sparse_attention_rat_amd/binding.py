@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.rat_dilated_attn_prefill_continue.argtypes = [i32, i32, i32, i64, i32, P, P, f32,
                                                         i64, i64, P, P, P, P, P, P, P, P, P, P]
         L.rat_dilated_attn_prefill_continue.restype = i32
-        L.rat_prefill_backward_workspace_bytes.argtypes = [i32, i32, i64, i32, P]
+        L.rat_prefill_backward_workspace_bytes.argtypes = [i32, i32, i64, i32, P, P]
         L.rat_prefill_backward_workspace_bytes.restype = i64
         L.rat_prefill_backward.argtypes = [i32, i32, i32, i64, i32, P, P, f32] + [P] * 14 + [sz, P]
         L.rat_prefill_backward.restype = i32
@@ -349,8 +349,9 @@ def rat_decode_step(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, o,
     _check("rat_decode_step", lib().rat_decode_step(*args))
 
 
-def rat_prefill_backward_workspace_bytes(B: int, H: int, T: int, hd: int, D) -> int:
-    r = lib().rat_prefill_backward_workspace_bytes(B, H, T, hd, _ptr(_heads(D, H)))
+def rat_prefill_backward_workspace_bytes(B: int, H: int, T: int, hd: int, D, W) -> int:
+    r = lib().rat_prefill_backward_workspace_bytes(B, H, T, hd, _ptr(_heads(D, H)),
+                                                   _ptr(_heads(W, H)))
     if r < 0:
         raise RatError("rat_prefill_backward_workspace_bytes", int(r))
     return int(r)
@@ -373,7 +374,7 @@ def rat_prefill_backward(q, k, v, g, hk, hv, o, lse, dO, D, W, dq, dk, dv, dg, w
     args.append(_dev(dO, "dO", shp, st, dev))
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (dg, "dg")):
         args.append(_dev(t, n, shp, st, dev))
-    need = rat_prefill_backward_workspace_bytes(B, H, T, hd, Dh)
+    need = rat_prefill_backward_workspace_bytes(B, H, T, hd, Dh, Wh)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must hold {need} bytes")
     if workspace.device != dev or not workspace.is_contiguous():
@@ -423,7 +424,7 @@ def decode_workspace(B: int, H: int, hd: int, T_cap: int, D, W, device,
     return torch.empty(((n + 15) // 16) * 4, dtype=torch.int32, device=device)
 
 
-def backward_workspace(B: int, H: int, T: int, hd: int, D, device):
+def backward_workspace(B: int, H: int, T: int, hd: int, D, W, device):
     torch = _torch()
-    n = rat_prefill_backward_workspace_bytes(B, H, T, hd, D)
+    n = rat_prefill_backward_workspace_bytes(B, H, T, hd, D, W)
     return torch.empty(((n + 15) // 16) * 4, dtype=torch.int32, device=device)

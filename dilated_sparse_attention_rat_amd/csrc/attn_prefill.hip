@@ -520,9 +520,6 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   const int g = lane >> 4;
   const int T = p.T;
   const int64_t off = bh * T * HD;
-  const ST* qp = reinterpret_cast<const ST*>(p.q) + off;
-  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
-  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
 
   const int a0 = p.t0;  // absolute position of local row 0
   WaveState<ST, HD, 1> ws;

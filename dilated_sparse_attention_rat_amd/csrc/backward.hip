@@ -10,23 +10,30 @@
 //     (anchors j = D-1 mod D before the window, the window t-W..t-1, t):
 //     P = exp2(c*q.hk - lse*log2 e) from the forward's lse, dP = dO.hv,
 //     delta = dO.o, dS = P (dP - delta); dq = scale sum dS hk.  The own
-//     position is handled per lane: its dq term, and its dh terms
-//     (scale dS q and P dO) written as the first contribution to the fp32
-//     gradient of each state; delta is kept for kernel 2.
+//     position is handled per lane: its dq term, and the two scalars of its
+//     state-gradient terms (scale dS_own and P_own; the terms are those
+//     times q_t and dO_t) kept for kernel 3; delta is kept for kernel 2.
 //  2. bwd_dkv_kernel (key-parallel, MFMA): for each tile of 64 keys -- a
 //     tile of anchors (rows of hk/hv at positions aD+D-1) or a tile of
 //     window positions -- over the query tiles that see them:
-//     dhv += P^T dO, dhk += scale dS^T q.  Anchor gradients go to their own
-//     fp32 rows; window gradients are added to the state gradients.
+//     dhv += P^T dO, dhk += scale dS^T q.  An anchor tile's queries are split
+//     over several workgroups, each writing a partial sum of the anchor
+//     gradients; window tiles write the window gradients of their positions.
 //  3. bwd_rscan_{agg,carry,apply}: the recurrence in reverse,
-//     lambda_t = dh_t + g_{t+1} lambda_{t+1} (lambda_T = 0), where dh_t adds
-//     the anchor gradient at anchor positions; dk = (1-g) lambda_k,
+//     lambda_t = dh_t + g_{t+1} lambda_{t+1} (lambda_T = 0), where dh_t is the
+//     own term, the window gradient and, at anchor positions, the anchor
+//     gradient's partial sums; dk = (1-g) lambda_k,
 //     dv = (1-g) lambda_v, dg = lambda_k (h^k_{t-1} - k) + lambda_v
 //     (h^v_{t-1} - v) with the stored states (h_{-1} = 0).  Chunks of 64
-//     positions: per-chunk affine maps, a carry pass over chunks, then the
-//     chunks again from their carries.
+//     positions, 16-byte accesses per lane as in the forward scan: per-chunk
+//     affine maps, a carry pass over chunks, then the chunks again from
+//     their carries.
 // The storage rounding of the states enters the derivative as the identity.
 #include "rat_device.h"
+
+// fp32 tiles at hd = 128 need more LDS than two workgroups per CU allow, so
+// those instantiations run at one wave per SIMD (the bf16 ones at two)
+#pragma clang diagnostic ignored "-Wpass-failed"
 
 namespace rat {
 
@@ -165,28 +172,9 @@ void bwd_dq_kernel(const BwdParams p) {
   const float lse2 = p.lse[bh * T + min(tq, T - 1)] * kLog2e;
   const float p_own = __builtin_amdgcn_exp2f(s_own * p.scale_log2 - lse2);
   const float ds_own = p_own * (dp_own - delta);
-  if (valid) {
-    float* dhk = p.dhk + base + (int64_t)tq * HD;
-    float* dhv = p.dhv + base + (int64_t)tq * HD;
-#pragma unroll
-    for (int s = 0; s < C::NS; ++s) {
-      float qv[8], dv[8];
-      frag_to_f32(qf[s], qv);
-      frag_to_f32(dof[s], dv);
-      f32x4 a0, a1, c0, c1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a0[j] = p.scale * ds_own * qv[j];
-        a1[j] = p.scale * ds_own * qv[4 + j];
-        c0[j] = p_own * dv[j];
-        c1[j] = p_own * dv[4 + j];
-      }
-      *reinterpret_cast<f32x4*>(dhk + 32 * s + 8 * g) = a0;
-      *reinterpret_cast<f32x4*>(dhk + 32 * s + 8 * g + 4) = a1;
-      *reinterpret_cast<f32x4*>(dhv + 32 * s + 8 * g) = c0;
-      *reinterpret_cast<f32x4*>(dhv + 32 * s + 8 * g + 4) = c1;
-    }
-    if (g == 0) p.delta[bh * T + tq] = delta;
+  if (valid && g == 0) {
+    p.delta[bh * T + tq] = delta;
+    *reinterpret_cast<f32x2*>(p.own + 2 * (bh * T + tq)) = f32x2{p.scale * ds_own, p_own};
   }
   // dq^T accumulators start at the own term ds_own * hk_t (unscaled)
   f32x4 acc[C::NDB];
@@ -325,9 +313,10 @@ void bwd_dkv_kernel(const BwdParams p) {
   const int na_t = (na + C::BN - 1) / C::BN;
   const int nb_t = W > 0 ? (T + C::BN - 1) / C::BN : 0;
   const int x = blockIdx.x;
-  if (x >= na_t + nb_t) return;
-  const bool anchor = x < na_t;
-  const int key0 = anchor ? x * C::BN : (x - na_t) * C::BN;
+  if (x >= na_t * p.nsplit + nb_t) return;
+  const bool anchor = x < na_t * p.nsplit;
+  const int split = anchor ? x % p.nsplit : 0;
+  const int key0 = anchor ? (x / p.nsplit) * C::BN : (x - na_t * p.nsplit) * C::BN;
   const int nkeys = anchor ? na : T;                 // valid key indices < nkeys
 
   const int tid = threadIdx.x;
@@ -371,8 +360,14 @@ void bwd_dkv_kernel(const BwdParams p) {
     t_lo = key0 + 1;
     t_hi = (int)min<int64_t>(T - 1, (int64_t)min(key0 + C::BN, nkeys) - 1 + W);
   }
-  const int qt0 = t_lo / C::BN;
-  const int qt1 = t_lo <= t_hi ? t_hi / C::BN : qt0 - 1;
+  int qt0 = t_lo / C::BN;
+  int qt1 = t_lo <= t_hi ? t_hi / C::BN : qt0 - 1;
+  if (anchor && p.nsplit > 1) {  // this workgroup's share of the query tiles
+    const int len = (qt1 - qt0 + p.nsplit) / p.nsplit;
+    const int a0 = qt0 + split * len;
+    qt1 = min(qt1, a0 + len - 1);
+    qt0 = a0;
+  }
 
   Stage4<ST, HD, true> pq, po;
   float lpre = 0.f, dpre = 0.f;
@@ -445,76 +440,124 @@ void bwd_dkv_kernel(const BwdParams p) {
   }
 
   if (key < nkeys) {
-    if (anchor) {
-      const int64_t r = ((int64_t)b * p.R + p.ht.aoff[h] + key) * HD;
+    // anchors: this split's partial sums; window: the position's gradient
+    float* dkp = anchor ? p.dKc + split * p.kc_split + ((int64_t)b * p.R + p.ht.aoff[h] + key) * HD
+                        : p.dhk + base + (int64_t)key * HD;
+    float* dvp = anchor ? p.dVc + split * p.kc_split + ((int64_t)b * p.R + p.ht.aoff[h] + key) * HD
+                        : p.dhv + base + (int64_t)key * HD;
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        *reinterpret_cast<f32x4*>(p.dKc + r + 16 * db + 4 * g) = p.scale * dk[db];
-        *reinterpret_cast<f32x4*>(p.dVc + r + 16 * db + 4 * g) = dv[db];
-      }
-    } else {
-      float* dhk = p.dhk + base + (int64_t)key * HD;
-      float* dhv = p.dhv + base + (int64_t)key * HD;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        f32x4* a = reinterpret_cast<f32x4*>(dhk + 16 * db + 4 * g);
-        f32x4* c = reinterpret_cast<f32x4*>(dhv + 16 * db + 4 * g);
-        *a = *a + p.scale * dk[db];
-        *c = *c + dv[db];
-      }
+    for (int db = 0; db < C::NDB; ++db) {
+      *reinterpret_cast<f32x4*>(dkp + 16 * db + 4 * g) = p.scale * dk[db];
+      *reinterpret_cast<f32x4*>(dvp + 16 * db + 4 * g) = dv[db];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. the recurrence in reverse (one thread per channel, chunks of 64)
+// 3. the recurrence in reverse (chunks of 64 positions)
 // ---------------------------------------------------------------------------
+// Lane layout as in the forward scan: LPR lanes cover a row, VEC channels
+// each (16-byte accesses); a 256-thread workgroup holds 256/LPR chunks of one
+// (b, h), one row at a time per chunk.
 constexpr int kRChunk = 64;
 
-template <typename ST>
-__device__ __forceinline__ float ld1(const ST* p) {
-  return (float)*p;
-}
+template <typename ST, int HD>
+struct RCfg {
+  static constexpr int VEC = StTraits<ST>::VEC;
+  static constexpr int LPR = HD / VEC;      // lanes per row
+  static constexpr int CPB = 256 / LPR;     // chunks per workgroup
+};
 
-// state gradient of position t, channel c: the query-side and window terms
-// plus, at an anchor position, the anchor's own gradient
-__device__ __forceinline__ void dh_at(const BwdParams& p, int b, int h, int64_t bh, int t, int c,
-                                      int HD, float& k, float& v) {
-  const int64_t i = (bh * p.T + t) * HD + c;
-  k = p.dhk[i];
-  v = p.dhv[i];
-  const int D = p.ht.D[h];
+// the state gradients of position t for the lane's VEC channels: own term
+// (scalars from kernel 1 times q_t and dO_t), window gradient (W > 0) and, at
+// an anchor position, the partial sums of the anchor's gradient
+template <typename ST, int HD>
+__device__ __forceinline__ void dh_row(const BwdParams& p, int b, int h, int64_t bh, int t, int c0,
+                                       int W, int D, float (&k)[StTraits<ST>::VEC],
+                                       float (&v)[StTraits<ST>::VEC]) {
+  constexpr int VEC = StTraits<ST>::VEC;
+  const int64_t i = (bh * p.T + t) * HD + c0;
+  const f32x2 own = *reinterpret_cast<const f32x2*>(p.own + 2 * (bh * p.T + t));
+  float qv[VEC], ov[VEC];
+  unpack16(ld_raw16(reinterpret_cast<const ST*>(p.q) + i), qv, (ST*)nullptr);
+  unpack16(ld_raw16(reinterpret_cast<const ST*>(p.dO) + i), ov, (ST*)nullptr);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    k[e] = own[0] * qv[e];
+    v[e] = own[1] * ov[e];
+  }
+  if (W > 0) {
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(p.dhk + i + e);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(p.dhv + i + e);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        k[e + j] += a[j];
+        v[e + j] += c[j];
+      }
+    }
+  }
   if (t % D == D - 1) {
-    const int64_t r = ((int64_t)b * p.R + p.ht.aoff[h] + t / D) * HD + c;
-    k += p.dKc[r];
-    v += p.dVc[r];
+    const int64_t r = ((int64_t)b * p.R + p.ht.aoff[h] + t / D) * HD + c0;
+    for (int s = 0; s < p.nsplit; ++s) {
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p.dKc + s * p.kc_split + r + e);
+        const f32x4 c = *reinterpret_cast<const f32x4*>(p.dVc + s * p.kc_split + r + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          k[e + j] += a[j];
+          v[e + j] += c[j];
+        }
+      }
+    }
   }
 }
 
 template <typename ST, int HD>
-__global__ __launch_bounds__(HD) void bwd_rscan_agg_kernel(const BwdParams p) {
-  const int ch = blockIdx.x;
+__global__ __launch_bounds__(256) void bwd_rscan_agg_kernel(const BwdParams p) {
+  using R = RCfg<ST, HD>;
+  constexpr int VEC = R::VEC;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int c = threadIdx.x;
+  const int ch = blockIdx.x * R::CPB + (int)threadIdx.x / R::LPR;
+  const int c0 = ((int)threadIdx.x % R::LPR) * VEC;
+  if (ch >= p.nchunk) return;
   const int T = p.T;
+  const int D = p.ht.D[h];
+  const int W = p.ht.W[h];
   const int64_t bh = (int64_t)b * p.H + h;
-  const ST* gp = reinterpret_cast<const ST*>(p.g) + bh * T * HD + c;
+  const ST* gp = reinterpret_cast<const ST*>(p.g) + bh * T * HD + c0;
   const int s = ch * kRChunk;
   const int e = min(T, s + kRChunk) - 1;
-  float A = 1.f, lk = 0.f, lv = 0.f;
-  for (int t = e; t >= s; --t) {
-    const float gn = t + 1 < T ? ld1(gp + (int64_t)(t + 1) * HD) : 0.f;
-    float dk, dv;
-    dh_at(p, b, h, bh, t, c, HD, dk, dv);
-    lk = dk + gn * lk;
-    lv = dv + gn * lv;
-    A *= gn;
+  float A[VEC], lk[VEC], lv[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    A[j] = 1.f;
+    lk[j] = 0.f;
+    lv[j] = 0.f;
   }
-  float* a = p.agg + ((bh * p.nchunk + ch) * 3) * HD + c;
-  a[0] = A;
-  a[HD] = lk;
-  a[2 * HD] = lv;
+  for (int t = e; t >= s; --t) {
+    float gn[VEC];
+    unpack16(ld_raw16(gp + (int64_t)min(t + 1, T - 1) * HD), gn, (ST*)nullptr);
+    float dk[VEC], dv[VEC];
+    dh_row<ST, HD>(p, b, h, bh, t, c0, W, D, dk, dv);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const float gj = t + 1 < T ? gn[j] : 0.f;
+      lk[j] = dk[j] + gj * lk[j];
+      lv[j] = dv[j] + gj * lv[j];
+      A[j] *= gj;
+    }
+  }
+  float* a = p.agg + ((bh * p.nchunk + ch) * 3) * HD + c0;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    a[j] = A[j];
+    a[HD + j] = lk[j];
+    a[2 * HD + j] = lv[j];
+  }
 }
 
 template <int HD>
@@ -533,14 +576,19 @@ __global__ __launch_bounds__(HD) void bwd_rscan_carry_kernel(const BwdParams p) 
 }
 
 template <typename ST, int HD>
-__global__ __launch_bounds__(HD) void bwd_rscan_apply_kernel(const BwdParams p) {
-  const int ch = blockIdx.x;
+__global__ __launch_bounds__(256) void bwd_rscan_apply_kernel(const BwdParams p) {
+  using R = RCfg<ST, HD>;
+  constexpr int VEC = R::VEC;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int c = threadIdx.x;
+  const int ch = blockIdx.x * R::CPB + (int)threadIdx.x / R::LPR;
+  const int c0 = ((int)threadIdx.x % R::LPR) * VEC;
+  if (ch >= p.nchunk) return;
   const int T = p.T;
+  const int D = p.ht.D[h];
+  const int W = p.ht.W[h];
   const int64_t bh = (int64_t)b * p.H + h;
-  const int64_t off = bh * T * HD + c;
+  const int64_t off = bh * T * HD + c0;
   const ST* gp = reinterpret_cast<const ST*>(p.g) + off;
   const ST* kp = reinterpret_cast<const ST*>(p.k) + off;
   const ST* vp = reinterpret_cast<const ST*>(p.v) + off;
@@ -551,21 +599,40 @@ __global__ __launch_bounds__(HD) void bwd_rscan_apply_kernel(const BwdParams p) 
   ST* dgp = reinterpret_cast<ST*>(p.dg) + off;
   const int s = ch * kRChunk;
   const int e = min(T, s + kRChunk) - 1;
-  const float* cr = p.carry + ((bh * p.nchunk + ch) * 2) * HD + c;
-  float lk = cr[0], lv = cr[HD];
+  const float* cr = p.carry + ((bh * p.nchunk + ch) * 2) * HD + c0;
+  float lk[VEC], lv[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    lk[j] = cr[j];
+    lv[j] = cr[HD + j];
+  }
   for (int t = e; t >= s; --t) {
     const int64_t r = (int64_t)t * HD;
-    const float gn = t + 1 < T ? ld1(gp + r + HD) : 0.f;
-    float dhk, dhv;
-    dh_at(p, b, h, bh, t, c, HD, dhk, dhv);
-    lk = dhk + gn * lk;
-    lv = dhv + gn * lv;
-    const float gt = ld1(gp + r);
-    const float pk = t > 0 ? ld1(hkp + r - HD) : 0.f;
-    const float pv = t > 0 ? ld1(hvp + r - HD) : 0.f;
-    dkp[r] = (ST)((1.f - gt) * lk);
-    dvp[r] = (ST)((1.f - gt) * lv);
-    dgp[r] = (ST)(lk * (pk - ld1(kp + r)) + lv * (pv - ld1(vp + r)));
+    const int64_t rp = (int64_t)max(t - 1, 0) * HD;
+    float gn[VEC], gt[VEC], kv[VEC], vv[VEC], pk[VEC], pv[VEC];
+    unpack16(ld_raw16(gp + (int64_t)min(t + 1, T - 1) * HD), gn, (ST*)nullptr);
+    unpack16(ld_raw16(gp + r), gt, (ST*)nullptr);
+    unpack16(ld_raw16(kp + r), kv, (ST*)nullptr);
+    unpack16(ld_raw16(vp + r), vv, (ST*)nullptr);
+    unpack16(ld_raw16(hkp + rp), pk, (ST*)nullptr);
+    unpack16(ld_raw16(hvp + rp), pv, (ST*)nullptr);
+    float dk[VEC], dv[VEC];
+    dh_row<ST, HD>(p, b, h, bh, t, c0, W, D, dk, dv);
+    float ok[VEC], ov[VEC], og[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const float gj = t + 1 < T ? gn[j] : 0.f;
+      lk[j] = dk[j] + gj * lk[j];
+      lv[j] = dv[j] + gj * lv[j];
+      const float hk_prev = t > 0 ? pk[j] : 0.f;
+      const float hv_prev = t > 0 ? pv[j] : 0.f;
+      ok[j] = (1.f - gt[j]) * lk[j];
+      ov[j] = (1.f - gt[j]) * lv[j];
+      og[j] = lk[j] * (hk_prev - kv[j]) + lv[j] * (hv_prev - vv[j]);
+    }
+    st_raw16(dkp + r, pack16(ok, (ST*)nullptr));
+    st_raw16(dvp + r, pack16(ov, (ST*)nullptr));
+    st_raw16(dgp + r, pack16(og, (ST*)nullptr));
   }
 }
 
@@ -575,9 +642,10 @@ int launch_t(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_dq_kernel<ST, HD>), dim3(nq, p.H, p.B), dim3(256), 0, st, p);
   if (p.nkt > 0)
     hipLaunchKernelGGL((bwd_dkv_kernel<ST, HD>), dim3(p.nkt, p.H, p.B), dim3(256), 0, st, p);
-  hipLaunchKernelGGL((bwd_rscan_agg_kernel<ST, HD>), dim3(p.nchunk, p.H, p.B), dim3(HD), 0, st, p);
+  const int ncb = (p.nchunk + RCfg<ST, HD>::CPB - 1) / RCfg<ST, HD>::CPB;
+  hipLaunchKernelGGL((bwd_rscan_agg_kernel<ST, HD>), dim3(ncb, p.H, p.B), dim3(256), 0, st, p);
   hipLaunchKernelGGL((bwd_rscan_carry_kernel<HD>), dim3(p.B * p.H), dim3(HD), 0, st, p);
-  hipLaunchKernelGGL((bwd_rscan_apply_kernel<ST, HD>), dim3(p.nchunk, p.H, p.B), dim3(HD), 0, st, p);
+  hipLaunchKernelGGL((bwd_rscan_apply_kernel<ST, HD>), dim3(ncb, p.H, p.B), dim3(256), 0, st, p);
   return (int)hipGetLastError();
 }
 

@@ -433,26 +433,37 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D, const int
 namespace {
 
 // Backward workspace (fp32 throughout), each part 256-byte aligned:
-// delta [B,H,T], dhk and dhv [B,H,T,hd], dKc and dVc [B,R,hd],
-// chunk maps [B*H][nchunk][3][hd], carries [B*H][nchunk][2][hd].
+// delta [B,H,T], own-position scalars [B,H,T][2], window gradients dhk and
+// dhv [B,H,T,hd] (only when some head has a window), partial anchor
+// gradients dKc and dVc [kBwdMaxSplit][B,R,hd], chunk maps
+// [B*H][nchunk][3][hd], carries [B*H][nchunk][2][hd].
+constexpr int kBwdMaxSplit = 8;
+
 struct BwdLayout {
   int64_t R = 0, nchunk = 0;
-  int64_t off_delta = 0, off_dhk = 0, off_dhv = 0, off_dkc = 0, off_dvc = 0, off_agg = 0,
-          off_carry = 0, bytes = 0;
+  int64_t off_delta = 0, off_own = 0, off_dhk = 0, off_dhv = 0, off_dkc = 0, off_dvc = 0,
+          off_agg = 0, off_carry = 0, bytes = 0;
 };
 
-bool bwd_layout(int B, int H, int64_t T, int hd, const int32_t* D, BwdLayout& L) {
+bool bwd_layout(int B, int H, int64_t T, int hd, const int32_t* D, const int32_t* W,
+                BwdLayout& L) {
   L.R = 0;
-  for (int h = 0; h < H; ++h) L.R += T / D[h];
+  bool window = false;
+  for (int h = 0; h < H; ++h) {
+    L.R += T / D[h];
+    window = window || (W != nullptr && W[h] > 0);
+  }
   L.nchunk = (T + 63) / 64;
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   const int64_t bh = (int64_t)B * H;
+  const int64_t dh = window ? bh * T * hd * 4 : 0;
   int64_t o = 0;
   L.off_delta = o; o = up(o + bh * T * 4);
-  L.off_dhk = o; o = up(o + bh * T * hd * 4);
-  L.off_dhv = o; o = up(o + bh * T * hd * 4);
-  L.off_dkc = o; o = up(o + (int64_t)B * L.R * hd * 4);
-  L.off_dvc = o; o = up(o + (int64_t)B * L.R * hd * 4);
+  L.off_own = o; o = up(o + bh * T * 8);
+  L.off_dhk = o; o = up(o + dh);
+  L.off_dhv = o; o = up(o + dh);
+  L.off_dkc = o; o = up(o + kBwdMaxSplit * (int64_t)B * L.R * hd * 4);
+  L.off_dvc = o; o = up(o + kBwdMaxSplit * (int64_t)B * L.R * hd * 4);
   L.off_agg = o; o = up(o + bh * L.nchunk * 3 * hd * 4);
   L.off_carry = o; o = up(o + bh * L.nchunk * 2 * hd * 4);
   L.bytes = std::max<int64_t>(o, 256);
@@ -463,14 +474,13 @@ bool bwd_layout(int B, int H, int64_t T, int hd, const int32_t* D, BwdLayout& L)
 
 extern "C" {
 
-int64_t rat_prefill_backward_workspace_bytes(int B, int H, int64_t T, int hd, const int32_t* D) {
-  if (B < 0 || H < 0 || T < 0 || T > kMaxT || D == nullptr) return RAT_ERR_INVALID_ARG;
-  if (H > RAT_MAX_HEADS) return RAT_ERR_UNSUPPORTED;
-  if (hd != 64 && hd != 128) return RAT_ERR_UNSUPPORTED;
-  for (int h = 0; h < H; ++h)
-    if (D[h] < 1) return RAT_ERR_INVALID_ARG;
+int64_t rat_prefill_backward_workspace_bytes(int B, int H, int64_t T, int hd, const int32_t* D,
+                                             const int32_t* W) {
+  if (T < 0 || T > kMaxT) return RAT_ERR_INVALID_ARG;
+  const int st = check_common(RAT_DTYPE_BF16, B, H, hd, D, W);
+  if (st != RAT_OK) return st;
   BwdLayout L;
-  if (!bwd_layout(B, H, T, hd, D, L)) return RAT_ERR_UNSUPPORTED;
+  if (!bwd_layout(B, H, T, hd, D, W, L)) return RAT_ERR_UNSUPPORTED;
   return L.bytes;
 }
 
@@ -492,7 +502,7 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
   for (void* ptr : out)
     if (ptr == nullptr || !aligned16(ptr)) return RAT_ERR_INVALID_ARG;
   BwdLayout L;
-  if (!bwd_layout(B, H, T, hd, D, L)) return RAT_ERR_UNSUPPORTED;
+  if (!bwd_layout(B, H, T, hd, D, W, L)) return RAT_ERR_UNSUPPORTED;
   if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < L.bytes)
     return RAT_ERR_WORKSPACE;
   BwdParams p;
@@ -508,14 +518,30 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
   p.scale_log2 = sc * 1.4426950408889634f;
   p.R = R;
   p.nchunk = (int)L.nchunk;
+  // the queries of an anchor tile are shared by nsplit workgroups (partial
+  // sums) so that the key-side grid holds about two workgroups per CU
+  int64_t max_na_t = 0;
+  for (int h = 0; h < H; ++h) max_na_t = std::max<int64_t>(max_na_t, (T / D[h] + 63) / 64);
+  int nsplit = 1;
+  if (max_na_t > 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return RAT_ERR_HIP;
+    const int64_t wgs = (int64_t)B * H * max_na_t;
+    nsplit = (int)std::min<int64_t>(kBwdMaxSplit, std::max<int64_t>(1, (2 * cus + wgs - 1) / wgs));
+    nsplit = (int)std::min<int64_t>(nsplit, (T + 63) / 64);
+  }
   int64_t nkt = 0;
   for (int h = 0; h < H; ++h) {
     const int64_t na_t = (T / D[h] + 63) / 64;
     const int64_t nb_t = W[h] > 0 ? (T + 63) / 64 : 0;
-    nkt = std::max(nkt, na_t + nb_t);
+    nkt = std::max(nkt, na_t * nsplit + nb_t);
   }
   if ((int64_t)B * H * L.nchunk > INT32_MAX || nkt > INT32_MAX) return RAT_ERR_UNSUPPORTED;
   p.nkt = (int)nkt;
+  p.nsplit = nsplit;
+  p.kc_split = (int64_t)B * R * hd;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -531,6 +557,7 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
   p.dg = dg;
   char* ws = static_cast<char*>(workspace);
   p.delta = reinterpret_cast<float*>(ws + L.off_delta);
+  p.own = reinterpret_cast<float*>(ws + L.off_own);
   p.dhk = reinterpret_cast<float*>(ws + L.off_dhk);
   p.dhv = reinterpret_cast<float*>(ws + L.off_dhv);
   p.dKc = reinterpret_cast<float*>(ws + L.off_dkc);

@@ -112,7 +112,9 @@ struct BwdParams {
   float scale_log2;  // scale * log2(e)
   int64_t R;         // anchor rows per batch row (floor(T / D_h) summed over heads)
   int nchunk;        // reverse-scan chunks of 64 positions per sequence
-  int nkt;           // key tiles per head in the key-side grid (max over heads)
+  int nkt;           // workgroups per head in the key-side grid (max over heads)
+  int nsplit;        // workgroups sharing the queries of one anchor tile
+  int64_t kc_split;  // elements of one partial anchor-gradient buffer (B*R*hd)
   const void* q;
   const void* k;
   const void* v;
@@ -127,9 +129,10 @@ struct BwdParams {
   void* dv;
   void* dg;
   float* delta;      // workspace: [B,H,T] dO . o
-  float* dhk;        // workspace: [B,H,T,hd] state gradients (query side + window)
+  float* own;        // workspace: [B,H,T][2] scale*dS and P of the own position
+  float* dhk;        // workspace: [B,H,T,hd] window gradients (heads with W > 0)
   float* dhv;
-  float* dKc;        // workspace: [B,R,hd] anchor gradients
+  float* dKc;        // workspace: [nsplit][B,R,hd] partial anchor gradients
   float* dVc;
   float* agg;        // workspace: [B*H][nchunk][3][hd] reverse-scan chunk maps
   float* carry;      // workspace: [B*H][nchunk][2][hd] lambda after each chunk

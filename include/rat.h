@@ -244,11 +244,11 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace rat_prefill_backward needs for (B, H, T, hd, D).
- * Pure host function; returns bytes (> 0) or a negative code.
+ * Bytes of device workspace rat_prefill_backward needs for (B, H, T, hd, D,
+ * W).  Pure host function; returns bytes (> 0) or a negative code.
  */
 int64_t rat_prefill_backward_workspace_bytes(int B, int H, int64_t T, int hd,
-                                             const int32_t* D);
+                                             const int32_t* D, const int32_t* W);
 
 /*
  * Backward of the prefill (scan + dilated attention) for a loss L with

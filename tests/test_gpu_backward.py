@@ -58,7 +58,7 @@ def gpu_forward_backward(inp, dO, D, W, dtype):
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
     rat.rat_dilated_attn_prefill(q, hk, hv, c["Kc"], c["Vc"], D, W, T, o, lse)
     grads = [torch.full_like(q, float("nan")) for _ in range(4)]
-    bws = rat.backward_workspace(B, H, T, hd, D, "cuda")
+    bws = rat.backward_workspace(B, H, T, hd, D, W, "cuda")
     bws.fill_(-1)  # the backward needs no initialised workspace
     rat.rat_prefill_backward(q, k, v, g, hk, hv, o, lse, do, D, W, *grads, bws)
     torch.cuda.synchronize()

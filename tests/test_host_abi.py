@@ -195,9 +195,9 @@ def test_attention_continue_validation(L):
 
 def test_backward_validation(L):
     d, w, dp, wp = _tables(2, 4, 0)
-    assert L.rat_prefill_backward_workspace_bytes(1, 2, 100, 128, dp) > 0
-    assert L.rat_prefill_backward_workspace_bytes(1, 2, 100, 96, dp) == rb.RAT_ERR_UNSUPPORTED
-    assert L.rat_prefill_backward_workspace_bytes(1, 2, -1, 128, dp) == rb.RAT_ERR_INVALID_ARG
+    assert L.rat_prefill_backward_workspace_bytes(1, 2, 100, 128, dp, wp) > 0
+    assert L.rat_prefill_backward_workspace_bytes(1, 2, 100, 96, dp, wp) == rb.RAT_ERR_UNSUPPORTED
+    assert L.rat_prefill_backward_workspace_bytes(1, 2, -1, 128, dp, wp) == rb.RAT_ERR_INVALID_ARG
 
     def bwd(dtype=0, T=16, hd=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30, B=1):
         return L.rat_prefill_backward(dtype, B, 2, T, hd, dp, wp, 0.0, *([_p(ptr)] * 13),
