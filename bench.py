@@ -24,7 +24,8 @@ decode-step time of the metric is measured on the decode workload (batch 64,
 32 heads, context 32768, D=64, W=128, 256 steps) and reported beside it, as
 is a chunked prefill (the long-prefill workload in four chunks through the
 continuation entry points, against the same sequence in one call) and the
-prefill backward (dq, dk, dv, dg) of the step's workload.
+prefill backward (dq, dk, dv, dg) of the step's workload, and one whole RAT+
+layer over it (projections as GEMMs around the prefill, d_model = H*hd).
 ``roofline`` is for the kernel that takes the most time in the step;
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
 """
@@ -57,6 +58,8 @@ def parse():
                     help="replay each step as a captured HIP graph instead of three launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-workload", action="store_true")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the layer measurement (projections around the prefill)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the prefill-backward measurement")
     ap.add_argument("--no-chunked", action="store_true",
@@ -318,6 +321,9 @@ def main():
     backward_info = None
     if not args.no_backward:
         backward_info = bench_backward(rat, synth, torch, np, w)
+    layer_info = None
+    if not args.no_layer:
+        layer_info = bench_layer(rat, synth, torch, np, w)
 
     del sets
     torch.cuda.empty_cache()
@@ -357,6 +363,7 @@ def main():
         "decode_workload": decode_info,
         "chunked_prefill": chunked_info,
         "backward": backward_info,
+        "layer": layer_info,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -538,6 +545,52 @@ def bench_backward(rat, synth, torch, np, w, reps=10):
                mfma_frac_useful=nf / (med * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                tok_s=B * T / (med * 1e-6))
     del t, c, hk, hv, o, lse, dO, grads, bws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_layer(rat, synth, torch, np, w, reps=5):
+    """One RAT+ layer over the step's prefill workload: d_model = H*hd, random
+    projection weights, x ~ N(0, 1).  HIP-event time of rat_layer_prefill."""
+    B, H, T, hd = w.B, w.H, w.T, w.hd
+    D, W = list(w.D), list(w.W)
+    dm = H * hd
+    st = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 7)
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device="cuda") * std).to(st)
+
+    x = rnd((B, T, dm), 1.0)
+    wq, wk, wv = (rnd((dm, dm), w.qkv_std / math.sqrt(dm)) for _ in range(3))
+    wg = rnd((dm, dm), 1.0 / math.sqrt(dm))
+    wo = rnd((dm, dm), 1.0 / math.sqrt(dm))
+    bg = torch.full((dm,), float(w.g_bias), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(x)
+    cache = rat.alloc_cache(B, H, hd, T, D, W, st, "cuda")
+    ws = rat.layer_workspace(rat.binding._dtype_code(x), B, H, T, hd, "cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        rat.rat_layer_prefill(x, wq, wk, wv, wg, bg, wo, out, D, W, H, hd, T, cache, ws)
+
+    run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+    med = us[reps // 2]
+    gemm_flops = 5 * 2 * B * T * dm * dm
+    res = dict(workload=f"{w.name} layer: B={B} T={T} d_model={dm} H={H} hd={hd} D={D[0]} W={W[0]}",
+               us_median=med, us_min=us[0], tok_s=B * T / (med * 1e-6),
+               gemm_flops=gemm_flops, attn_flops=attn_flops(w),
+               tflops_total=(gemm_flops + attn_flops(w)) / (med * 1e-6) / 1e12)
+    del x, wq, wk, wv, wg, wo, bg, out, cache, ws
     torch.cuda.empty_cache()
     return res
 

@@ -8,7 +8,8 @@ from .binding import (RAT_DTYPE_BF16, RAT_DTYPE_F32, RAT_ERR_CAPACITY,  # noqa: 
                       RAT_ERR_HIP, RAT_ERR_INVALID_ARG, RAT_ERR_UNSUPPORTED,
                       RAT_ERR_WORKSPACE, RAT_MAX_HEADS, RAT_OK, RatError,
                       alloc_cache, backward_workspace, decode_workspace, lib,
-                      rat_anchor_rows, rat_prefill_backward,
+                      layer_workspace, rat_anchor_rows, rat_layer_prefill,
+                      rat_layer_workspace_bytes, rat_prefill_backward,
                       rat_prefill_backward_workspace_bytes,
                       rat_decode_step, rat_decode_workspace_bytes,
                       rat_dilated_attn_prefill,

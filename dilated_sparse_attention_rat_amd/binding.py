@@ -34,6 +34,7 @@ EXPORTED = [
     "rat_scan_prefill_continue", "rat_dilated_attn_prefill_continue",
     "rat_decode_workspace_bytes", "rat_decode_step",
     "rat_prefill_backward_workspace_bytes", "rat_prefill_backward",
+    "rat_layer_workspace_bytes", "rat_layer_prefill",
 ]
 
 
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.rat_prefill_backward_workspace_bytes.restype = i64
         L.rat_prefill_backward.argtypes = [i32, i32, i32, i64, i32, P, P, f32] + [P] * 14 + [sz, P]
         L.rat_prefill_backward.restype = i32
+        L.rat_layer_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
+        L.rat_layer_workspace_bytes.restype = i64
+        L.rat_layer_prefill.argtypes = [i32, i32, i32, i64, i32, i32, P, P, f32, i64] + [P] * 16 + [sz, P]
+        L.rat_layer_prefill.restype = i32
         L.rat_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, P, P, i32]
         L.rat_decode_workspace_bytes.restype = i64
         L.rat_decode_step.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64,
@@ -382,6 +387,54 @@ def rat_prefill_backward(q, k, v, g, hk, hv, o, lse, dO, D, W, dq, dk, dv, dg, w
     args += [ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
              _stream(stream, dev)]
     _check("rat_prefill_backward", lib().rat_prefill_backward(*args))
+
+
+def rat_layer_workspace_bytes(dtype_code: int, B: int, H: int, T: int, hd: int) -> int:
+    r = lib().rat_layer_workspace_bytes(dtype_code, B, H, T, hd)
+    if r < 0:
+        raise RatError("rat_layer_workspace_bytes", int(r))
+    return int(r)
+
+
+def rat_layer_prefill(x, w_q, w_k, w_v, w_g, b_g, w_o, out, D, W, H: int, hd: int, T_cap: int,
+                      cache, workspace, lse=None, scale: float = 0.0, stream=None):
+    """One RAT+ layer over a prefill.  x, out: [B,T,dm]; w_*: [dm,H*hd]
+    (w_o: [H*hd,dm]); b_g: [H*hd] fp32; cache: dict of alloc_cache."""
+    torch = _torch()
+    B, T, dm = x.shape
+    st = x.dtype
+    dev = x.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    R, _ = rat_anchor_rows(H, T_cap, Dh)
+    WS, _ = rat_ring_rows(H, Wh)
+    HD = H * hd
+    args = [_dtype_code(x), B, H, T, hd, dm, _ptr(Dh), _ptr(Wh), float(scale), T_cap,
+            _dev(x, "x", (B, T, dm), st, dev)]
+    for t, n in ((w_q, "w_q"), (w_k, "w_k"), (w_v, "w_v"), (w_g, "w_g")):
+        args.append(_dev(t, n, (dm, HD), st, dev))
+    args += [_dev(b_g, "b_g", (HD,), torch.float32, dev), _dev(w_o, "w_o", (HD, dm), st, dev),
+             _dev(out, "out", (B, T, dm), st, dev),
+             _opt(lse, "lse", (B, H, T), torch.float32, dev),
+             _opt(cache["Kc"], "Kc", (B, R, hd), st, dev), _opt(cache["Vc"], "Vc", (B, R, hd), st, dev),
+             _opt(cache["k_ring"], "k_ring", (B, WS, hd), st, dev),
+             _opt(cache["v_ring"], "v_ring", (B, WS, hd), st, dev),
+             _dev(cache["state_k"], "state_k", (B, H, hd), torch.float32, dev),
+             _dev(cache["state_v"], "state_v", (B, H, hd), torch.float32, dev)]
+    need = rat_layer_workspace_bytes(_dtype_code(x), B, H, T, hd)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    args += [ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+             _stream(stream, dev)]
+    _check("rat_layer_prefill", lib().rat_layer_prefill(*args))
+
+
+def layer_workspace(dtype_code: int, B: int, H: int, T: int, hd: int, device):
+    """Zero-filled layer workspace (zero it again only after a failed call)."""
+    torch = _torch()
+    n = rat_layer_workspace_bytes(dtype_code, B, H, T, hd)
+    return torch.zeros(((n + 15) // 16) * 4, dtype=torch.int32, device=device)
 
 
 # ---------------------------------------------------------------------------

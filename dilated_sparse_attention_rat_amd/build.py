@@ -56,7 +56,7 @@ def build_library(extra_flags=(), jobs: int = 8, verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-lrocblas", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

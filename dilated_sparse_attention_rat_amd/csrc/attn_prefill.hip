@@ -440,14 +440,14 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   }
 
   // ---- normalise and store --------------------------------------------------
-  ST* op = reinterpret_cast<ST*>(p.o) + bh * T * HD;
+  ST* op = reinterpret_cast<ST*>(p.o) + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
     const float lt = xor16_32_sum(ws.l[nb]);
     const int t = ws.tq[nb] - a0;  // local row
     if (t < T) {
       const float inv = 1.f / lt;
-      ST* orow = op + (int64_t)t * HD;
+      ST* orow = op + (int64_t)t * p.o_st;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) st4(orow + 16 * db + 4 * g, ws.acc[nb][db] * inv);
       if (p.lse != nullptr && g == 0) p.lse[bh * T + t] = (ws.m[nb] + __log2f(lt)) * kLn2;
@@ -519,7 +519,6 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   const int col = lane & 15;
   const int g = lane >> 4;
   const int T = p.T;
-  const int64_t off = bh * T * HD;
 
   const int a0 = p.t0;  // absolute position of local row 0
   WaveState<ST, HD, 1> ws;
@@ -546,11 +545,13 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   const float inv = 1.f / lt;
   // buffer stores: lanes of rows past T (and the lse of lanes g > 0, or a
   // null lse) use an offset outside the region, which the hardware drops
-  const auto orsrc = buffer_region(reinterpret_cast<ST*>(p.o) + off);
+  const auto orsrc = buffer_region(reinterpret_cast<ST*>(p.o) + (int64_t)(bh / p.H) * p.o_sb +
+                                   (int64_t)(bh % p.H) * p.o_sh);
   const auto lrsrc = buffer_region(p.lse != nullptr ? p.lse + bh * T : nullptr);
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) {
-    const uint32_t ob = t < T ? (uint32_t)(((int64_t)t * HD + 16 * db + 4 * g) * sizeof(ST)) : kDropOffset;
+    const uint32_t ob =
+        t < T ? (uint32_t)(((int64_t)t * p.o_st + 16 * db + 4 * g) * sizeof(ST)) : kDropOffset;
     buffer_st4(orsrc, ob, ws.acc[0][db] * inv);
   }
   const uint32_t lb = (t < T && g == 0 && p.lse != nullptr) ? (uint32_t)t * 4u : kDropOffset;

@@ -9,6 +9,11 @@
 #include <cstdint>
 #include <cstring>
 
+#include <rocblas/rocblas.h>
+
+#include <map>
+#include <mutex>
+
 #include "rat.h"
 #include "rat_params.h"
 
@@ -147,7 +152,8 @@ int scan_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
               int64_t T_cap, int64_t t0, const void* k, const void* v, const void* g,
               const float* sk_in, const float* sv_in, void* hk, void* hv, void* Kc, void* Vc,
               const void* kr_in, const void* vr_in, void* k_ring, void* v_ring, float* state_k,
-              float* state_v, void* workspace, size_t workspace_bytes, void* stream) {
+              float* state_v, void* workspace, size_t workspace_bytes, void* stream,
+              const float* gate_bias = nullptr) {
   int st = check_common(dtype, B, H, hd, D, W);
   if (st != RAT_OK) return st;
   if (T < 0 || t0 < 0 || T_cap > kMaxT) return RAT_ERR_INVALID_ARG;
@@ -206,6 +212,7 @@ int scan_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
   p.sv = state_v;
   p.sk_in = sk_in;
   p.sv_in = sv_in;
+  p.gate_bias = gate_bias;
   if (p.WS > 0 && t0 > 0 && kr_in != nullptr && kr_in != k_ring) {
     // window positions before t0 that stay in the window: previous ring ->
     // new ring (disjoint from the slots the scan writes)
@@ -247,7 +254,7 @@ namespace {
 int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, const int32_t* W,
               float scale, int64_t T_cap, int64_t t0, const void* q, const void* hk,
               const void* hv, const void* Kc, const void* Vc, const void* kr_prev,
-              const void* vr_prev, void* o, float* lse, void* stream) {
+              const void* vr_prev, void* o, float* lse, void* stream, bool o_tok = false) {
   int st = check_common(dtype, B, H, hd, D, W);
   if (st != RAT_OK) return st;
   if (T < 0 || t0 < 0 || T_cap > kMaxT) return RAT_ERR_INVALID_ARG;
@@ -281,7 +288,7 @@ int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
   p.qb = avg_keys >= 512.0 ? 2 : 1;
   // resident-anchor kernel: bf16, no window, every head's anchors fit in LDS
   // (per-(b,h) output rows are addressed with 32-bit byte offsets there)
-  bool resident = dtype == RAT_DTYPE_BF16 && T * hd * 2 <= INT32_MAX;
+  bool resident = dtype == RAT_DTYPE_BF16 && T * (o_tok ? H : 1) * hd * 2 <= INT32_MAX;
   for (int h = 0; h < H && resident; ++h)
     resident = W[h] == 0 && (t0 + T - 1) / D[h] <= kResidentAnchors;
   if (resident) {
@@ -312,6 +319,9 @@ int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
   p.vr = vr_prev;
   p.WS = WS;
   p.o = o;
+  p.o_sb = o_tok ? T * H * hd : (int64_t)H * T * hd;
+  p.o_sh = o_tok ? hd : T * hd;
+  p.o_st = o_tok ? (int64_t)H * hd : hd;
   p.lse = lse;
   // heads in descending cost of one pair-block (anchor tiles + band tiles of
   // the heaviest and the lightest query tile), so heavy heads start first
@@ -565,6 +575,147 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
   p.agg = reinterpret_cast<float*>(ws + L.off_agg);
   p.carry = reinterpret_cast<float*>(ws + L.off_carry);
   return map_hip(launch_backward(dtype, hd, p, stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// layer prefill: projections (rocBLAS GEMMs) around the scan and attention
+// ---------------------------------------------------------------------------
+namespace {
+
+// one rocBLAS handle per device, created on the first layer call there
+rocblas_handle blas_handle(int& err) {
+  static std::mutex mu;
+  static std::map<int, rocblas_handle> handles;
+  err = RAT_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    err = RAT_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = handles.find(dev);
+  if (it != handles.end()) return it->second;
+  rocblas_handle h = nullptr;
+  if (rocblas_create_handle(&h) != rocblas_status_success) {
+    err = RAT_ERR_HIP;
+    return nullptr;
+  }
+  handles[dev] = h;
+  return h;
+}
+
+// layer workspace: q, k, v, the gate pre-activation and hk, hv in
+// [B,H,T,hd], o token-major [B,T,H,hd] (all ST), then the scan workspace
+struct LayerLayout {
+  int64_t act = 0, off_scan = 0, scan_bytes = 0, bytes = 0;
+};
+
+bool layer_layout(int dtype, int B, int H, int64_t T, int hd, LayerLayout& L) {
+  const int64_t es = dtype == RAT_DTYPE_BF16 ? 2 : 4;
+  L.act = ((int64_t)B * H * T * hd * es + 255) / 256 * 256;
+  L.off_scan = 7 * L.act;
+  L.scan_bytes = rat_scan_workspace_bytes(B, H, T, hd);
+  if (L.scan_bytes < 0) return false;
+  L.bytes = L.off_scan + L.scan_bytes;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t rat_layer_workspace_bytes(int dtype, int B, int H, int64_t T, int hd) {
+  if (B < 0 || H < 0 || T < 0 || T > kMaxT) return RAT_ERR_INVALID_ARG;
+  if (dtype != RAT_DTYPE_BF16 && dtype != RAT_DTYPE_F32) return RAT_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 128) return RAT_ERR_UNSUPPORTED;
+  LayerLayout L;
+  if (!layer_layout(dtype, B, H, T, hd, L)) return RAT_ERR_UNSUPPORTED;
+  return L.bytes;
+}
+
+int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const int32_t* D,
+                      const int32_t* W, float scale, int64_t T_cap, const void* x,
+                      const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+                      const float* b_g, const void* w_o, void* out, float* lse, void* Kc,
+                      void* Vc, void* k_ring, void* v_ring, float* state_k, float* state_v,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(dtype, B, H, hd, D, W);
+  if (st != RAT_OK) return st;
+  if (T < 0 || T_cap > kMaxT || dm <= 0) return RAT_ERR_INVALID_ARG;
+  if (T > T_cap) return RAT_ERR_CAPACITY;
+  if (B == 0 || H == 0 || T == 0) return RAT_OK;
+  const void* ptrs[] = {x, w_q, w_k, w_v, w_g, b_g, w_o, out};
+  for (const void* ptr : ptrs)
+    if (ptr == nullptr || !aligned16(ptr)) return RAT_ERR_INVALID_ARG;
+  const int64_t HD = (int64_t)H * hd;
+  if ((int64_t)B * T > INT32_MAX || HD > INT32_MAX || T * HD > INT32_MAX)
+    return RAT_ERR_UNSUPPORTED;
+  LayerLayout L;
+  if (!layer_layout(dtype, B, H, T, hd, L)) return RAT_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < L.bytes)
+    return RAT_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* q = ws;
+  void* k = ws + L.act;
+  void* v = ws + 2 * L.act;
+  void* g = ws + 3 * L.act;
+  void* hk = ws + 4 * L.act;
+  void* hv = ws + 5 * L.act;
+  void* o = ws + 6 * L.act;
+  int herr;
+  rocblas_handle hb = blas_handle(herr);
+  if (herr != RAT_OK) return herr;
+  static std::mutex blas_mu;  // the shared handle's stream is set per call
+  const rocblas_datatype dt = dtype == RAT_DTYPE_BF16 ? rocblas_datatype_bf16_r
+                                                       : rocblas_datatype_f32_r;
+  const int64_t es = dtype == RAT_DTYPE_BF16 ? 2 : 4;
+  const float one = 1.f, zero = 0.f;
+  {
+    std::lock_guard<std::mutex> lock(blas_mu);
+    if (rocblas_set_stream(hb, reinterpret_cast<hipStream_t>(stream)) != rocblas_status_success)
+      return RAT_ERR_HIP;
+    // projections straight into [B,H,T,hd]: for batch row b and head h,
+    // (proj)_{b,h} = x_b W[:, h*hd:(h+1)*hd].  Column-major view: the
+    // hd x T block C = W_h^T x_b^T, with W row-major [dm, H*hd] (ld H*hd,
+    // head h at column offset h*hd) and x_b row-major [T, dm] (ld dm); one
+    // strided batch over the heads per batch row (x_b shared: stride 0).
+    const void* wts[4] = {w_q, w_k, w_v, w_g};
+    void* dst[4] = {q, k, v, g};
+    for (int pj = 0; pj < 4; ++pj)
+      for (int b = 0; b < B; ++b) {
+        const char* xb = static_cast<const char*>(x) + (int64_t)b * T * dm * es;
+        char* cb = static_cast<char*>(dst[pj]) + (int64_t)b * H * T * hd * es;
+        rocblas_status r = rocblas_gemm_strided_batched_ex(
+            hb, rocblas_operation_none, rocblas_operation_none, hd, (int)T, dm, &one, wts[pj], dt,
+            (int)HD, hd, xb, dt, dm, 0, &zero, cb, dt, hd, T * hd, cb, dt, hd, T * hd, H,
+            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+        if (r != rocblas_status_success) return RAT_ERR_HIP;
+      }
+  }
+  // recurrence with the gate sigmoid(g + b_g) fused into its loads
+  st = scan_impl(dtype, B, H, T, hd, D, W, T_cap, 0, k, v, g, nullptr, nullptr, hk, hv, Kc, Vc,
+                 nullptr, nullptr, k_ring, v_ring, state_k, state_v, ws + L.off_scan,
+                 (size_t)L.scan_bytes, stream, b_g);
+  if (st != RAT_OK) return st;
+  // dilated attention; o written token-major for the output projection
+  st = attn_impl(dtype, B, H, T, hd, D, W, scale, T_cap, 0, q, hk, hv, Kc, Vc, nullptr, nullptr,
+                 o, lse, stream, true);
+  if (st != RAT_OK) return st;
+  {
+    std::lock_guard<std::mutex> lock(blas_mu);
+    if (rocblas_set_stream(hb, reinterpret_cast<hipStream_t>(stream)) != rocblas_status_success)
+      return RAT_ERR_HIP;
+    // out [B*T, dm] = o [B*T, H*hd] W_o [H*hd, dm]; column-major: out^T =
+    // W_o^T o^T with W_o (ld dm) and o (ld H*hd)
+    rocblas_status r = rocblas_gemm_ex(hb, rocblas_operation_none, rocblas_operation_none, dm,
+                                       (int)(B * T), (int)HD, &one, w_o, dt, dm, o, dt, (int)HD,
+                                       &zero, out, dt, dm, out, dt, dm, rocblas_datatype_f32_r,
+                                       rocblas_gemm_algo_standard, 0, 0);
+    if (r != rocblas_status_success) return RAT_ERR_HIP;
+  }
+  return RAT_OK;
 }
 
 }  // extern "C"

@@ -50,6 +50,8 @@ struct ScanParams {
   float* sv;
   const float* sk_in;  // state before row 0 (nullable: zero)
   const float* sv_in;
+  const float* gate_bias;  // nullable; else g is the gate's pre-activation and
+                           // the gate is sigmoid(g + gate_bias[h*hd + c])
   uint32_t* hdr;    // workspace header (kScanHeaderBytes)
   uint64_t* agg;    // [entries][3][hd]: (tag << 32 | fp32) of A, Bk, Bv
   HeadTables ht;
@@ -79,6 +81,9 @@ struct AttnParams {
   const void* vr;
   int64_t WS;        // ring slots per batch row
   void* o;
+  int64_t o_sb, o_sh, o_st;  // element strides of o over b, h, t ([B,H,T,hd]:
+                             // H*T*hd, T*hd, hd; token-major [B,T,H,hd]:
+                             // T*H*hd, hd, H*hd)
   float* lse;        // nullable
   int32_t perm[kMaxHeads];  // heads in descending per-block cost
   HeadTables ht;

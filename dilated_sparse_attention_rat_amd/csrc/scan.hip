@@ -188,7 +188,7 @@ __device__ __forceinline__ void load_rows(const ScanParams& p, uint32_t ticket,
 // runs after the carry is known and before pass 2: the caller issues the
 // next chunk's loads there, so that no tree load waits behind them (vector
 // memory counters complete in order) while pass 2 still overlaps them.
-template <typename ST, int HD, int S, typename F>
+template <typename ST, int HD, int S, bool GATE, typename F>
 __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket, uint32_t tag,
                                            const ChunkRows<ST, HD, S>& rw, float (*s_A)[HD],
                                            float (*s_Bk)[HD], float (*s_Bv)[HD], float* s_hk,
@@ -211,6 +211,20 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
   const u32x4* rk = rw.k;
   const u32x4* rv = rw.v;
   const u32x4* rg = rw.g;
+  // GATE: g holds the gate's pre-activation; the gate is sigmoid(g + bias)
+  // with the head's per-channel bias (fused here instead of a separate pass)
+  float gbias[VEC];
+  if constexpr (GATE) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) gbias[i] = p.gate_bias[h * HD + c0 + i];
+  }
+  auto gate = [&](float (&gf)[VEC]) {
+    if constexpr (GATE) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i)
+        gf[i] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(gf[i] + gbias[i]) * kLog2e));
+    }
+  };
 
   // ---- pass 1: affine map of this lane's rows ----------------------------
   float A[VEC], Bk[VEC], Bv[VEC];
@@ -226,6 +240,7 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
     if (t < T) {
       float gf[VEC], kf[VEC], vf[VEC];
       unpack16(rg[s], gf, (ST*)nullptr);
+      gate(gf);
       unpack16(rk[s], kf, (ST*)nullptr);
       unpack16(rv[s], vf, (ST*)nullptr);
 #pragma unroll
@@ -332,6 +347,7 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
       if (t < T) {
         float gf[VEC], kf[VEC], vf[VEC];
         unpack16(rg[s], gf, (ST*)nullptr);
+        gate(gf);
         unpack16(rk[s], kf, (ST*)nullptr);
         unpack16(rv[s], vf, (ST*)nullptr);
 #pragma unroll
@@ -381,7 +397,7 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
 // the smallest unfinished ticket can always proceed (no deadlock), and no
 // ticket counter (atomic) is needed.  Every workgroup reads the epoch first;
 // the last one to finish advances it, so the epoch is this launch's tag.
-template <typename ST, int HD, int S>
+template <typename ST, int HD, int S, bool GATE>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void scan_kernel(const ScanParams p) {
   constexpr int VEC = StTraits<ST>::VEC;
@@ -412,12 +428,12 @@ void scan_kernel(const ScanParams p) {
     const uint32_t t1 = ticket + G;
     // (prefetches are unconditional -- past the end they re-load the last
     // ticket and are ignored -- so outstanding loads are counted exactly)
-    scan_chunk<ST, HD, S>(p, ticket, tag, ra, s_A, s_Bk, s_Bv, s_hk, s_hv,
+    scan_chunk<ST, HD, S, GATE>(p, ticket, tag, ra, s_A, s_Bk, s_Bv, s_hk, s_hv,
                           [&] { load_rows<ST, HD, S>(p, min(t1, n - 1), rb); });
     __syncthreads();  // LDS is reused by the next chunk
     if (t1 >= n) break;
     const uint32_t t2 = t1 + G;
-    scan_chunk<ST, HD, S>(p, t1, tag, rb, s_A, s_Bk, s_Bv, s_hk, s_hv,
+    scan_chunk<ST, HD, S, GATE>(p, t1, tag, rb, s_A, s_Bk, s_Bv, s_hk, s_hv,
                           [&] { load_rows<ST, HD, S>(p, min(t2, n - 1), ra); });
     __syncthreads();
     ticket = t2;
@@ -504,7 +520,11 @@ int launch_scan_t(const ScanParams& p, hipStream_t st) {
                        p.sk, p.sv, p.sk_in, p.sv_in, n);
     return (int)hipGetLastError();
   }
-  const void* kern = reinterpret_cast<const void*>(&scan_kernel<ST, HD, kScanRowsPerThread>);
+  // the gated variant has its own register use, hence its own residency limit
+  const bool gated = p.gate_bias != nullptr;
+  const void* kern = gated
+      ? reinterpret_cast<const void*>(&scan_kernel<ST, HD, kScanRowsPerThread, true>)
+      : reinterpret_cast<const void*>(&scan_kernel<ST, HD, kScanRowsPerThread, false>);
   const int lim = coop_grid_limit(kern, kScanThreads);
   if (lim <= 0) return (int)hipErrorInvalidValue;
   // A plain launch: with the grid within the device's capacity every
@@ -514,8 +534,12 @@ int launch_scan_t(const ScanParams& p, hipStream_t st) {
   // CUs, the late workgroups start when those finish; a wait that outlasts
   // the spin bound is reported in the workspace error word, never a hang.
   const unsigned grid = (unsigned)std::min<int64_t>(p.nticket, lim);
-  hipLaunchKernelGGL((scan_kernel<ST, HD, kScanRowsPerThread>), dim3(grid), dim3(kScanThreads), 0,
-                     st, p);
+  if (gated)
+    hipLaunchKernelGGL((scan_kernel<ST, HD, kScanRowsPerThread, true>), dim3(grid),
+                       dim3(kScanThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((scan_kernel<ST, HD, kScanRowsPerThread, false>), dim3(grid),
+                       dim3(kScanThreads), 0, st, p);
   return (int)hipGetLastError();
 }
 

@@ -282,6 +282,45 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * Bytes of device workspace rat_layer_prefill needs.  Zero-fill it once
+ * before its first use (it holds a scan workspace); afterwards it is ready
+ * for every later call.  Pure host function; bytes (> 0) or a negative code.
+ */
+int64_t rat_layer_workspace_bytes(int dtype, int B, int H, int64_t T, int hd);
+
+/*
+ * One RAT+ layer over a prefill: the steps on either side of the hot path
+ * (abstract: RAT+ augments the attention of a transformer layer; deep dive,
+ * section 2.1: the input-dependent forget gate) around rat_scan_prefill and
+ * rat_dilated_attn_prefill:
+ *   q = x W_q, k = x W_k, v = x W_v (per head h: columns h*hd .. h*hd+hd-1);
+ *   g = sigmoid(x W_g + b_g)   (the bias and sigmoid fused into the scan);
+ *   recurrence, anchor cache, ring, state and dilated attention as in the
+ *   two prefill entry points (same D, W, scale, T_cap);
+ *   out = o W_o with o [B, T, H*hd] (heads concatenated).
+ * Reads  x [B, T, dm] ST; w_q, w_k, w_v, w_g [dm, H*hd] ST (row-major);
+ *        b_g [H*hd] fp32; w_o [H*hd, dm] ST.
+ * Writes out [B, T, dm] ST; lse [B, H, T] fp32 (nullable); Kc, Vc, k_ring,
+ *        v_ring, state_k, state_v as rat_scan_prefill.
+ * The projections run as rocBLAS GEMMs (bf16 or fp32 in and out, fp32
+ * accumulation) on the same stream.  Unlike the other entry points this one
+ * uses a library with state of its own: the first call on a device creates a
+ * rocBLAS handle there (kept until the process ends), and rocBLAS manages
+ * its own device memory.  Calls from several host threads are safe (the
+ * handle's stream is set under a lock).
+ * workspace: rat_layer_workspace_bytes bytes (q, k, v, the gate
+ * pre-activation, the states and o, then a scan workspace).
+ */
+int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm,
+                      const int32_t* D, const int32_t* W, float scale,
+                      int64_t T_cap, const void* x, const void* w_q,
+                      const void* w_k, const void* w_v, const void* w_g,
+                      const float* b_g, const void* w_o, void* out, float* lse,
+                      void* Kc, void* Vc, void* k_ring, void* v_ring,
+                      float* state_k, float* state_v, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,5 +9,5 @@ against closed forms, brute force and library routines; nothing in it is
 "parity unpinned".
 """
 from .oracle import (anchor_offsets, attention, attention_rows, backward, build,  # noqa: F401
-                     build_cache, decode_step, in_keyset, keyset_size, lib,
+                     build_cache, decode_step, in_keyset, keyset_size, layer_prefill, lib,
                      num_threads, prefill, round_bf16, scan)

@@ -240,3 +240,26 @@ def backward(q, k, v, g, dO, D, W, scale, st_bf16: bool):
     lib().rat_oracle_backward(B, H, T, hd, _p(D), _p(W), float(scale), _p(q), _p(k),
                               _p(v), _p(g), _p(dO), int(st_bf16), *[_p(a) for a in out])
     return dict(dq=out[0], dk=out[1], dv=out[2], dg=out[3])
+
+
+def layer_prefill(x, w_q, w_k, w_v, w_g, b_g, w_o, H: int, hd: int, D, W, scale, st_bf16: bool):
+    """One layer over a prefill: projections (numpy matmul in float64; each
+    projection output rounded to the storage type, as stored), the gate
+    sigmoid(x W_g + b_g), the prefill of this module, and out = o W_o with o
+    rounded to the storage type and the heads concatenated.  x: [B,T,dm]."""
+    x = _f64(x)
+    B, T, dm = x.shape
+
+    def heads(y):  # [B,T,H*hd] -> [B,H,T,hd]
+        return np.ascontiguousarray(y.reshape(B, T, H, hd).transpose(0, 2, 1, 3))
+
+    rnd = round_bf16 if st_bf16 else (lambda a: a)
+    q = heads(rnd(x @ _f64(w_q)))
+    k = heads(rnd(x @ _f64(w_k)))
+    v = heads(rnd(x @ _f64(w_v)))
+    gpre = heads(rnd(x @ _f64(w_g)))
+    g = 1.0 / (1.0 + np.exp(-(gpre + _f64(b_g).reshape(1, H, 1, hd))))
+    r = prefill(q, k, v, g, D, W, scale, st_bf16)
+    o = rnd(r["o"]).transpose(0, 2, 1, 3).reshape(B, T, H * hd)
+    r["out"] = o @ _f64(w_o)
+    return r

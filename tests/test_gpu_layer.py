@@ -1,0 +1,88 @@
+"""GPU parity of one RAT+ layer over a prefill (projections as rocBLAS GEMMs,
+the gate fused into the scan, dilated attention, output projection) against
+the oracle's layer, through the C ABI.
+
+Tolerances, relative to the tensor's scale (max |err| / max |ref| and mean
+|err| / mean |ref|): bf16 2e-2 for both -- the projections are rounded to
+bf16 after an fp32 sum taken in another order than the oracle's float64 sum,
+so single elements may land one bf16 step apart, and the recurrence and the
+output projection carry that along (observed: about 4e-3 for out); fp32
+1e-5 (observed: below 1e-6).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+
+from gpu_common import Checks, say, to_dev, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+TOL = {"bf16": (2e-2, 2e-2), "f32": (1e-5, 1e-5)}
+
+
+def check_rel(name, got, ref, dtype):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    d = np.abs(got - ref)
+    mx = float(d.max()) / max(float(np.abs(ref).max()), 1e-30)
+    mn = float(d.mean()) / max(float(np.abs(ref).mean()), 1e-30)
+    say(f"  {name}: max|err|/max|ref|={mx:.2e}  mean|err|/mean|ref|={mn:.2e}")
+    tmax, tmean = TOL[dtype]
+    assert mx <= tmax and mn <= tmean, f"{name}: {mx}, {mn}"
+
+
+CASES = [
+    # label, B, H, T, hd, dm, D, W, dtype
+    ("bf16-hybrid", 2, 3, 300, 128, 256, [4, 1, 16], [0, 37, 3], "bf16"),
+    ("bf16-64-resident", 1, 4, 640, 64, 192, [16, 8, 16, 32], [0, 0, 0, 0], "bf16"),
+    ("f32-64", 2, 2, 130, 64, 96, [3, 5], [4, 0], "f32"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_layer_matches_oracle(case):
+    import dilated_sparse_attention_rat_amd as rat
+    label, B, H, T, hd, dm, D, W, dtype = case
+    say(f"[layer] {label}: B={B} H={H} T={T} hd={hd} dm={dm} D={D} W={W} {dtype}")
+    rng = np.random.default_rng(zlib.crc32(label.encode()) % 1000)
+    HD = H * hd
+    qkv_std = 1.0 if dtype == "f32" else hd ** -0.5
+
+    def r(shape, std):
+        a = (rng.standard_normal(shape) * std).astype(np.float32)
+        return oracle.round_bf16(a).astype(np.float32) if dtype == "bf16" else a
+
+    x = r((B, T, dm), 1.0)
+    wq, wk, wv = (r((dm, HD), qkv_std / np.sqrt(dm)) for _ in range(3))
+    wg = r((dm, HD), 1.0 / np.sqrt(dm))
+    bg = np.full(HD, 3.0, np.float32)
+    wo = r((HD, dm), 1.0 / np.sqrt(HD))
+    D, W = np.array(D, np.int32), np.array(W, np.int32)
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = lambda a: to_dev(a, dtype)
+    cache = rat.alloc_cache(B, H, hd, T, D, W, st, "cuda")
+    out = torch.empty((B, T, dm), dtype=st, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    ws = rat.layer_workspace(rat.binding._dtype_code(out), B, H, T, hd, "cuda")
+    bgt = torch.from_numpy(bg).cuda()
+    for rep in range(2):  # the workspace is reused as is
+        rat.rat_layer_prefill(dev(x), dev(wq), dev(wk), dev(wv), dev(wg), bgt, dev(wo), out, D, W,
+                              H, hd, T, cache, ws, lse=lse)
+        torch.cuda.synchronize()
+        ref = oracle.layer_prefill(x, wq, wk, wv, wg, bg, wo, H, hd, D, W, hd ** -0.5,
+                                   dtype == "bf16")
+        chk = Checks()
+        chk(check_rel, "out", to_np(out), ref["out"], dtype)
+        chk(check_rel, "lse", to_np(lse), ref["lse"], dtype)
+        chk(check_rel, "state_k", to_np(cache["state_k"]), ref["state_k"], dtype)
+        chk(check_rel, "state_v", to_np(cache["state_v"]), ref["state_v"], dtype)
+        chk.done()

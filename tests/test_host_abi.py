@@ -213,6 +213,27 @@ def test_backward_validation(L):
     assert bwd(B=0) == rb.RAT_OK
 
 
+def test_layer_validation(L):
+    d, w, dp, wp = _tables(2, 4, 0)
+    assert L.rat_layer_workspace_bytes(0, 1, 2, 100, 128) > 0
+    assert L.rat_layer_workspace_bytes(0, 1, 2, 100, 96) == rb.RAT_ERR_UNSUPPORTED
+    assert L.rat_layer_workspace_bytes(3, 1, 2, 100, 128) == rb.RAT_ERR_UNSUPPORTED
+
+    def layer(dm=64, T=16, T_cap=16, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30, B=1, hd=64):
+        return L.rat_layer_prefill(0, B, 2, T, hd, dm, dp, wp, 0.0, T_cap, *([_p(ptr)] * 16),
+                                   ws_bytes, None) if ws == FAKE else \
+            L.rat_layer_prefill(0, B, 2, T, hd, dm, dp, wp, 0.0, T_cap, *([_p(ptr)] * 15),
+                                _p(ws) if ws else None, ws_bytes, None)
+
+    assert layer(dm=0) == rb.RAT_ERR_INVALID_ARG
+    assert layer(hd=96) == rb.RAT_ERR_UNSUPPORTED
+    assert layer(T=17) == rb.RAT_ERR_CAPACITY
+    assert layer(ptr=0) == rb.RAT_ERR_INVALID_ARG
+    assert layer(ws=0) == rb.RAT_ERR_WORKSPACE
+    assert layer(ws_bytes=64) == rb.RAT_ERR_WORKSPACE
+    assert layer(B=0) == rb.RAT_OK
+
+
 def _dec(L, dtype=0, B=1, H=2, hd=64, D=4, W=0, pos=5, T_cap=16, splits=0, ws=0, ws_bytes=0,
          q=FAKE):
     d, w, dp, wp = _tables(H, D, W)

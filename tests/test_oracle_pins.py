@@ -429,6 +429,63 @@ def test_backward_storage_rounding_is_straight_through():
         np.testing.assert_array_equal(a[n], b[n])
 
 
+# --------------------------------------------------------------------------
+# layer: projections around the prefill
+# --------------------------------------------------------------------------
+def test_layer_identity_projections_reduce_to_prefill():
+    """With W_q = W_k = W_v = W_o = I (dm = H*hd), W_g = 0 and a per-channel
+    gate bias, the layer is the prefill of x split into heads with the gate
+    sigmoid(b_g); per-head D and W make a head-layout mistake visible."""
+    B, T, H, hd = 2, 30, 3, 4
+    dm = H * hd
+    x = _rand((B, T, dm))
+    bg = _rand((H * hd,))
+    eye, zero = np.eye(dm), np.zeros((dm, dm))
+    D, W = [3, 1, 7], [0, 4, 2]
+    r = oracle.layer_prefill(x, eye, eye, eye, zero, bg, eye, H, hd, D, W, 0.4, False)
+    xh = x.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+    g = np.broadcast_to(1.0 / (1.0 + np.exp(-bg.reshape(1, H, 1, hd))), xh.shape)
+    ref = oracle.prefill(xh, xh, xh, g, D, W, 0.4, False)
+    np.testing.assert_allclose(r["o"], ref["o"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(r["out"], ref["o"].transpose(0, 2, 1, 3).reshape(B, T, dm),
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_layer_projections_bruteforce():
+    """Every projection and the output projection, written as explicit sums
+    over the model dimension for a tiny case."""
+    B, T, H, hd, dm = 1, 6, 2, 4, 5
+    x = _rand((B, T, dm))
+    wq, wk, wv, wg = (_rand((dm, H * hd)) for _ in range(4))
+    wo = _rand((H * hd, dm))
+    bg = _rand((H * hd,))
+    D, W = [2, 3], [1, 0]
+    r = oracle.layer_prefill(x, wq, wk, wv, wg, bg, wo, H, hd, D, W, 0.5, False)
+
+    def proj(w):
+        y = np.zeros((B, H, T, hd))
+        for b in range(B):
+            for h in range(H):
+                for t in range(T):
+                    for c in range(hd):
+                        y[b, h, t, c] = sum(x[b, t, j] * w[j, h * hd + c] for j in range(dm))
+        return y
+
+    q, k, v, gp = proj(wq), proj(wk), proj(wv), proj(wg)
+    g = np.zeros_like(gp)
+    for h in range(H):
+        for c in range(hd):
+            g[:, h, :, c] = 1.0 / (1.0 + math.e ** (-(gp[:, h, :, c] + bg[h * hd + c])))
+    ref = oracle.prefill(q, k, v, g, D, W, 0.5, False)
+    out = np.zeros((B, T, dm))
+    for b in range(B):
+        for t in range(T):
+            for i in range(dm):
+                out[b, t, i] = sum(ref["o"][b, h, t, c] * wo[h * hd + c, i]
+                                   for h in range(H) for c in range(hd))
+    np.testing.assert_allclose(r["out"], out, rtol=1e-10, atol=1e-12)
+
+
 MUTANTS = [
     ("backward drops the softmax mean", "const double ds = p[j] * (dp[j] - delta);",
      "const double ds = p[j] * dp[j];", ["backward"]),
