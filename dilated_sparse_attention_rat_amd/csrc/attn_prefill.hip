@@ -312,15 +312,12 @@ struct RowMap {
 };
 
 // One query tile of 64*QB queries at local row lt0 (absolute position
-// p.t0 + lt0).  `qin` holds this tile's query inputs (already loaded); if
-// `next_lt0` >= 0, the inputs of the query tile at next_lt0 are loaded into
-// `qnext` right after they are consumed here, so their HBM latency overlaps
-// this tile's key loop.  Positions (queries, band keys, anchors) are
-// absolute; rows of q, hk, hv, o and lse are local to this call.
+// p.t0 + lt0).  `qin` holds this tile's query inputs (already loaded).
+// Positions (queries, band keys, anchors) are absolute; rows of q, hk, hv,
+// o and lse are local to this call.
 template <typename ST, int HD, int QB, bool RING>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, int lt0, ST* sK,
-                                             ST* sVt, const QueryIn<ST, HD, QB>& qin,
-                                             QueryIn<ST, HD, QB>& qnext, int next_lt0) {
+                                             ST* sVt, const QueryIn<ST, HD, QB>& qin) {
   using C = AttnCfg<ST, HD, QB>;
   constexpr int QW = 16 * QB;  // queries per wave
   const int tid = threadIdx.x;
@@ -333,7 +330,6 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   const int D = p.ht.D[h];
   const int W = p.ht.W[h];
   const int64_t bh = (int64_t)b * p.H + h;
-  const ST* qp = reinterpret_cast<const ST*>(p.q) + bh * T * HD;
   const ST* hkp = reinterpret_cast<const ST*>(p.hk) + bh * T * HD;
   const ST* hvp = reinterpret_cast<const ST*>(p.hv) + bh * T * HD;
   const ST* kcp = reinterpret_cast<const ST*>(p.Kc) + ((int64_t)b * p.R + p.ht.aoff[h]) * HD;
@@ -412,7 +408,6 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] = qin.v[nb][db].f32();
   }
-  if (next_lt0 >= 0) qnext.load(qp, hkp, hvp, next_lt0 + QW * wave, T);
 
   const int w_end = wave_active ? max(0, awlast - W) / D : 0;
   const int w_full = wave_active ? max(0, aw0 - W) / D : 0;
@@ -455,13 +450,16 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   }
 }
 
-// Occupancy target: 2 waves per SIMD (two workgroups per CU) for both QB, so
-// one workgroup's MFMAs overlap the other's staging and softmax (QB = 2 fits
-// the resulting 256-register budget without spills).  RING: a continuation
-// whose window reaches before t0 (band rows from the previous call's ring);
+// Occupancy: one workgroup's MFMAs overlap the others' staging and softmax.
+// QB = 2 runs 2 waves per SIMD (fits the 256-register budget without
+// spills); QB = 1 runs 3 (168 registers; its tiles are short and wait on
+// memory, so more waves in flight beat prefetching the partner tile's
+// queries, which would need 48 more registers).  RING: a continuation whose
+// window reaches before t0 (band rows from the previous call's ring);
 // without it the band tiles are plain linear reads.
 template <typename ST, int HD, int QB, bool RING>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(QB == 1 ? 3 : 2, QB == 1 ? 3 : 2)))
 void attn_prefill_kernel(const AttnParams p) {
   using C = AttnCfg<ST, HD, QB>;
   __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::KSTR];
@@ -486,15 +484,12 @@ void attn_prefill_kernel(const AttnParams p) {
   const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
   const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
   const int wave = threadIdx.x >> 6;
-  QueryIn<ST, HD, QB> q0, q1;
-  q0.load(qp, hkp, hvp, qa * C::BM + 16 * QB * wave, p.T);
-  // QB = 1 (streaming-bound): the partner tile's query inputs are loaded
-  // while the first tile runs; QB = 2 has no registers to spare for that
-  const bool pre = QB == 1 && ntiles == 2;
-  process_tile<ST, HD, QB, RING>(p, b, h, qa * C::BM, sK, sVt, q0, q1, pre ? pr * C::BM : -1);
+  QueryIn<ST, HD, QB> qin;
+  qin.load(qp, hkp, hvp, qa * C::BM + 16 * QB * wave, p.T);
+  process_tile<ST, HD, QB, RING>(p, b, h, qa * C::BM, sK, sVt, qin);
   if (ntiles == 2) {
-    if (!pre) q1.load(qp, hkp, hvp, pr * C::BM + 16 * QB * wave, p.T);
-    process_tile<ST, HD, QB, RING>(p, b, h, pr * C::BM, sK, sVt, q1, q0, -1);
+    qin.load(qp, hkp, hvp, pr * C::BM + 16 * QB * wave, p.T);
+    process_tile<ST, HD, QB, RING>(p, b, h, pr * C::BM, sK, sVt, qin);
   }
 }
 

@@ -39,6 +39,21 @@ namespace rat {
 
 namespace {
 
+// XCD-aware block order: workgroups are dealt round-robin over the 8 XCDs,
+// each with its own L2.  Block L is the (L / 8)-th block of XCD L % 8; the
+// per-XCD sequence runs over whole (b, h) groups of n blocks, so all blocks
+// of one (b, h) -- which share that head's Q, dO and anchor rows -- run on
+// one XCD.  Returns false for the padding blocks past B*H.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool xcd_group(int nbh, int n, int& bh, int& x) {
+  const int L = blockIdx.x;
+  const int xcd = L % kXcds;
+  const int s = L / kXcds;
+  bh = (s / n) * kXcds + xcd;
+  x = s % n;
+  return bh < nbh;
+}
+
 template <typename ST, int HD>
 struct BwdCfg {
   static constexpr int BN = 64;          // keys (or queries) per staged tile
@@ -130,9 +145,11 @@ void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) ST sKt[HD * C::TSTR];
 
   const int nq = (p.T + C::BN - 1) / C::BN;
-  const int qt = nq - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  int bhi, xi;
+  if (!xcd_group(p.B * p.H, nq, bhi, xi)) return;
+  const int qt = nq - 1 - xi;
+  const int h = bhi % p.H;
+  const int b = bhi / p.H;
   const int T = p.T;
   const int D = p.ht.D[h];
   const int W = p.ht.W[h];
@@ -304,15 +321,16 @@ void bwd_dkv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) float sL[C::BN];
   __shared__ __attribute__((aligned(16))) float sDl[C::BN];
 
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  int bhi, x;
+  if (!xcd_group(p.B * p.H, p.nkt, bhi, x)) return;
+  const int h = bhi % p.H;
+  const int b = bhi / p.H;
   const int T = p.T;
   const int D = p.ht.D[h];
   const int W = p.ht.W[h];
   const int na = T / D;                              // anchors of the head
   const int na_t = (na + C::BN - 1) / C::BN;
   const int nb_t = W > 0 ? (T + C::BN - 1) / C::BN : 0;
-  const int x = blockIdx.x;
   if (x >= na_t * p.nsplit + nb_t) return;
   const bool anchor = x < na_t * p.nsplit;
   const int split = anchor ? x % p.nsplit : 0;
@@ -639,9 +657,10 @@ __global__ __launch_bounds__(256) void bwd_rscan_apply_kernel(const BwdParams p)
 template <typename ST, int HD>
 int launch_t(const BwdParams& p, hipStream_t st) {
   const int nq = (p.T + 63) / 64;
-  hipLaunchKernelGGL((bwd_dq_kernel<ST, HD>), dim3(nq, p.H, p.B), dim3(256), 0, st, p);
+  const int ngrp = (p.B * p.H + kXcds - 1) / kXcds * kXcds;  // (b, h) groups, padded
+  hipLaunchKernelGGL((bwd_dq_kernel<ST, HD>), dim3(ngrp * nq), dim3(256), 0, st, p);
   if (p.nkt > 0)
-    hipLaunchKernelGGL((bwd_dkv_kernel<ST, HD>), dim3(p.nkt, p.H, p.B), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dkv_kernel<ST, HD>), dim3(ngrp * p.nkt), dim3(256), 0, st, p);
   const int ncb = (p.nchunk + RCfg<ST, HD>::CPB - 1) / RCfg<ST, HD>::CPB;
   hipLaunchKernelGGL((bwd_rscan_agg_kernel<ST, HD>), dim3(ncb, p.H, p.B), dim3(256), 0, st, p);
   hipLaunchKernelGGL((bwd_rscan_carry_kernel<HD>), dim3(p.B * p.H), dim3(HD), 0, st, p);
