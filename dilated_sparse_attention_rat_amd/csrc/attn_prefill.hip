@@ -172,16 +172,20 @@ struct QueryIn {
   Raw4<ST> v[QB][C::NDB];
 
   // rows of the wave's queries tw0 + 16*nb + (lane % 16), clamped to T-1
-  __device__ __forceinline__ void load(const ST* qp, const ST* hkp, const ST* hvp, int tw0, int T) {
+  // (q rows q_st elements apart, state rows HD apart)
+  __device__ __forceinline__ void load(const ST* qp, const ST* hkp, const ST* hvp, int tw0, int T,
+                                       int64_t q_st) {
     const int lane = threadIdx.x & 63;
     const int col = lane & 15;
     const int g = lane >> 4;
 #pragma unroll
     for (int nb = 0; nb < QB; ++nb) {
-      const int64_t row = (int64_t)min(tw0 + 16 * nb + col, T - 1) * HD;
+      const int tr = min(tw0 + 16 * nb + col, T - 1);
+      const int64_t row = (int64_t)tr * HD;
+      const int64_t qrow = (int64_t)tr * q_st;
 #pragma unroll
       for (int s = 0; s < C::NS; ++s) {
-        q[nb][s] = frag_ld8(qp + row + 32 * s + 8 * g);
+        q[nb][s] = frag_ld8(qp + qrow + 32 * s + 8 * g);
         k[nb][s] = frag_ld8(hkp + row + 32 * s + 8 * g);
       }
 #pragma unroll
@@ -480,15 +484,15 @@ void attn_prefill_kernel(const AttnParams p) {
   const int ntiles = pr < qa ? 2 : 1;
   const int64_t bh = (int64_t)b * p.H + h;
   const int64_t off = bh * p.T * HD;
-  const ST* qp = reinterpret_cast<const ST*>(p.q) + off;
+  const ST* qp = reinterpret_cast<const ST*>(p.q) + (bh / p.H) * p.q_sb + (bh % p.H) * p.q_sh;
   const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
   const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
   const int wave = threadIdx.x >> 6;
   QueryIn<ST, HD, QB> qin;
-  qin.load(qp, hkp, hvp, qa * C::BM + 16 * QB * wave, p.T);
+  qin.load(qp, hkp, hvp, qa * C::BM + 16 * QB * wave, p.T, p.q_st);
   process_tile<ST, HD, QB, RING>(p, b, h, qa * C::BM, sK, sVt, qin);
   if (ntiles == 2) {
-    qin.load(qp, hkp, hvp, pr * C::BM + 16 * QB * wave, p.T);
+    qin.load(qp, hkp, hvp, pr * C::BM + 16 * QB * wave, p.T, p.q_st);
     process_tile<ST, HD, QB, RING>(p, b, h, pr * C::BM, sK, sVt, qin);
   }
 }
@@ -623,14 +627,14 @@ void attn_resident_kernel(const AttnParams p) {
   const int stride = p.nra * kResidentWaves;
   const int first = r + p.nra * wave;
   const int64_t off = bh * T * HD;
-  const ST* qp = reinterpret_cast<const ST*>(p.q) + off;
+  const ST* qp = reinterpret_cast<const ST*>(p.q) + (bh / p.H) * p.q_sb + (bh % p.H) * p.q_sh;
   const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
   const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
   // the wave's blocks first + j*stride; sixteen waves per CU hide the load
   // latency of each block's query inputs
   for (int bi = first; bi < nblk; bi += stride) {
     QueryIn<ST, HD, 1> qa;
-    qa.load(qp, hkp, hvp, 16 * bi, T);
+    qa.load(qp, hkp, hvp, 16 * bi, T, p.q_st);
     resident_block<ST, HD>(p, bh, D, 16 * bi, sK, sVt, qa);
   }
 }

@@ -153,7 +153,7 @@ int scan_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
               const float* sk_in, const float* sv_in, void* hk, void* hv, void* Kc, void* Vc,
               const void* kr_in, const void* vr_in, void* k_ring, void* v_ring, float* state_k,
               float* state_v, void* workspace, size_t workspace_bytes, void* stream,
-              const float* gate_bias = nullptr) {
+              const float* gate_bias = nullptr, bool in_tok = false) {
   int st = check_common(dtype, B, H, hd, D, W);
   if (st != RAT_OK) return st;
   if (T < 0 || t0 < 0 || T_cap > kMaxT) return RAT_ERR_INVALID_ARG;
@@ -213,6 +213,10 @@ int scan_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
   p.sk_in = sk_in;
   p.sv_in = sv_in;
   p.gate_bias = gate_bias;
+  // k, v, g: [B,H,T,hd], or token-major [B,T,H,hd] (in_tok)
+  p.in_sb = (int64_t)H * T * hd;
+  p.in_sh = in_tok ? hd : T * hd;
+  p.in_st = in_tok ? (int64_t)H * hd : hd;
   if (p.WS > 0 && t0 > 0 && kr_in != nullptr && kr_in != k_ring) {
     // window positions before t0 that stay in the window: previous ring ->
     // new ring (disjoint from the slots the scan writes)
@@ -254,7 +258,8 @@ namespace {
 int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, const int32_t* W,
               float scale, int64_t T_cap, int64_t t0, const void* q, const void* hk,
               const void* hv, const void* Kc, const void* Vc, const void* kr_prev,
-              const void* vr_prev, void* o, float* lse, void* stream, bool o_tok = false) {
+              const void* vr_prev, void* o, float* lse, void* stream, bool o_tok = false,
+              bool q_tok = false) {
   int st = check_common(dtype, B, H, hd, D, W);
   if (st != RAT_OK) return st;
   if (T < 0 || t0 < 0 || T_cap > kMaxT) return RAT_ERR_INVALID_ARG;
@@ -311,6 +316,9 @@ int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
   if ((int64_t)H * B * p.np > INT32_MAX) return RAT_ERR_UNSUPPORTED;
   p.scale_log2 = sc * 1.4426950408889634f;
   p.q = q;
+  p.q_sb = (int64_t)H * T * hd;
+  p.q_sh = q_tok ? hd : T * hd;
+  p.q_st = q_tok ? (int64_t)H * hd : hd;
   p.hk = hk;
   p.hv = hv;
   p.Kc = Kc;
@@ -606,8 +614,9 @@ rocblas_handle blas_handle(int& err) {
   return h;
 }
 
-// layer workspace: q, k, v, the gate pre-activation and hk, hv in
-// [B,H,T,hd], o token-major [B,T,H,hd] (all ST), then the scan workspace
+// layer workspace: q, k, v and the gate pre-activation token-major
+// [B,T,H,hd] (the projections' output), hk, hv [B,H,T,hd], o token-major
+// (all ST), then the scan workspace
 struct LayerLayout {
   int64_t act = 0, off_scan = 0, scan_bytes = 0, bytes = 0;
 };
@@ -670,38 +679,31 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const 
   static std::mutex blas_mu;  // the shared handle's stream is set per call
   const rocblas_datatype dt = dtype == RAT_DTYPE_BF16 ? rocblas_datatype_bf16_r
                                                        : rocblas_datatype_f32_r;
-  const int64_t es = dtype == RAT_DTYPE_BF16 ? 2 : 4;
   const float one = 1.f, zero = 0.f;
   {
     std::lock_guard<std::mutex> lock(blas_mu);
     if (rocblas_set_stream(hb, reinterpret_cast<hipStream_t>(stream)) != rocblas_status_success)
       return RAT_ERR_HIP;
-    // projections straight into [B,H,T,hd]: for batch row b and head h,
-    // (proj)_{b,h} = x_b W[:, h*hd:(h+1)*hd].  Column-major view: the
-    // hd x T block C = W_h^T x_b^T, with W row-major [dm, H*hd] (ld H*hd,
-    // head h at column offset h*hd) and x_b row-major [T, dm] (ld dm); one
-    // strided batch over the heads per batch row (x_b shared: stride 0).
+    // projections token-major, [B*T, H*hd] = x [B*T, dm] W [dm, H*hd]: one
+    // GEMM each (column-major: Y^T = W^T x^T, W with ld H*hd, x with ld dm)
     const void* wts[4] = {w_q, w_k, w_v, w_g};
     void* dst[4] = {q, k, v, g};
-    for (int pj = 0; pj < 4; ++pj)
-      for (int b = 0; b < B; ++b) {
-        const char* xb = static_cast<const char*>(x) + (int64_t)b * T * dm * es;
-        char* cb = static_cast<char*>(dst[pj]) + (int64_t)b * H * T * hd * es;
-        rocblas_status r = rocblas_gemm_strided_batched_ex(
-            hb, rocblas_operation_none, rocblas_operation_none, hd, (int)T, dm, &one, wts[pj], dt,
-            (int)HD, hd, xb, dt, dm, 0, &zero, cb, dt, hd, T * hd, cb, dt, hd, T * hd, H,
-            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-        if (r != rocblas_status_success) return RAT_ERR_HIP;
-      }
+    for (int pj = 0; pj < 4; ++pj) {
+      rocblas_status r = rocblas_gemm_ex(
+          hb, rocblas_operation_none, rocblas_operation_none, (int)HD, (int)(B * T), dm, &one,
+          wts[pj], dt, (int)HD, x, dt, dm, &zero, dst[pj], dt, (int)HD, dst[pj], dt, (int)HD,
+          rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+      if (r != rocblas_status_success) return RAT_ERR_HIP;
+    }
   }
   // recurrence with the gate sigmoid(g + b_g) fused into its loads
   st = scan_impl(dtype, B, H, T, hd, D, W, T_cap, 0, k, v, g, nullptr, nullptr, hk, hv, Kc, Vc,
                  nullptr, nullptr, k_ring, v_ring, state_k, state_v, ws + L.off_scan,
-                 (size_t)L.scan_bytes, stream, b_g);
+                 (size_t)L.scan_bytes, stream, b_g, true);
   if (st != RAT_OK) return st;
   // dilated attention; o written token-major for the output projection
   st = attn_impl(dtype, B, H, T, hd, D, W, scale, T_cap, 0, q, hk, hv, Kc, Vc, nullptr, nullptr,
-                 o, lse, stream, true);
+                 o, lse, stream, true, true);
   if (st != RAT_OK) return st;
   {
     std::lock_guard<std::mutex> lock(blas_mu);

@@ -52,6 +52,8 @@ struct ScanParams {
   const float* sv_in;
   const float* gate_bias;  // nullable; else g is the gate's pre-activation and
                            // the gate is sigmoid(g + gate_bias[h*hd + c])
+  int64_t in_sb, in_sh, in_st;  // element strides of k, v, g over b, h, t
+                                // ([B,H,T,hd]: H*T*hd, T*hd, hd)
   uint32_t* hdr;    // workspace header (kScanHeaderBytes)
   uint64_t* agg;    // [entries][3][hd]: (tag << 32 | fp32) of A, Bk, Bv
   HeadTables ht;
@@ -73,6 +75,7 @@ struct AttnParams {
   float scale_log2;  // scale * log2(e)
   int64_t R;
   const void* q;
+  int64_t q_sb, q_sh, q_st;  // element strides of q over b, h, t
   const void* hk;
   const void* hv;
   const void* Kc;

@@ -173,11 +173,12 @@ __device__ __forceinline__ void load_rows(const ScanParams& p, uint32_t ticket,
   const int r = tid / LPR;
   const int c0 = (tid - r * LPR) * VEC;
   const int tbase = chunk * LC + r * S;
-  const int64_t seq_base = (int64_t)seq * p.T * HD;
+  const int b = seq / p.H;
+  const int64_t in_base = (int64_t)b * p.in_sb + (int64_t)(seq - b * p.H) * p.in_sh + c0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int t = min(tbase + s, p.T - 1);
-    const int64_t off = seq_base + (int64_t)t * HD + c0;
+    const int64_t off = in_base + (int64_t)t * p.in_st;
     rw.k[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.k) + off);
     rw.v[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.v) + off);
     rw.g[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.g) + off);
