@@ -15,14 +15,18 @@
 //    a workgroup takes a pair of query tiles (i, nq-1-i) so all workgroups of
 //    a head cost about the same; heads are ordered by per-workgroup cost
 //    (heaviest first) so a head-wise hybrid launch is longest-job-first;
-//  * K/V tiles of 64 keys are staged in LDS once per workgroup: K row-major,
-//    V transposed (keys contiguous) so both MFMA operands are plain
-//    ds_read_b128 / ds_read_b64; the global loads of tile i+1 are issued
-//    into registers before tile i's MFMAs, so their latency is hidden;
+//  * K/V tiles of 64 keys are staged in LDS once per workgroup, both
+//    row-major for bf16: K fragments are plain ds_read_b128 and the V^T
+//    fragments of the PV product come out of ds_read_b64_tr_b16, the gfx950
+//    transposing read, so staging is a plain copy (fp32 stages V transposed,
+//    keys contiguous); the global loads of tile i+1 are issued into
+//    registers before tile i's MFMAs, so their latency is hidden;
 //  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16),
 //    so each lane owns one query column: the row max needs two cross-lane
-//    steps, the running sum stays per lane, and P^T is already the B operand
-//    of O^T += V^T P^T (keys permuted identically on both operands);
+//    steps, and P^T is already the B operand of O^T += V^T P^T (keys
+//    permuted identically on both operands); the row sums come out of the
+//    same product through one all-ones V^T block (an MFMA per key slab
+//    instead of a VALU add per score);
 //  * the staircase mask of the anchors (a < floor(max(0,t-W)/D)) and the band
 //    mask of the window are applied only on the tiles that need them;
 //  * the own position is a per-query dot product folded into the initial
@@ -39,6 +43,32 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
+__device__ __forceinline__ Frag<bf16> frag_ones(bf16*) {
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  return f;
+}
+__device__ __forceinline__ Frag<float> frag_ones(float*) {
+  return Frag<float>{f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+// 4j + i / 4 of its group, j = 0..3 (the gfx950 lane layout, checked on the
+// device).  With lanes 4j..4j+3 addressing row j of a 4-row x 16-column
+// block (4 columns each), lane i gets column i of the 4 rows: two reads,
+// the second `step` elements further on, fill the 8 slots of an MFMA
+// fragment.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ Frag<bf16> frag_ld_tr(const bf16* p, int step) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + step));
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  return f;
+}
+
 template <typename ST, int HD, int QB>
 struct AttnCfg {
   static constexpr int BM = 64 * QB;    // queries per tile: 4 waves x 16*QB
@@ -52,12 +82,22 @@ struct AttnCfg {
   // 68 dwords apart (bf16) and V^T rows 34 dwords apart.
   static constexpr int KSTR = HD + 16 / (int)sizeof(ST);  // K tile row stride
   static constexpr int VSTR = BN + 4;                     // V^T tile row stride
+  // row-major V tile (bf16): the transposing reads of a 16-lane group cover
+  // 4 rows x 32 bytes; rows 72 dwords apart put the 8 rows read by each half
+  // wave on disjoint banks
+  static constexpr int VRSTR = HD + 32 / (int)sizeof(ST);
   static constexpr int VEC = StTraits<ST>::VEC;
   static constexpr int CPR = HD / VEC;   // 16-byte chunks per row
+  // bf16: V is staged row-major like K and its transposed MFMA fragments are
+  // read with ds_read_b64_tr_b16; fp32: V is staged transposed (keys
+  // contiguous)
+  static constexpr bool VROW = sizeof(ST) == 2;
   static constexpr int KITEMS = BN * CPR;          // K chunks per tile
-  static constexpr int VITEMS = (BN / 4) * CPR;    // V work items (4 rows x VEC)
+  static constexpr int VITEMS = VROW ? KITEMS : (BN / 4) * CPR;  // V chunks / 4-row items
   static constexpr int KPT = (KITEMS + 255) / 256;  // per thread
   static constexpr int VPT = (VITEMS + 255) / 256;
+  static constexpr int VROWS = VROW ? 1 : 4;       // rows per V item
+  static constexpr int VLDS = VROW ? BN * VRSTR : HD * VSTR;  // V tile elements in LDS
 };
 
 // One K/V tile held in registers between its global load and its LDS store
@@ -68,7 +108,7 @@ template <typename ST, int HD, int QB>
 struct Prefetch {
   using C = AttnCfg<ST, HD, QB>;
   u32x4 k[C::KPT];
-  u32x4 v[C::VPT][4];
+  u32x4 v[C::VPT][C::VROWS];
 
   // Rows [0, BN) of the tile (nvalid >= 1); rows.k(r) / rows.v(r) give the
   // K and V row pointers of tile row r.  Rows at or beyond nvalid re-read row
@@ -89,15 +129,40 @@ struct Prefetch {
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
       const int idx = min(tid + 256 * i, C::VITEMS - 1);
-      const int dg = idx / (C::BN / 4);
-      const int kg = idx - dg * (C::BN / 4);
+      if constexpr (C::VROW) {
+        const int row = idx / C::CPR;
+        const int c16 = idx - row * C::CPR;
+        v[i][0] = ld_raw16(rows.v(min(row, last)) + c16 * C::VEC);
+      } else {
+        const int dg = idx / (C::BN / 4);
+        const int kg = idx - dg * (C::BN / 4);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        v[i][rr] = ld_raw16(rows.v(min(4 * kg + rr, last)) + dg * C::VEC);
+        for (int rr = 0; rr < 4; ++rr)
+          v[i][rr] = ld_raw16(rows.v(min(4 * kg + rr, last)) + dg * C::VEC);
+      }
     }
   }
 
-  // K row-major, V transposed (keys contiguous)
+  // Linear rows (row r of K at kh + r*HD, of V at vh + r*HD), bf16: buffer
+  // loads with 32-bit offsets shared by K and V, one address per chunk.
+  __device__ __forceinline__ void load_linear(const ST* kh, const ST* vh, int nvalid) {
+    static_assert(C::VROW && C::VPT == C::KPT, "row-major V");
+    const auto kr = buffer_region(kh);
+    const auto vr = buffer_region(vh);
+    const int tid = threadIdx.x;
+    const int last = nvalid - 1;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int idx = min(tid + 256 * i, C::KITEMS - 1);
+      const int row = idx / C::CPR;
+      const int c16 = idx - row * C::CPR;
+      const uint32_t off = (uint32_t)((min(row, last) * HD + c16 * C::VEC) * (int)sizeof(ST));
+      k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+      v[i][0] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+    }
+  }
+
+  // K row-major; V row-major (bf16) or transposed (fp32, keys contiguous)
   __device__ __forceinline__ void store(ST* sK, ST* sVt) const {
     const int tid = threadIdx.x;
 #pragma unroll
@@ -105,26 +170,20 @@ struct Prefetch {
       const int idx = tid + 256 * i;
       const int row = idx / C::CPR;
       const int c16 = idx - row * C::CPR;
-      if (idx < C::KITEMS) st_raw16(sK + row * C::KSTR + c16 * C::VEC, k[i]);
+      if (C::KITEMS % 256 == 0 || idx < C::KITEMS) st_raw16(sK + row * C::KSTR + c16 * C::VEC, k[i]);
     }
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
       const int idx = tid + 256 * i;
-      const int dg = idx / (C::BN / 4);
-      const int kg = idx - dg * (C::BN / 4);
-      if (idx >= C::VITEMS) continue;
-      ST* dst = sVt + (dg * C::VEC) * C::VSTR + 4 * kg;
-      if constexpr (sizeof(ST) == 2) {
-#pragma unroll
-        for (int e = 0; e < C::VEC; ++e) {
-          const int w = e >> 1;
-          const int sh = (e & 1) * 16;
-          const uint32_t x0 = (v[i][0][w] >> sh) & 0xffffu, x1 = (v[i][1][w] >> sh) & 0xffffu;
-          const uint32_t x2 = (v[i][2][w] >> sh) & 0xffffu, x3 = (v[i][3][w] >> sh) & 0xffffu;
-          u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
-          *reinterpret_cast<u32x2*>(dst + e * C::VSTR) = pk;
-        }
+      if (C::VITEMS % 256 != 0 && idx >= C::VITEMS) continue;
+      if constexpr (C::VROW) {
+        const int row = idx / C::CPR;
+        const int c16 = idx - row * C::CPR;
+        st_raw16(sVt + row * C::VRSTR + c16 * C::VEC, v[i][0]);
       } else {
+        const int dg = idx / (C::BN / 4);
+        const int kg = idx - dg * (C::BN / 4);
+        ST* dst = sVt + (dg * C::VEC) * C::VSTR + 4 * kg;
 #pragma unroll
         for (int e = 0; e < C::VEC; ++e) {
           u32x4 pk = {v[i][0][e], v[i][1][e], v[i][2][e], v[i][3][e]};
@@ -140,7 +199,9 @@ struct WaveState {
   using C = AttnCfg<ST, HD, QB>;
   Frag<ST> qf[QB][C::NS];  // Q^T B-operand fragments of the wave's query blocks
   f32x4 acc[QB][C::NDB];   // O^T accumulators
-  float m[QB], l[QB];      // running max (log2 domain) and per-lane partial sum
+  float m[QB];             // running max (log2 domain)
+  f32x4 l[QB];             // running sum, in every element and every lane (an
+                           // all-ones V^T block through the PV MFMA)
   int tq[QB];              // query positions
   int nlo[QB];             // anchors visible to each query
 };
@@ -194,14 +255,17 @@ struct QueryIn {
   }
 };
 
-// One staged tile against one wave's 16*QB queries.
+// One staged tile against one wave's 16*QB queries.  VR: V tile row-major
+// (row stride VS), else transposed (keys contiguous, row stride VS).
 //  kind 0: anchors, key index = anchor index a, visible iff a < nlo(t)
 //  kind 1: band,    key index = position j,     visible iff t-W <= j <= t
-template <typename ST, int HD, int QB, int VS = AttnCfg<ST, HD, QB>::VSTR>
+template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
+          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR)>
 __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST* sK,
                                             const ST* sVt, int key0, int kind, bool need_mask,
                                             int W) {
   using C = AttnCfg<ST, HD, QB>;
+  static_assert(!VR || sizeof(ST) == 2, "transposing reads are 16-bit");
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
@@ -266,16 +330,10 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
 #pragma unroll
       for (int mb = 0; mb < C::NMB; ++mb) S[mb][nb] -= delta;
     }
-    float lsum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(S[mb][nb][i]);
-        S[mb][nb][i] = pv;
-        lsum += pv;
-      }
-    ws.l[nb] += lsum;
+      for (int i = 0; i < 4; ++i) S[mb][nb][i] = __builtin_amdgcn_exp2f(S[mb][nb][i]);
   }
 
 #pragma unroll
@@ -285,11 +343,23 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
     for (int nb = 0; nb < QB; ++nb) pb[nb] = frag_from(S[2 * kk][nb], S[2 * kk + 1][nb], (ST*)nullptr);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const ST* vrow = sVt + (16 * db + col) * VS + 32 * kk + 4 * g;
-      const Frag<ST> va = frag_ld4x2(vrow, vrow + 16);
+      Frag<ST> va;
+      if constexpr (VR) {
+        // keys 32kk + 4g + j (slots j < 4) and 32kk + 16 + 4g + j (slots
+        // j >= 4) of channel 16db + col, transposed out of the row-major tile
+        va = frag_ld_tr(sVt + (32 * kk + 4 * g + (col >> 2)) * VS + 16 * db + 4 * (col & 3), 16 * VS);
+      } else {
+        const ST* vrow = sVt + (16 * db + col) * VS + 32 * kk + 4 * g;
+        va = frag_ld4x2(vrow, vrow + 16);
+      }
 #pragma unroll
       for (int nb = 0; nb < QB; ++nb) mma16(ws.acc[nb][db], va, pb[nb]);
     }
+    // the row sums: an all-ones V^T block gives sum_k P[k][query] in every
+    // element (the same bf16-rounded weights as the numerator)
+    const Frag<ST> ones = frag_ones((ST*)nullptr);
+#pragma unroll
+    for (int nb = 0; nb < QB; ++nb) mma16(ws.l[nb], ones, pb[nb]);
   }
 }
 
@@ -384,7 +454,10 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
     RowMap<ST, HD> rows;
     int nv, k0;
     item_src(i, rows, nv, k0);
-    pf.load(rows, nv);
+    if constexpr (!RING && C::VROW)
+      pf.load_linear(rows.kh, rows.vh, nv);
+    else
+      pf.load(rows, nv);
   };
 
   Prefetch<ST, HD, QB> pf;
@@ -408,7 +481,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
     }
     d = xor16_32_sum(d);
     ws.m[nb] = d * p.scale_log2;
-    ws.l[nb] = (g == 0) ? 1.f : 0.f;
+    ws.l[nb] = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] = qin.v[nb][db].f32();
   }
@@ -442,7 +515,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   ST* op = reinterpret_cast<ST*>(p.o) + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
-    const float lt = xor16_32_sum(ws.l[nb]);
+    const float lt = ws.l[nb][0];
     const int t = ws.tq[nb] - a0;  // local row
     if (t < T) {
       const float inv = 1.f / lt;
@@ -467,7 +540,7 @@ __attribute__((amdgpu_waves_per_eu(QB == 1 ? 3 : 2, QB == 1 ? 3 : 2)))
 void attn_prefill_kernel(const AttnParams p) {
   using C = AttnCfg<ST, HD, QB>;
   __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::KSTR];
-  __shared__ __attribute__((aligned(16))) ST sVt[HD * C::VSTR];
+  __shared__ __attribute__((aligned(16))) ST sVt[C::VLDS];
 
   // block -> (head rank, batch row, pair): heads in cost order, so the
   // heaviest blocks are dispatched first; consecutive blocks land on
@@ -531,15 +604,15 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   }
   d = xor16_32_sum(d);
   ws.m[0] = d * p.scale_log2;
-  ws.l[0] = (g == 0) ? 1.f : 0.f;
+  ws.l[0] = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) ws.acc[0][db] = qin.v[0][db].f32();
   const int n_end = (a0 + min(tb + 15, T - 1)) / D;  // anchors any query of the block sees
   const int w_full = (a0 + tb) / D;                  // anchors every query of the block sees
   for (int key0 = 0; key0 < n_end; key0 += C::BN)
-    tile_update<ST, HD, 1, VS>(ws, sK + key0 * C::KSTR, sVt + key0, key0, 0, key0 + C::BN > w_full, 0);
+    tile_update<ST, HD, 1, false, VS>(ws, sK + key0 * C::KSTR, sVt + key0, key0, 0, key0 + C::BN > w_full, 0);
 
-  const float lt = xor16_32_sum(ws.l[0]);
+  const float lt = ws.l[0][0];
   const int t = ws.tq[0] - a0;  // local row
   const float inv = 1.f / lt;
   // buffer stores: lanes of rows past T (and the lse of lanes g > 0, or a
