@@ -43,6 +43,16 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
+// c0 + a*b into a fresh accumulator (c0 is left as it is)
+__device__ __forceinline__ f32x4 mma16_from(const f32x4& c0, const Frag<bf16>& a, const Frag<bf16>& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16_from(const f32x4& c0, const Frag<float>& a, const Frag<float>& b) {
+  f32x4 c = c0;
+  mma16(c, a, b);
+  return c;
+}
+
 __device__ __forceinline__ Frag<bf16> frag_ones(bf16*) {
   Frag<bf16> f;
   f.v = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
@@ -255,92 +265,133 @@ struct QueryIn {
   }
 };
 
-// One staged tile against one wave's 16*QB queries.  VR: V tile row-major
-// (row stride VS), else transposed (keys contiguous, row stride VS).
+// One staged tile against one wave's 16*QB queries, in three phases:
+// scores (MFMA), softmax (VALU), PV (MFMA).  VR: V tile row-major (row
+// stride VS), else transposed (keys contiguous, row stride VS).
 //  kind 0: anchors, key index = anchor index a, visible iff a < nlo(t)
 //  kind 1: band,    key index = position j,     visible iff t-W <= j <= t
-template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
-          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR)>
-__device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST* sK,
-                                            const ST* sVt, int key0, int kind, bool need_mask,
-                                            int W) {
+template <typename ST, int HD, int QB>
+struct TileRegs {
   using C = AttnCfg<ST, HD, QB>;
-  static_assert(!VR || sizeof(ST) == 2, "transposing reads are 16-bit");
+  f32x4 S[C::NMB][QB];     // scores S^T, then exp2 arguments
+  Frag<ST> P[C::NKK][QB];  // P^T as the B operand of the PV product
+};
+
+// S = c*K Q^T - m.  With Q pre-scaled by c = scale*log2(e) the MFMA result
+// is directly the exp2 argument of the running softmax (the first slab's
+// MFMAs read one {-m} tuple per query block as their C operand).
+template <typename ST, int HD, int QB>
+__device__ __forceinline__ void tile_scores(const WaveState<ST, HD, QB>& ws, const ST* sK,
+                                            TileRegs<ST, HD, QB>& tr) {
+  using C = AttnCfg<ST, HD, QB>;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
-
-  // accumulators start at -m: with Q pre-scaled by scale*log2(e) the MFMA
-  // result is c*s - m, the exp2 argument of the running softmax
-  f32x4 S[C::NMB][QB];
+  f32x4 minit[QB];
 #pragma unroll
-  for (int mb = 0; mb < C::NMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < QB; ++nb) {
-      const float mneg = -ws.m[nb];
-      S[mb][nb] = f32x4{mneg, mneg, mneg, mneg};
-    }
-
+  for (int nb = 0; nb < QB; ++nb) {
+    const float mneg = -ws.m[nb];
+    minit[nb] = f32x4{mneg, mneg, mneg, mneg};
+  }
 #pragma unroll
   for (int s = 0; s < C::NS; ++s) {
 #pragma unroll
     for (int mb = 0; mb < C::NMB; ++mb) {
       const Frag<ST> a = frag_ld8(sK + (16 * mb + col) * C::KSTR + 32 * s + 8 * g);
 #pragma unroll
-      for (int nb = 0; nb < QB; ++nb) mma16(S[mb][nb], a, ws.qf[nb][s]);
+      for (int nb = 0; nb < QB; ++nb) {
+        if (s == 0)
+          tr.S[mb][nb] = mma16_from(minit[nb], a, ws.qf[nb][s]);
+        else
+          mma16(tr.S[mb][nb], a, ws.qf[nb][s]);
+      }
     }
   }
+}
 
-  // Online softmax in the log2 domain.  The running max m is raised only
-  // when a tile's max exceeds it by more than kRescaleSlack: every weight is
-  // then exp2(c*s - m) <= 2^kRescaleSlack (no overflow in fp32 or bf16), the
-  // result is the same softmax, and the accumulators are rescaled on few
-  // tiles (wave-uniform skip otherwise).
+// Online softmax in the log2 domain.  The running max m is raised only when
+// a tile's max exceeds it by more than kRescaleSlack: every weight is then
+// exp2(c*s - m) <= 2^kRescaleSlack (no overflow in fp32 or bf16), the result
+// is the same softmax, and the accumulators are rescaled on few tiles
+// (wave-uniform skip otherwise).  One basic block per phase for all query
+// blocks (masks, maxima, the rare rescale, the exponentials), so the
+// exponentials of one block can be scheduled among MFMAs.
+template <typename ST, int HD, int QB>
+__device__ __forceinline__ void tile_softmax(WaveState<ST, HD, QB>& ws, TileRegs<ST, HD, QB>& tr,
+                                             int key0, int kind, bool need_mask, int W) {
+  using C = AttnCfg<ST, HD, QB>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  if (need_mask) {
 #pragma unroll
-  for (int nb = 0; nb < QB; ++nb) {
-    // visible keys of this lane's query: lo <= key <= hi
-    //   anchors: a < nlo(t);  band: t - W <= j <= t - 1 (own position folded)
-    const int lo = kind == 0 ? 0 : ws.tq[nb] - W;
-    const int hi = kind == 0 ? ws.nlo[nb] - 1 : ws.tq[nb] - 1;
-    const int base = key0 + 4 * g - lo;
-    const uint32_t span = (uint32_t)(hi - lo);
-    float tmax = -INFINITY;
-    if (need_mask) {
+    for (int nb = 0; nb < QB; ++nb) {
+      // visible keys of this lane's query: lo <= key <= hi
+      //   anchors: a < nlo(t);  band: t - W <= j <= t - 1 (own position folded)
+      const int lo = kind == 0 ? 0 : ws.tq[nb] - W;
+      const int hi = kind == 0 ? ws.nlo[nb] - 1 : ws.tq[nb] - 1;
+      const int base = key0 + 4 * g - lo;
+      const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
       for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool vis = (uint32_t)(base + 16 * mb + i) <= span && hi >= lo;
-          S[mb][nb][i] = vis ? S[mb][nb][i] : -INFINITY;
+          tr.S[mb][nb][i] = vis ? tr.S[mb][nb][i] : -INFINITY;
         }
     }
+  }
+  float tmax[QB];
+  bool grow_any = false;
+#pragma unroll
+  for (int nb = 0; nb < QB; ++nb) {
+    float t = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, S[mb][nb][i]);
-    tmax = xor16_32_max(tmax);
-    const bool grow = tmax > kRescaleSlack;
-    if (__any(grow)) {
-      const float delta = grow ? tmax : 0.f;
+      for (int i = 0; i < 4; ++i) t = fmaxf(t, tr.S[mb][nb][i]);
+    tmax[nb] = xor16_32_max(t);
+    grow_any = grow_any || tmax[nb] > kRescaleSlack;
+  }
+  if (__any(grow_any)) {
+#pragma unroll
+    for (int nb = 0; nb < QB; ++nb) {
+      const float delta = tmax[nb] > kRescaleSlack ? tmax[nb] : 0.f;
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       ws.m[nb] += delta;
       ws.l[nb] *= alpha;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < C::NMB; ++mb) S[mb][nb] -= delta;
+      for (int mb = 0; mb < C::NMB; ++mb) tr.S[mb][nb] -= delta;
     }
-#pragma unroll
-    for (int mb = 0; mb < C::NMB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[mb][nb][i] = __builtin_amdgcn_exp2f(S[mb][nb][i]);
   }
+#pragma unroll
+  for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < QB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tr.S[mb][nb][i] = __builtin_amdgcn_exp2f(tr.S[mb][nb][i]);
+#pragma unroll
+  for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+    for (int nb = 0; nb < QB; ++nb)
+      tr.P[kk][nb] = frag_from(tr.S[2 * kk][nb], tr.S[2 * kk + 1][nb], (ST*)nullptr);
+}
 
+// O^T += V^T P^T, and the row sums through one all-ones V^T block (sum_k
+// P[k][query] in every element: the same bf16-rounded weights as the
+// numerator).
+template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
+          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR)>
+__device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileRegs<ST, HD, QB>& tr,
+                                        const ST* sVt) {
+  using C = AttnCfg<ST, HD, QB>;
+  static_assert(!VR || sizeof(ST) == 2, "transposing reads are 16-bit");
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) {
-    Frag<ST> pb[QB];
-#pragma unroll
-    for (int nb = 0; nb < QB; ++nb) pb[nb] = frag_from(S[2 * kk][nb], S[2 * kk + 1][nb], (ST*)nullptr);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
       Frag<ST> va;
@@ -353,14 +404,23 @@ __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST*
         va = frag_ld4x2(vrow, vrow + 16);
       }
 #pragma unroll
-      for (int nb = 0; nb < QB; ++nb) mma16(ws.acc[nb][db], va, pb[nb]);
+      for (int nb = 0; nb < QB; ++nb) mma16(ws.acc[nb][db], va, tr.P[kk][nb]);
     }
-    // the row sums: an all-ones V^T block gives sum_k P[k][query] in every
-    // element (the same bf16-rounded weights as the numerator)
     const Frag<ST> ones = frag_ones((ST*)nullptr);
 #pragma unroll
-    for (int nb = 0; nb < QB; ++nb) mma16(ws.l[nb], ones, pb[nb]);
+    for (int nb = 0; nb < QB; ++nb) mma16(ws.l[nb], ones, tr.P[kk][nb]);
   }
+}
+
+template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
+          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR)>
+__device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST* sK,
+                                            const ST* sVt, int key0, int kind, bool need_mask,
+                                            int W) {
+  TileRegs<ST, HD, QB> tr;
+  tile_scores<ST, HD, QB>(ws, sK, tr);
+  tile_softmax<ST, HD, QB>(ws, tr, key0, kind, need_mask, W);
+  tile_pv<ST, HD, QB, VR, VS>(ws, tr, sVt);
 }
 
 // Key rows of one staged tile.  Anchor tiles, and band tiles at positions

@@ -48,6 +48,12 @@ SMALL = [
     ("T2-D-beyond-T", 1, 2, 2, 64, [7, 2], [0, 0], "f32", 1.0, 2.0, 0),
     ("T129", 1, 1, 129, 128, [1], [0], "bf16", 128 ** -0.5, 3.0, 0),
     ("T127-window", 1, 1, 127, 128, [3], [64], "bf16", 128 ** -0.5, 3.0, 0),
+    # average key set of 512 or more: the MFMA-bound launch (two 16-query
+    # blocks per wave), with ragged query tiles, band tiles and both dtypes
+    ("qb2-dense-hybrid", 1, 2, 1500, 128, [1, 2], [0, 100], "bf16", 128 ** -0.5, 3.0, 3),
+    ("qb2-hd64", 1, 1, 1100, 64, [1], [0], "bf16", 64 ** -0.5, 3.0, 0),
+    ("qb2-window-band", 1, 2, 1300, 128, [1, 1], [300, 0], "bf16", 128 ** -0.5, 3.0, 0),
+    ("qb2-f32", 1, 1, 1030, 64, [1], [0], "f32", 1.0, 2.0, 0),
 ]
 
 
