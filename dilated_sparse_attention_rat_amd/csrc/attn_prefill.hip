@@ -103,7 +103,8 @@ struct AttnCfg {
   // contiguous)
   static constexpr bool VROW = sizeof(ST) == 2;
   static constexpr int KITEMS = BN * CPR;          // K chunks per tile
-  static constexpr int VITEMS = VROW ? KITEMS : (BN / 4) * CPR;  // V chunks / 4-row items
+  static constexpr int VTITEMS = (BN / 4) * CPR;  // transposed staging: 4 rows x VEC items
+  static constexpr int VITEMS = VROW ? KITEMS : VTITEMS;  // V items of the streamed tile
   static constexpr int KPT = (KITEMS + 255) / 256;  // per thread
   static constexpr int VPT = (VITEMS + 255) / 256;
   static constexpr int VROWS = VROW ? 1 : 4;       // rows per V item
@@ -732,7 +733,8 @@ void attn_resident_kernel(const AttnParams p) {
         }
       }
       // V transposed: work item = 4 anchors x VEC channels
-      for (int idx = tid; idx < C::VITEMS; idx += NT) {
+      static_assert((C::VTITEMS / (C::BN / 4)) * C::VEC == HD, "items cover hd channels");
+      for (int idx = tid; idx < C::VTITEMS; idx += NT) {
         const int dg = idx / (C::BN / 4);
         const int kg = idx - dg * (C::BN / 4);
         u32x4 v[4];
