@@ -62,22 +62,6 @@ __device__ __forceinline__ Frag<float> frag_ones(float*) {
   return Frag<float>{f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
 }
 
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// lane i receives element i % 4 of the 8-byte pieces addressed by lanes
-// 4j + i / 4 of its group, j = 0..3 (the gfx950 lane layout, checked on the
-// device).  With lanes 4j..4j+3 addressing row j of a 4-row x 16-column
-// block (4 columns each), lane i gets column i of the 4 rows: two reads,
-// the second `step` elements further on, fill the 8 slots of an MFMA
-// fragment.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-__device__ __forceinline__ Frag<bf16> frag_ld_tr(const bf16* p, int step) {
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + step));
-  Frag<bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-  return f;
-}
 
 template <typename ST, int HD, int QB>
 struct AttnCfg {

@@ -69,7 +69,27 @@ struct BwdCfg {
   static constexpr int TSTR = BN + 4;
   static constexpr int G4 = (BN / 4) * CPR;       // items of 4 rows x VEC channels
   static constexpr int G4PT = (G4 + 255) / 256;   // per thread
+  // bf16 reads the transposed operands straight out of the row-major tile
+  // (ds_read_b64_tr_b16); fp32 stages a transposed copy
+  static constexpr bool TR = sizeof(ST) == 2;
+  static constexpr int TLDS = TR ? 8 : HD * TSTR;  // transposed copy (elements)
 };
+
+// A operand whose K dimension runs over a staged tile's rows: channels
+// 16db + col, rows 32kk + 4g + j (slots j < 4) and 32kk + 16 + 4g + j (slots
+// j >= 4), from the row-major tile (bf16) or its transposed copy (fp32).
+template <typename ST, int HD>
+__device__ __forceinline__ Frag<ST> frag_rows(const ST* sRow, const ST* sT, int kk, int db,
+                                              int col, int g) {
+  using C = BwdCfg<ST, HD>;
+  if constexpr (C::TR) {
+    return frag_ld_tr(sRow + (32 * kk + 4 * g + (col >> 2)) * C::RSTR + 16 * db + 4 * (col & 3),
+                      16 * C::RSTR);
+  } else {
+    const ST* r = sT + (16 * db + col) * C::TSTR + 32 * kk + 4 * g;
+    return frag_ld4x2(r, r + 16);
+  }
+}
 
 // A tile of BN rows staged through registers into LDS: items of 4
 // consecutive rows x VEC channels, stored row-major and, with TRANS, also
@@ -134,15 +154,16 @@ struct Stage4 {
 // ---------------------------------------------------------------------------
 // Workgroup: 4 waves x 16 queries of one (b, h), query tile qt (heaviest
 // first).  Key tiles as in the forward: anchors [0, n_end) then the window
-// positions [jb0, last query].  K is staged row-major (scores) and
-// transposed (dq), V row-major (dP).
+// positions [jb0, last query].  K and V are staged row-major; the dq product
+// reads K's transposed fragments from the same tile (bf16: transposing LDS
+// reads; fp32: a transposed copy).
 template <typename ST, int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const BwdParams p) {
   using C = BwdCfg<ST, HD>;
   __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::RSTR];
   __shared__ __attribute__((aligned(16))) ST sV[C::BN * C::RSTR];
-  __shared__ __attribute__((aligned(16))) ST sKt[HD * C::TSTR];
+  __shared__ __attribute__((aligned(16))) ST sKt[C::TLDS];
 
   const int nq = (p.T + C::BN - 1) / C::BN;
   int bhi, xi;
@@ -225,7 +246,7 @@ void bwd_dq_kernel(const BwdParams p) {
       nvalid = tlast + 1 - key0;
     }
   };
-  Stage4<ST, HD, true> pk;
+  Stage4<ST, HD, !C::TR> pk;
   Stage4<ST, HD, false> pv;
   auto load = [&](int i) {
     int key0, nv;
@@ -288,10 +309,8 @@ void bwd_dq_kernel(const BwdParams p) {
     for (int kk = 0; kk < C::NKK; ++kk) {
       const Frag<ST> bfr = frag_from(dS[2 * kk], dS[2 * kk + 1], (ST*)nullptr);
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const ST* kr = sKt + (16 * db + col) * C::TSTR + 32 * kk + 4 * g;
-        mma16(acc[db], frag_ld4x2(kr, kr + 16), bfr);
-      }
+      for (int db = 0; db < C::NDB; ++db)
+        mma16(acc[db], frag_rows<ST, HD>(sK, sKt, kk, db, col, g), bfr);
     }
   }
 
@@ -309,15 +328,16 @@ void bwd_dq_kernel(const BwdParams p) {
 // are the B operand, held in registers).  Tile x < na_t: anchors
 // [64x, 64x+64), seen by queries t >= (a+1)D + W; next nb_t tiles: window
 // positions [64y, 64y+64), seen by queries j+1 .. j+W.  Per query tile of 64:
-// Q and dO staged row-major and transposed, lse and delta beside them.
+// Q and dO staged row-major (their transposed fragments read from the same
+// tiles, as in the dq kernel), lse and delta beside them.
 template <typename ST, int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkv_kernel(const BwdParams p) {
   using C = BwdCfg<ST, HD>;
   __shared__ __attribute__((aligned(16))) ST sQ[C::BN * C::RSTR];
   __shared__ __attribute__((aligned(16))) ST sO[C::BN * C::RSTR];
-  __shared__ __attribute__((aligned(16))) ST sQt[HD * C::TSTR];
-  __shared__ __attribute__((aligned(16))) ST sOt[HD * C::TSTR];
+  __shared__ __attribute__((aligned(16))) ST sQt[C::TLDS];
+  __shared__ __attribute__((aligned(16))) ST sOt[C::TLDS];
   __shared__ __attribute__((aligned(16))) float sL[C::BN];
   __shared__ __attribute__((aligned(16))) float sDl[C::BN];
 
@@ -387,7 +407,7 @@ void bwd_dkv_kernel(const BwdParams p) {
     qt0 = a0;
   }
 
-  Stage4<ST, HD, true> pq, po;
+  Stage4<ST, HD, !C::TR> pq, po;
   float lpre = 0.f, dpre = 0.f;
   auto load = [&](int qt) {
     const int tq0 = qt * C::BN;
@@ -449,10 +469,8 @@ void bwd_dkv_kernel(const BwdParams p) {
       const Frag<ST> bs = frag_from(dS[2 * kk], dS[2 * kk + 1], (ST*)nullptr);
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const ST* orow = sOt + (16 * db + col) * C::TSTR + 32 * kk + 4 * g;
-        const ST* qrow = sQt + (16 * db + col) * C::TSTR + 32 * kk + 4 * g;
-        mma16(dv[db], frag_ld4x2(orow, orow + 16), bp);
-        mma16(dk[db], frag_ld4x2(qrow, qrow + 16), bs);
+        mma16(dv[db], frag_rows<ST, HD>(sO, sOt, kk, db, col, g), bp);
+        mma16(dk[db], frag_rows<ST, HD>(sQ, sQt, kk, db, col, g), bs);
       }
     }
   }
