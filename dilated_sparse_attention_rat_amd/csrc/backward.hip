@@ -642,11 +642,14 @@ __global__ __launch_bounds__(256) void bwd_rscan_apply_kernel(const BwdParams p)
     lk[j] = cr[j];
     lv[j] = cr[HD + j];
   }
+  // g of the position after t: loaded once before the loop, then the
+  // previous iteration's g_t (each g row is read once per chunk)
+  float gn[VEC];
+  unpack16(ld_raw16(gp + (int64_t)min(e + 1, T - 1) * HD), gn, (ST*)nullptr);
   for (int t = e; t >= s; --t) {
     const int64_t r = (int64_t)t * HD;
     const int64_t rp = (int64_t)max(t - 1, 0) * HD;
-    float gn[VEC], gt[VEC], kv[VEC], vv[VEC], pk[VEC], pv[VEC];
-    unpack16(ld_raw16(gp + (int64_t)min(t + 1, T - 1) * HD), gn, (ST*)nullptr);
+    float gt[VEC], kv[VEC], vv[VEC], pk[VEC], pv[VEC];
     unpack16(ld_raw16(gp + r), gt, (ST*)nullptr);
     unpack16(ld_raw16(kp + r), kv, (ST*)nullptr);
     unpack16(ld_raw16(vp + r), vv, (ST*)nullptr);
@@ -669,6 +672,8 @@ __global__ __launch_bounds__(256) void bwd_rscan_apply_kernel(const BwdParams p)
     st_raw16(dkp + r, pack16(ok, (ST*)nullptr));
     st_raw16(dvp + r, pack16(ov, (ST*)nullptr));
     st_raw16(dgp + r, pack16(og, (ST*)nullptr));
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) gn[j] = gt[j];
   }
 }
 
