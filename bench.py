@@ -45,6 +45,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+SPIN_CYCLES = 2_000_000         # device-side spin ahead of an event-timed region
 
 
 def head_list(v):
@@ -418,6 +419,7 @@ def bench_decode_workload(rat, synth, torch, np):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda._sleep(SPIN_CYCLES)  # the first step queued before its event
     evs[0].record(stream)
     for s in range(steps):
         x = inputs[s]
@@ -494,8 +496,14 @@ def bench_chunked(rat, synth, torch, np, reps=5, nchunks=4):
     tot_chunked, tot_whole = [], []
     for _ in range(reps):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nchunks)]
+        # a short device-side spin first, so that every launch of the region
+        # is queued before its first event (an idle GPU would otherwise time
+        # the host's launch latency into the first chunk)
+        torch.cuda._sleep(SPIN_CYCLES)
         chunked(ev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
         e0.record(stream)
         whole()
         e1.record(stream)

@@ -13,8 +13,9 @@
 //    per wave (1 for streaming-bound calls: fewer registers, more waves in
 //    flight; 2 for MFMA-bound calls: twice the reuse of every LDS operand);
 //    a workgroup takes a pair of query tiles (i, nq-1-i) so all workgroups of
-//    a head cost about the same; heads are ordered by per-workgroup cost
-//    (heaviest first) so a head-wise hybrid launch is longest-job-first;
+//    a head cost about the same (single tiles, heaviest first, when pairs
+//    would leave too few workgroups); heads are ordered by per-workgroup
+//    cost (heaviest first) so a head-wise hybrid launch is longest-job-first;
 //  * K/V tiles of 64 keys are staged in LDS once per workgroup, both
 //    row-major for bf16: K fragments are plain ds_read_b128 and the V^T
 //    fragments of the PV product come out of ds_read_b64_tr_b16, the gfx950
@@ -599,7 +600,7 @@ void attn_prefill_kernel(const AttnParams p) {
   const int h = p.perm[rank];
 
   const int qa = p.nq - 1 - pr;  // heavy tile first, then its partner
-  const int ntiles = pr < qa ? 2 : 1;
+  const int ntiles = p.paired && pr < qa ? 2 : 1;
   const int64_t bh = (int64_t)b * p.H + h;
   const int64_t off = bh * p.T * HD;
   const ST* qp = reinterpret_cast<const ST*>(p.q) + (bh / p.H) * p.q_sb + (bh % p.H) * p.q_sh;

@@ -313,6 +313,21 @@ int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
   const int bm = 64 * p.qb;
   p.nq = (int)((T + bm - 1) / bm);
   p.np = (p.nq + 1) / 2;
+  p.paired = 1;
+  if (!resident) {
+    // Pairs (i, nq-1-i) even out the causal staircase; when pairing would
+    // leave fewer than two rounds of resident workgroups (a short chunk),
+    // single tiles give twice the parallelism instead.
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return RAT_ERR_HIP;
+    const int64_t slots = (int64_t)cus * (p.qb == 1 ? 3 : 2);  // resident workgroups
+    if ((int64_t)B * H * p.np < 2 * slots) {
+      p.np = p.nq;
+      p.paired = 0;
+    }
+  }
   if ((int64_t)H * B * p.np > INT32_MAX) return RAT_ERR_UNSUPPORTED;
   p.scale_log2 = sc * 1.4426950408889634f;
   p.q = q;

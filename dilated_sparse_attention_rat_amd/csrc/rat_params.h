@@ -71,7 +71,8 @@ struct AttnParams {
   int nra;           // mode 1: workgroups per (b, h)
   int qb;            // 16-query blocks per wave (1 or 2): tile = 64*qb queries
   int nq;            // query tiles per (b, h)
-  int np;            // pair-blocks per (b, h)
+  int np;            // workgroups per (b, h): pairs of query tiles, or single tiles
+  int paired;        // 1: workgroup pr takes tiles nq-1-pr and pr; 0: tile nq-1-pr only
   float scale_log2;  // scale * log2(e)
   int64_t R;
   const void* q;
