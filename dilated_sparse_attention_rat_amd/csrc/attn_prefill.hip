@@ -159,7 +159,7 @@ struct Prefetch {
   }
 
   // K row-major; V row-major (bf16) or transposed (fp32, keys contiguous)
-  __device__ __forceinline__ void store(ST* sK, ST* sVt) const {
+  __device__ __forceinline__ void store(ST* sK, ST* sV) const {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
@@ -175,11 +175,11 @@ struct Prefetch {
       if constexpr (C::VROW) {
         const int row = idx / C::CPR;
         const int c16 = idx - row * C::CPR;
-        st_raw16(sVt + row * C::VRSTR + c16 * C::VEC, v[i][0]);
+        st_raw16(sV + row * C::VRSTR + c16 * C::VEC, v[i][0]);
       } else {
         const int dg = idx / (C::BN / 4);
         const int kg = idx - dg * (C::BN / 4);
-        ST* dst = sVt + (dg * C::VEC) * C::VSTR + 4 * kg;
+        ST* dst = sV + (dg * C::VEC) * C::VSTR + 4 * kg;
 #pragma unroll
         for (int e = 0; e < C::VEC; ++e) {
           u32x4 pk = {v[i][0][e], v[i][1][e], v[i][2][e], v[i][3][e]};
@@ -370,7 +370,7 @@ __device__ __forceinline__ void tile_softmax(WaveState<ST, HD, QB>& ws, TileRegs
 template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
           int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR)>
 __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileRegs<ST, HD, QB>& tr,
-                                        const ST* sVt) {
+                                        const ST* sV) {
   using C = AttnCfg<ST, HD, QB>;
   static_assert(!VR || sizeof(ST) == 2, "transposing reads are 16-bit");
   const int lane = threadIdx.x & 63;
@@ -384,9 +384,9 @@ __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileReg
       if constexpr (VR) {
         // keys 32kk + 4g + j (slots j < 4) and 32kk + 16 + 4g + j (slots
         // j >= 4) of channel 16db + col, transposed out of the row-major tile
-        va = frag_ld_tr(sVt + (32 * kk + 4 * g + (col >> 2)) * VS + 16 * db + 4 * (col & 3), 16 * VS);
+        va = frag_ld_tr(sV + (32 * kk + 4 * g + (col >> 2)) * VS + 16 * db + 4 * (col & 3), 16 * VS);
       } else {
-        const ST* vrow = sVt + (16 * db + col) * VS + 32 * kk + 4 * g;
+        const ST* vrow = sV + (16 * db + col) * VS + 32 * kk + 4 * g;
         va = frag_ld4x2(vrow, vrow + 16);
       }
 #pragma unroll
@@ -401,12 +401,12 @@ __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileReg
 template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
           int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR)>
 __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST* sK,
-                                            const ST* sVt, int key0, int kind, bool need_mask,
+                                            const ST* sV, int key0, int kind, bool need_mask,
                                             int W) {
   TileRegs<ST, HD, QB> tr;
   tile_scores<ST, HD, QB>(ws, sK, tr);
   tile_softmax<ST, HD, QB>(ws, tr, key0, kind, need_mask, W);
-  tile_pv<ST, HD, QB, VR, VS>(ws, tr, sVt);
+  tile_pv<ST, HD, QB, VR, VS>(ws, tr, sV);
 }
 
 // Key rows of one staged tile.  Anchor tiles, and band tiles at positions
@@ -437,7 +437,7 @@ struct RowMap {
 // o and lse are local to this call.
 template <typename ST, int HD, int QB, bool RING>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, int lt0, ST* sK,
-                                             ST* sVt, const QueryIn<ST, HD, QB>& qin) {
+                                             ST* sV, const QueryIn<ST, HD, QB>& qin) {
   using C = AttnCfg<ST, HD, QB>;
   constexpr int QW = 16 * QB;  // queries per wave
   const int tid = threadIdx.x;
@@ -537,7 +537,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   const int wj0 = max(0, aw0 - W);
   for (int i = 0; i < n_items; ++i) {
     __syncthreads();  // every wave is done reading the previous tile
-    pf.store(sK, sVt);
+    pf.store(sK, sV);
     __syncthreads();
     if (i + 1 < n_items) load_item(pf, i + 1);  // overlaps this tile's MFMAs
     RowMap<ST, HD> rows;
@@ -554,7 +554,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
       // aw0+QW-1 - W <= key0 and key0 + BN - 1 <= aw0 - 1 (and no clamped rows)
       need_mask = !((aw0 + QW - 1 - W <= key0) && (key0 + C::BN <= aw0) && (tw0 + QW - 1 < T));
     }
-    if (part) tile_update<ST, HD, QB>(ws, sK, sVt, key0, kind, need_mask, W);
+    if (part) tile_update<ST, HD, QB>(ws, sK, sV, key0, kind, need_mask, W);
   }
 
   // ---- normalise and store --------------------------------------------------
@@ -586,7 +586,7 @@ __attribute__((amdgpu_waves_per_eu(QB == 1 ? 3 : 2, QB == 1 ? 3 : 2)))
 void attn_prefill_kernel(const AttnParams p) {
   using C = AttnCfg<ST, HD, QB>;
   __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::KSTR];
-  __shared__ __attribute__((aligned(16))) ST sVt[C::VLDS];
+  __shared__ __attribute__((aligned(16))) ST sV[C::VLDS];
 
   // block -> (head rank, batch row, pair): heads in cost order, so the
   // heaviest blocks are dispatched first; consecutive blocks land on
@@ -609,10 +609,10 @@ void attn_prefill_kernel(const AttnParams p) {
   const int wave = threadIdx.x >> 6;
   QueryIn<ST, HD, QB> qin;
   qin.load(qp, hkp, hvp, qa * C::BM + 16 * QB * wave, p.T, p.q_st);
-  process_tile<ST, HD, QB, RING>(p, b, h, qa * C::BM, sK, sVt, qin);
+  process_tile<ST, HD, QB, RING>(p, b, h, qa * C::BM, sK, sV, qin);
   if (ntiles == 2) {
     qin.load(qp, hkp, hvp, pr * C::BM + 16 * QB * wave, p.T, p.q_st);
-    process_tile<ST, HD, QB, RING>(p, b, h, pr * C::BM, sK, sVt, qin);
+    process_tile<ST, HD, QB, RING>(p, b, h, pr * C::BM, sK, sV, qin);
   }
 }
 
