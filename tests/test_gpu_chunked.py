@@ -139,6 +139,10 @@ CASES = [
     ("bf16-resident-anchors", 1, 2, [700, 1300], 128, [16, 64], [0, 0], "bf16", 0, True),
     ("bf16-empty-middle-chunk", 1, 2, [50, 0, 30], 64, [4, 1], [6, 2], "bf16", 0, False),
     ("bf16-unaligned-boundaries", 2, 2, [129, 255, 63], 128, [5, 2], [0, 130], "bf16", 9, True),
+    # continuation chunks whose average key set is 512 or more: the launch with
+    # two query blocks per wave reading the previous call's ring
+    ("qb2-ring-bf16", 1, 2, [700, 600], 128, [1, 1], [300, 0], "bf16", 0, True),
+    ("qb2-ring-f32", 1, 2, [600, 500], 64, [1, 2], [200, 0], "f32", 4, False),
 ]
 
 
