@@ -86,3 +86,43 @@ def test_layer_matches_oracle(case):
         chk(check_rel, "state_k", to_np(cache["state_k"]), ref["state_k"], dtype)
         chk(check_rel, "state_v", to_np(cache["state_v"]), ref["state_v"], dtype)
         chk.done()
+
+
+def test_layer_workload_size_sampled():
+    """The layer at the size the benchmark times (1.5B-like prefill, d_model =
+    H*hd = 2048): the GPU runs all four batch rows, the oracle checks batch
+    rows 0 and B-1 in full (output, lse, final states)."""
+    import dilated_sparse_attention_rat_amd as rat
+    from dilated_sparse_attention_rat_amd import synth
+    w = synth.WORKLOADS[1]
+    B, H, T, hd = w.B, w.H, w.T, w.hd
+    dm = HD = H * hd
+    say(f"[layer] workload 1 size: B={B} H={H} T={T} hd={hd} dm={dm}")
+    rng = np.random.default_rng(1234)
+
+    def r(shape, std):
+        return oracle.round_bf16((rng.standard_normal(shape) * std).astype(np.float32)).astype(np.float32)
+
+    x = r((B, T, dm), 1.0)
+    wq, wk, wv = (r((dm, HD), w.qkv_std / np.sqrt(dm)) for _ in range(3))
+    wg = r((dm, HD), 1.0 / np.sqrt(dm))
+    bg = np.full(HD, float(w.g_bias), np.float32)
+    wo = r((HD, dm), 1.0 / np.sqrt(HD))
+    D, W = np.array(w.D, np.int32), np.array(w.W, np.int32)
+    dev = lambda a: to_dev(a, "bf16")
+    cache = rat.alloc_cache(B, H, hd, T, D, W, torch.bfloat16, "cuda")
+    out = torch.empty((B, T, dm), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    ws = rat.layer_workspace(rat.binding._dtype_code(out), B, H, T, hd, "cuda")
+    rat.rat_layer_prefill(dev(x), dev(wq), dev(wk), dev(wv), dev(wg), torch.from_numpy(bg).cuda(),
+                          dev(wo), out, D, W, H, hd, T, cache, ws, lse=lse)
+    torch.cuda.synchronize()
+    chk = Checks()
+    for b in (0, B - 1):
+        say(f" batch row {b}")
+        ref = oracle.layer_prefill(x[b:b + 1], wq, wk, wv, wg, bg, wo, H, hd, D, W, hd ** -0.5, True)
+        chk(check_rel, "out", to_np(out[b:b + 1]), ref["out"], "bf16")
+        chk(check_rel, "lse", to_np(lse[b:b + 1]), ref["lse"], "bf16")
+        chk(check_rel, "state_k", to_np(cache["state_k"][b:b + 1]), ref["state_k"], "bf16")
+        chk(check_rel, "state_v", to_np(cache["state_v"][b:b + 1]), ref["state_v"], "bf16")
+    chk.done()
