@@ -16,6 +16,8 @@ from .binding import (RAT_DTYPE_BF16, RAT_DTYPE_F32, RAT_ERR_CAPACITY,  # noqa: 
                       rat_dilated_attn_prefill_continue, rat_ring_rows,
                       rat_scan_prefill, rat_scan_prefill_continue,
                       rat_scan_workspace_bytes,
-                      rat_status_string, rat_version, scan_workspace)
+                      rat_status_string, rat_version, scan_workspace,
+                      TOPK_BLOCK, TOPK_MAX_K, alloc_topk_history,
+                      rat_decode_step_topk, rat_topk_cache_build)
 
 __version__ = "0.1.0"

@@ -35,7 +35,11 @@ EXPORTED = [
     "rat_decode_workspace_bytes", "rat_decode_step",
     "rat_prefill_backward_workspace_bytes", "rat_prefill_backward",
     "rat_layer_workspace_bytes", "rat_layer_prefill",
+    "rat_topk_cache_build", "rat_decode_step_topk",
 ]
+
+TOPK_BLOCK = 64   # RAT_TOPK_BLOCK
+TOPK_MAX_K = 64   # RAT_TOPK_MAX_K
 
 
 class RatError(RuntimeError):
@@ -94,6 +98,10 @@ def lib() -> ctypes.CDLL:
                                       P, P, P, P, P, P, P, P, P, P, P, i32, P,
                                       sz, P]
         L.rat_decode_step.restype = i32
+        L.rat_topk_cache_build.argtypes = [i32, i32, i32, i64, i32, i64, P, P, P, P, P, P]
+        L.rat_topk_cache_build.restype = i32
+        L.rat_decode_step_topk.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64, i32] + [P] * 16
+        L.rat_decode_step_topk.restype = i32
         _lib = L
     return _lib
 
@@ -352,6 +360,70 @@ def rat_decode_step(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, o,
         _stream(stream, dev),
     ]
     _check("rat_decode_step", lib().rat_decode_step(*args))
+
+
+def rat_topk_cache_build(hk, hv, hk_hist, hv_hist, block_means, stream=None):
+    """History cache of a prefill for top-k decode: rows of hk, hv [B,H,T,hd]
+    into hk_hist, hv_hist [B,H,T_cap,hd], block means [B,H,T_cap//64,hd] fp32."""
+    torch = _torch()
+    B, H, T, hd = hk.shape
+    st = hk.dtype
+    dev = hk.device
+    T_cap = hk_hist.shape[2]
+    NB = T_cap // TOPK_BLOCK
+    args = [
+        _dtype_code(hk), B, H, T, hd, T_cap,
+        _dev(hk, "hk", (B, H, T, hd), st, dev), _dev(hv, "hv", (B, H, T, hd), st, dev),
+        _dev(hk_hist, "hk_hist", (B, H, T_cap, hd), st, dev),
+        _dev(hv_hist, "hv_hist", (B, H, T_cap, hd), st, dev),
+        _opt(block_means, "block_means", (B, H, NB, hd), torch.float32, dev),
+        _stream(stream, dev),
+    ]
+    _check("rat_topk_cache_build", lib().rat_topk_cache_build(*args))
+
+
+def rat_decode_step_topk(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, hk_hist, hv_hist,
+                         block_means, o, D, W, pos: int, T_cap: int, k_blocks: int,
+                         scale: float = 0.0, sel_out=None, stream=None):
+    """One decode step at position pos with top-k block selection.
+    q, k, v, g, o: [B,H,hd]; history [B,H,T_cap,hd]; sel_out [B,H,k_blocks] int32."""
+    torch = _torch()
+    B, H, hd = q.shape
+    st = q.dtype
+    dev = q.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    R, _ = rat_anchor_rows(H, T_cap, Dh)
+    WS, _ = rat_ring_rows(H, Wh)
+    NB = T_cap // TOPK_BLOCK
+    args = [
+        _dtype_code(q), B, H, hd, _ptr(Dh), _ptr(Wh), float(scale), pos, T_cap, int(k_blocks),
+        _dev(q, "q", (B, H, hd), st, dev), _dev(k, "k", (B, H, hd), st, dev),
+        _dev(v, "v", (B, H, hd), st, dev), _dev(g, "g", (B, H, hd), st, dev),
+        _dev(state_k, "state_k", (B, H, hd), torch.float32, dev),
+        _dev(state_v, "state_v", (B, H, hd), torch.float32, dev),
+        _opt(Kc, "Kc", (B, R, hd), st, dev), _opt(Vc, "Vc", (B, R, hd), st, dev),
+        _opt(k_ring, "k_ring", (B, WS, hd), st, dev), _opt(v_ring, "v_ring", (B, WS, hd), st, dev),
+        _dev(hk_hist, "hk_hist", (B, H, T_cap, hd), st, dev),
+        _dev(hv_hist, "hv_hist", (B, H, T_cap, hd), st, dev),
+        _opt(block_means, "block_means", (B, H, NB, hd), torch.float32, dev),
+        _dev(o, "o", (B, H, hd), st, dev),
+        _opt(sel_out, "sel_out", (B, H, int(k_blocks)), torch.int32, dev),
+        _stream(stream, dev),
+    ]
+    _check("rat_decode_step_topk", lib().rat_decode_step_topk(*args))
+
+
+def alloc_topk_history(B: int, H: int, hd: int, T_cap: int, dtype, device, fill=None):
+    """State history [B,H,T_cap,hd] (k and v) and block means [B,H,T_cap//64,hd] fp32."""
+    torch = _torch()
+
+    def mk(shape, dt):
+        if fill is None:
+            return torch.empty(shape, dtype=dt, device=device)
+        return torch.full(shape, fill, dtype=dt, device=device)
+
+    return dict(hk_hist=mk((B, H, T_cap, hd), dtype), hv_hist=mk((B, H, T_cap, hd), dtype),
+                block_means=mk((B, H, T_cap // TOPK_BLOCK, hd), torch.float32))
 
 
 def rat_prefill_backward_workspace_bytes(B: int, H: int, T: int, hd: int, D, W) -> int:

@@ -458,6 +458,73 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D, const int
   return map_hip(launch_decode(dtype, hd, p, stream));
 }
 
+int rat_topk_cache_build(int dtype, int B, int H, int64_t T, int hd, int64_t T_cap,
+                         const void* hk, const void* hv, void* hk_hist, void* hv_hist,
+                         float* block_means, void* stream) {
+  if (dtype != RAT_DTYPE_BF16 && dtype != RAT_DTYPE_F32) return RAT_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 128) return RAT_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || T < 0 || T_cap < 0 || T_cap > kMaxT) return RAT_ERR_INVALID_ARG;
+  if (T > T_cap) return RAT_ERR_CAPACITY;
+  if (B > 65535 || H > 65535) return RAT_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || T == 0) return RAT_OK;
+  for (const void* ptr : {hk, hv, (const void*)hk_hist, (const void*)hv_hist})
+    if (!ptr || !aligned16(ptr)) return RAT_ERR_INVALID_ARG;
+  if (T >= kTopkBlock && (!block_means || !aligned16(block_means))) return RAT_ERR_INVALID_ARG;
+  return map_hip(launch_topk_cache_build(dtype, hd, B, H, T, T_cap, hk, hv, hk_hist, hv_hist,
+                                         block_means, stream));
+}
+
+int rat_decode_step_topk(int dtype, int B, int H, int hd, const int32_t* D, const int32_t* W,
+                         float scale, int64_t pos, int64_t T_cap, int k_blocks, const void* q,
+                         const void* k, const void* v, const void* g, float* state_k,
+                         float* state_v, void* Kc, void* Vc, void* k_ring, void* v_ring,
+                         void* hk_hist, void* hv_hist, float* block_means, void* o,
+                         int32_t* sel_out, void* stream) {
+  int st = check_common(dtype, B, H, hd, D, W);
+  if (st != RAT_OK) return st;
+  if (T_cap < 0 || T_cap > kMaxT || pos < 0 || k_blocks < 0) return RAT_ERR_INVALID_ARG;
+  if (k_blocks > kTopkMaxK || T_cap / kTopkBlock > kTopkMaxBlocks) return RAT_ERR_UNSUPPORTED;
+  if (pos >= T_cap) return RAT_ERR_CAPACITY;
+  if (!(scale <= 0.f) && !std::isfinite(scale)) return RAT_ERR_INVALID_ARG;
+  if (B == 0 || H == 0) return RAT_OK;
+  if ((int64_t)B * H > INT32_MAX / 2) return RAT_ERR_UNSUPPORTED;
+  TopkParams p;
+  std::memset(&p, 0, sizeof(p));
+  st = fill_tables(H, T_cap, D, W, p.ht, p.R, p.WS);
+  if (st != RAT_OK) return st;
+  for (const void* ptr : {q, k, v, g, (const void*)o, (const void*)hk_hist, (const void*)hv_hist})
+    if (!ptr || !aligned16(ptr)) return RAT_ERR_INVALID_ARG;
+  if (!state_k || !state_v || !aligned16(state_k) || !aligned16(state_v)) return RAT_ERR_INVALID_ARG;
+  if (p.R > 0 && (!Kc || !Vc || !aligned16(Kc) || !aligned16(Vc))) return RAT_ERR_INVALID_ARG;
+  if (p.WS > 0 && (!k_ring || !v_ring || !aligned16(k_ring) || !aligned16(v_ring)))
+    return RAT_ERR_INVALID_ARG;
+  if (T_cap >= kTopkBlock && (!block_means || !aligned16(block_means))) return RAT_ERR_INVALID_ARG;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)hd);
+  p.B = B;
+  p.H = H;
+  p.pos = (int)pos;
+  p.k = k_blocks;
+  p.T_cap = T_cap;
+  p.NB = T_cap / kTopkBlock;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.q = q;
+  p.k_in = k;
+  p.v_in = v;
+  p.g = g;
+  p.sk = state_k;
+  p.sv = state_v;
+  p.Kc = Kc;
+  p.Vc = Vc;
+  p.kr = k_ring;
+  p.vr = v_ring;
+  p.hk = hk_hist;
+  p.hv = hv_hist;
+  p.means = block_means;
+  p.o = o;
+  p.sel = sel_out;
+  return map_hip(launch_decode_topk(dtype, hd, p, stream));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

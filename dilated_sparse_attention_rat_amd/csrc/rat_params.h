@@ -115,6 +115,35 @@ struct DecodeParams {
   HeadTables ht;
 };
 
+// Decode with top-k block selection: the decode step's fields plus the
+// state history and its block means.
+struct TopkParams {
+  int B, H;
+  int pos;
+  int k;             // blocks selected per (b, h)
+  int64_t T_cap;     // rows of the history per (b, h)
+  int64_t NB;        // block-mean rows per (b, h): T_cap / kTopkBlock
+  float scale_log2;
+  int64_t R;
+  int64_t WS;
+  const void* q;
+  const void* k_in;
+  const void* v_in;
+  const void* g;
+  float* sk;
+  float* sv;
+  void* Kc;
+  void* Vc;
+  void* kr;
+  void* vr;
+  void* hk;          // [B, H, T_cap, hd] stored states (history)
+  void* hv;
+  float* means;      // [B, H, NB, hd] fp32 mean key state of each complete block
+  void* o;
+  int32_t* sel;      // nullable: [B, H, k] selected blocks, -1 past the count
+  HeadTables ht;
+};
+
 struct BwdParams {
   int B, H, T;
   float scale;       // score scale
@@ -158,6 +187,12 @@ int launch_ring_carry(int dtype, int hd, int B, int H, int64_t WS, const HeadTab
 int launch_attn_prefill(int dtype, int hd, const AttnParams& p, void* stream);
 int launch_decode(int dtype, int hd, const DecodeParams& p, void* stream);
 int launch_backward(int dtype, int hd, const BwdParams& p, void* stream);
+int launch_decode_topk(int dtype, int hd, const TopkParams& p, void* stream);
+// history cache: rows [0, T) of hk/hv ([B,H,T,hd]) into Hk/Hv ([B,H,T_cap,hd])
+// and the mean of every complete block into means ([B,H,T_cap/64,hd] fp32)
+int launch_topk_cache_build(int dtype, int hd, int B, int H, int64_t T, int64_t T_cap,
+                            const void* hk, const void* hv, void* Hk, void* Hv, float* means,
+                            void* stream);
 
 // sizes shared by the host layer and the kernels
 constexpr int kScanThreads = 256;
@@ -166,5 +201,8 @@ int scan_rows_per_chunk(int dtype, int hd);
 
 constexpr int kAttnBN = 64;    // keys per LDS tile
 constexpr int kDecodeThreads = 256;
+constexpr int kTopkBlock = RAT_TOPK_BLOCK;   // positions per selectable block
+constexpr int kTopkMaxK = RAT_TOPK_MAX_K;    // blocks selected per (b, h), at most
+constexpr int kTopkMaxBlocks = 8192;    // eligible blocks per (b, h), at most (scores in LDS)
 
 }  // namespace rat

@@ -244,6 +244,55 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode combined with top-k block selection (RAT+ abstract, v1: RAT+
+ * sparsified to top-k block attention; deep dive, section 四: dilation and
+ * top-k block selection combine, the anchors covering the whole past and the
+ * selected blocks adding density).  The pages fix neither block size nor
+ * scoring; this library's reading: blocks are the aligned runs of
+ * RAT_TOPK_BLOCK positions; a block is eligible at position pos when it lies
+ * wholly before max(0, pos - W); its score is q . (mean stored key state of
+ * the block); the k_blocks highest are selected (equal scores: the lower
+ * block first).
+ *
+ * rat_topk_cache_build: the history cache of a prefill.  Copies rows 0 .. T-1
+ * of hk, hv [B, H, T, hd] ST (the prefill's stored states) into hk_hist,
+ * hv_hist [B, H, T_cap, hd] ST, and writes the mean of every complete block
+ * m < T / RAT_TOPK_BLOCK of hk into block_means [B, H, T_cap /
+ * RAT_TOPK_BLOCK, hd] fp32 (other rows untouched).  Requires T <= T_cap
+ * (else RAT_ERR_CAPACITY) and B, H <= 65535.  block_means may be NULL when
+ * T < RAT_TOPK_BLOCK.
+ */
+#define RAT_TOPK_BLOCK 64
+#define RAT_TOPK_MAX_K 64
+int rat_topk_cache_build(int dtype, int B, int H, int64_t T, int hd,
+                         int64_t T_cap, const void* hk, const void* hv,
+                         void* hk_hist, void* hv_hist, float* block_means,
+                         void* stream);
+
+/*
+ * rat_decode_step_topk: one decode step at position pos, as rat_decode_step
+ * (same state update, anchors from Kc/Vc, window from the ring, own
+ * position), with the k_blocks selected blocks' positions added to the key
+ * set; an anchor position inside a selected block is counted once.  Reads
+ * hk_hist/hv_hist rows < pos and block_means rows of the eligible blocks.
+ * Then, after every read, also writes history row pos <- hat and, when pos
+ * ends a block (pos mod RAT_TOPK_BLOCK = RAT_TOPK_BLOCK-1), that block's
+ * mean.  sel_out (nullable): [B, H, k_blocks] int32, the selected blocks of
+ * each (b, h) best first, -1 past the number selected.  One workgroup per
+ * (b, h), no workspace.  Requires 0 <= pos < T_cap (else RAT_ERR_CAPACITY);
+ * k_blocks <= RAT_TOPK_MAX_K and T_cap / RAT_TOPK_BLOCK <= 8192 (else
+ * RAT_ERR_UNSUPPORTED).
+ */
+int rat_decode_step_topk(int dtype, int B, int H, int hd, const int32_t* D,
+                         const int32_t* W, float scale, int64_t pos,
+                         int64_t T_cap, int k_blocks, const void* q,
+                         const void* k, const void* v, const void* g,
+                         float* state_k, float* state_v, void* Kc, void* Vc,
+                         void* k_ring, void* v_ring, void* hk_hist,
+                         void* hv_hist, float* block_means, void* o,
+                         int32_t* sel_out, void* stream);
+
+/*
  * Bytes of device workspace rat_prefill_backward needs for (B, H, T, hd, D,
  * W).  Pure host function; returns bytes (> 0) or a negative code.
  */

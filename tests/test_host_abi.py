@@ -254,6 +254,51 @@ def test_decode_validation(L):
     assert _dec(L, B=0) == rb.RAT_OK
 
 
+def _tk_build(L, dtype=0, B=1, H=2, T=64, hd=64, T_cap=128, ptr=FAKE, means=FAKE):
+    return L.rat_topk_cache_build(dtype, B, H, T, hd, T_cap, _p(ptr), _p(ptr), _p(ptr), _p(ptr),
+                                  _p(means) if means else None, None)
+
+
+def test_topk_cache_build_validation(L):
+    assert _tk_build(L, dtype=4) == rb.RAT_ERR_UNSUPPORTED
+    assert _tk_build(L, hd=32) == rb.RAT_ERR_UNSUPPORTED
+    assert _tk_build(L, T=129) == rb.RAT_ERR_CAPACITY
+    assert _tk_build(L, T=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_build(L, ptr=0) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_build(L, ptr=FAKE + 4) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_build(L, means=0) == rb.RAT_ERR_INVALID_ARG          # a complete block needs means
+    assert _tk_build(L, means=FAKE + 8) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_build(L, B=0) == rb.RAT_OK
+    assert _tk_build(L, T=0) == rb.RAT_OK
+
+
+def _tk_dec(L, dtype=0, B=1, H=2, hd=64, D=4, W=0, pos=70, T_cap=128, k=4, scale=0.0, q=FAKE,
+            hist=FAKE, means=FAKE, ring=FAKE):
+    d, w, dp, wp = _tables(H, D, W)
+    return L.rat_decode_step_topk(dtype, B, H, hd, dp, wp, scale, pos, T_cap, k, _p(q), _p(),
+                                  _p(), _p(), _p(), _p(), _p(), _p(), _p(ring), _p(ring),
+                                  _p(hist), _p(hist), _p(means) if means else None, _p(), None,
+                                  None)
+
+
+def test_topk_decode_validation(L):
+    assert _tk_dec(L, pos=128) == rb.RAT_ERR_CAPACITY
+    assert _tk_dec(L, pos=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_dec(L, k=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_dec(L, k=rb.TOPK_MAX_K + 1) == rb.RAT_ERR_UNSUPPORTED
+    assert _tk_dec(L, T_cap=64 * 8192 + 64, pos=5) == rb.RAT_ERR_UNSUPPORTED  # block table limit
+    assert _tk_dec(L, dtype=2) == rb.RAT_ERR_UNSUPPORTED
+    assert _tk_dec(L, hd=16) == rb.RAT_ERR_UNSUPPORTED
+    assert _tk_dec(L, D=0) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_dec(L, scale=float("nan")) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_dec(L, q=0) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_dec(L, hist=0) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_dec(L, hist=FAKE + 2) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_dec(L, means=0) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_dec(L, W=8, ring=0) == rb.RAT_ERR_INVALID_ARG         # window needs a ring
+    assert _tk_dec(L, B=0) == rb.RAT_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(rb, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(rb, "_lib", None)
