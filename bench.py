@@ -73,6 +73,8 @@ def parse():
                     help="replay each step as a captured HIP graph instead of three launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-workload", action="store_true")
+    ap.add_argument("--no-topk", action="store_true",
+                    help="skip the decode workload with top-k block selection")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the layer measurement (projections around the prefill)")
     ap.add_argument("--no-backward", action="store_true",
@@ -154,6 +156,22 @@ def decode_bytes(B, H, hd, D, W, pos, es=2):
         tot += 4 * hd * 4                      # fp32 state in and out (k, v)
         tot += (2 * hd * es if W[h] > 0 else 0)  # ring slot
         tot += (2 * hd * es if pos % D[h] == D[h] - 1 else 0)  # anchor row
+    return B * tot
+
+
+def topk_decode_bytes(B, H, hd, D, W, pos, k, es=2, blk=64):
+    """Decode-step bytes with top-k block selection: the plain step's, plus
+    the eligible blocks' fp32 means, the selected blocks' rows that are not
+    anchors (blk - blk/D per block for D dividing blk or a multiple of it),
+    and the history row the step appends (plus a mean when pos ends a block)."""
+    tot = decode_bytes(B, H, hd, D, W, pos, es) // B
+    for h in range(H):
+        ne = max(0, pos - W[h]) // blk
+        ks = min(k, ne)
+        tot += ne * hd * 4                                    # block means
+        tot += ks * (blk - blk // D[h] if D[h] <= blk else blk - 1) * hd * es * 2
+        tot += 2 * hd * es                                    # history row (k, v)
+        tot += (hd * 4 if pos % blk == blk - 1 else 0)        # completed block mean
     return B * tot
 
 
@@ -391,6 +409,9 @@ def main():
     decode_info = None
     if not args.no_decode_workload:
         decode_info = bench_decode_workload(rat, synth, torch, np)
+    topk_info = None
+    if not args.no_topk:
+        topk_info = bench_topk_decode(rat, synth, torch, np)
     chunked_info = None
     if not args.no_chunked:
         chunked_info = bench_chunked(rat, synth, torch, np)
@@ -440,6 +461,7 @@ def main():
         "decode_us_per_step": decode_info["us_mean"] if decode_info else None,
         "kernels": kernels,
         "decode_workload": decode_info,
+        "topk_decode_workload": topk_info,
         "chunked_prefill": chunked_info,
         "backward": backward_info,
         "layer": layer_info,
@@ -494,6 +516,59 @@ def bench_decode_workload(rat, synth, torch, np):
                bytes_mean=float(nbytes.mean()), gbs_mean=float(gbs.mean()),
                hbm_frac=float(gbs.mean() / HBM_PEAK_GBS), steps=steps)
     del cache, inputs
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_topk_decode(rat, synth, torch, np, k_sel=8):
+    """The decode workload with top-k block selection (k_sel blocks of 64
+    positions per query) on top of the dilated key set: the full per-head
+    state history [B,H,T_cap,hd] and its fp32 block means are built from the
+    same context, then every step is timed with HIP events."""
+    w = synth.WORKLOADS[3]
+    B, H, T, hd, steps = w.B, w.H, w.T, w.hd, w.decode_steps
+    T_cap = w.T_cap
+    D, W = list(w.D), list(w.W)
+    st = torch.bfloat16
+    cache = rat.alloc_cache(B, H, hd, T_cap, D, W, st, "cuda")
+    hist = rat.alloc_topk_history(B, H, hd, T_cap, st, "cuda")
+    ws = rat.scan_workspace(1, H, T, hd, "cuda")
+    hk = torch.empty((1, H, T, hd), dtype=st, device="cuda")
+    hv = torch.empty_like(hk)
+    for b in range(B):  # context one batch row at a time, then its history
+        kvg = synth.decode_context_row(w, b)
+        rat.rat_scan_prefill(kvg["k"], kvg["v"], kvg["g"], D, W, T_cap, cache["Kc"][b:b + 1],
+                             cache["Vc"][b:b + 1], cache["state_k"][b:b + 1],
+                             cache["state_v"][b:b + 1], ws, hk=hk, hv=hv,
+                             k_ring=cache["k_ring"][b:b + 1], v_ring=cache["v_ring"][b:b + 1])
+        rat.rat_topk_cache_build(hk, hv, hist["hk_hist"][b:b + 1], hist["hv_hist"][b:b + 1],
+                                 hist["block_means"][b:b + 1])
+        del kvg
+    del hk, hv
+    inputs = [synth.decode_step_inputs(w, s) for s in range(steps)]
+    outs = torch.empty((B, H, hd), dtype=st, device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda._sleep(SPIN_CYCLES)  # the first step queued before its event
+    evs[0].record(stream)
+    for s in range(steps):
+        x = inputs[s]
+        rat.rat_decode_step_topk(x["q"], x["k"], x["v"], x["g"], cache["state_k"],
+                                 cache["state_v"], cache["Kc"], cache["Vc"], cache["k_ring"],
+                                 cache["v_ring"], hist["hk_hist"], hist["hv_hist"],
+                                 hist["block_means"], outs, D, W, T + s, T_cap, k_sel)
+        evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([evs[s].elapsed_time(evs[s + 1]) * 1e3 for s in range(steps)])
+    nbytes = np.array([topk_decode_bytes(B, H, hd, D, W, T + s, k_sel) for s in range(steps)],
+                      dtype=np.float64)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = dict(k_blocks=k_sel, block=64, us_mean=float(us.mean()), us_max=float(us.max()),
+               us_min=float(us.min()), bytes_mean=float(nbytes.mean()),
+               gbs_mean=float(gbs.mean()), hbm_frac=float(gbs.mean() / HBM_PEAK_GBS),
+               steps=steps)
+    del cache, hist, inputs
     torch.cuda.empty_cache()
     return res
 

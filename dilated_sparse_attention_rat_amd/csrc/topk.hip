@@ -16,12 +16,12 @@
 //    anchor position in an eligible block is always an included anchor, so
 //    the union counts it once).
 //
-// Design: one workgroup per (b, h).  The block scores go to LDS (16 lanes
-// per 512-byte fp32 mean row, reduced by cross-lane adds), k rounds of a
-// workgroup arg-max select the blocks, then the anchors, ring slots and the
-// selected blocks' rows are streamed with an online softmax as in the plain
-// decode step (16-byte loads, 16 lanes per row, 4 rows in flight per lane
-// group); after every read the step writes o, the state, the ring slot, the
+// Design: one workgroup per (b, h).  The block scores go to LDS, sized to
+// the block table (one fp32 mean row per 8-32 lanes, reduced by cross-lane
+// adds), k rounds of a workgroup arg-max select the blocks, then the
+// anchors, ring slots and the selected blocks' rows are streamed with an
+// online softmax as in the plain decode step (16-byte loads, one row per
+// 8-32 lanes, 4 rows in flight per lane group); after every read the step writes o, the state, the ring slot, the
 // anchor row, the history row pos and, when pos ends a block, that block's
 // mean.
 #include "rat_device.h"
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const TopkParams p) {
   constexpr int VEC = StTraits<ST>::VEC;
   constexpr int LPR = HD / VEC;    // lanes per row
   constexpr int RPP = 256 / LPR;   // rows per pass
-  __shared__ float s_sc[kTopkMaxBlocks];
+  extern __shared__ float s_sc[];  // [NB] block scores (dynamic LDS)
   __shared__ int s_sel[kTopkMaxK];
   __shared__ float s_m[RPP], s_l[RPP];
   __shared__ float s_acc[RPP][HD];
@@ -162,10 +162,11 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const TopkParams p) {
           bb = s_redf[w];
           ii = s_redi[w];
         }
-      // no finite score left (non-finite input): the slot selects nothing
+      // no comparable score left (NaN input): the slot selects nothing
       if (ii >= ne) ii = -1;
       s_sel[r] = ii;
-      if (ii >= 0) s_sc[ii] = -INFINITY;
+      // a taken block becomes NaN, which no comparison selects again
+      if (ii >= 0) s_sc[ii] = __builtin_nanf("");
     }
     __syncthreads();
   }
@@ -308,7 +309,8 @@ template <typename ST, int HD>
 int launch_t(const TopkParams& p, hipStream_t st) {
   const int64_t nbh = (int64_t)p.B * p.H;
   if (nbh == 0) return 0;
-  hipLaunchKernelGGL((decode_topk_kernel<ST, HD>), dim3((unsigned)nbh), dim3(256), 0, st, p);
+  const size_t lds = sizeof(float) * (size_t)(p.NB > 0 ? p.NB : 1);
+  hipLaunchKernelGGL((decode_topk_kernel<ST, HD>), dim3((unsigned)nbh), dim3(256), lds, st, p);
   return (int)hipGetLastError();
 }
 
