@@ -92,3 +92,64 @@ def test_graph_replays_equal_eager_step(case):
             assert torch.equal(got[n], t), f"replay {rep}: {n} differs from the eager step"
         assert int(s["ws"][2].item()) == 0, "scan workspace reports a timed-out wait"
         say(f"  replay {rep}: identical")
+
+
+def test_graph_topk_decode_replays_equal_eager():
+    """Scan, history build and a top-k block decode step, captured and
+    replayed, equal the eager step bit for bit (history, block means, the
+    selection, o and the caches)."""
+    import dilated_sparse_attention_rat_amd as rat
+    case = ("topk", 2, 3, 700, 128, [4, 1, 64], [0, 33, 128])
+    say("[graph] topk decode")
+
+    def setup(seed):
+        s = _setup(case, seed)
+        B, H, hd = s["dec"]["q"].shape
+        s["hist"] = rat.alloc_topk_history(B, H, hd, s["T_cap"], torch.bfloat16, "cuda", fill=0.0)
+        s["sel"] = torch.zeros((B, H, 4), dtype=torch.int32, device="cuda")
+        return s
+
+    def step(s):
+        c, D, W, T, T_cap, h = s["c"], s["D"], s["W"], s["T"], s["T_cap"], s["hist"]
+        rat.rat_scan_prefill(s["k"], s["v"], s["g"], D, W, T_cap, c["Kc"], c["Vc"], c["state_k"],
+                             c["state_v"], s["ws"], hk=s["hk"], hv=s["hv"], k_ring=c["k_ring"],
+                             v_ring=c["v_ring"])
+        rat.rat_topk_cache_build(s["hk"], s["hv"], h["hk_hist"], h["hv_hist"], h["block_means"])
+        d = s["dec"]
+        rat.rat_decode_step_topk(d["q"], d["k"], d["v"], d["g"], c["state_k"], c["state_v"],
+                                 c["Kc"], c["Vc"], c["k_ring"], c["v_ring"], h["hk_hist"],
+                                 h["hv_hist"], h["block_means"], s["do"], D, W, T, T_cap, 4,
+                                 sel_out=s["sel"])
+
+    def snap(s):
+        out = {n: s[n].clone() for n in ("hk", "hv", "do", "sel")}
+        out.update({n: t.clone() for n, t in s["c"].items() if t is not None})
+        out.update({n: t.clone() for n, t in s["hist"].items()})
+        return out
+
+    def clear(s):
+        _clear(s)
+        s["sel"].zero_()
+        for t in s["hist"].values():
+            t.zero_()
+
+    s, other = setup(13), setup(14)
+    step(s)
+    torch.cuda.synchronize()
+    ref = snap(s)
+    assert int((ref["sel"] >= 0).sum().item()) > 0, "no block was selected"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        clear(s)
+        step(other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snap(s)
+        for n, t in ref.items():
+            assert torch.equal(got[n], t), f"replay {rep}: {n} differs from the eager step"
+        assert int(s["ws"][2].item()) == 0, "scan workspace reports a timed-out wait"
+        say(f"  replay {rep}: identical")
