@@ -186,12 +186,13 @@ def test_topk_matches_plain_decode_when_nothing_is_selected():
     o_topk = _gpu_chain(inp, T, 4, D, W, T_cap, 0, "bf16")[0]
     pre = {n: np.ascontiguousarray(inp[n][:, :, :T]) for n in "qkvg"}
     c = gpu_prefill(pre, D, W, T_cap, "bf16", with_hk=False)["cache"]
+    dws = rat.decode_workspace(B, H, hd, T_cap, D, W, "cuda")
     outs = []
     for s in range(4):
         q, k, v, g = (to_dev(inp[n][:, :, T + s], "bf16") for n in "qkvg")
         o = torch.empty_like(q)
         rat.rat_decode_step(q, k, v, g, c["state_k"], c["state_v"], c["Kc"], c["Vc"],
-                            c["k_ring"], c["v_ring"], o, D, W, T + s, T_cap)
+                            c["k_ring"], c["v_ring"], o, D, W, T + s, T_cap, workspace=dws)
         outs.append(o)
     o_plain = to_np(torch.stack(outs, dim=2))
     d = np.abs(o_topk - o_plain)
