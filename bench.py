@@ -786,7 +786,36 @@ def cpu_baseline(w, target_s):
                 sample=f"oracle prefill (scan + attention, fp64, OpenMP over heads) of {done_bh} "
                        f"of {w.B * w.H} (batch row, head) sequences at T={w.T}, {spent:.1f} s; "
                        "tokens scaled by the fraction of sequences done",
-                seconds=spent)
+                seconds=spent, topk_decode=cpu_topk_decode())
+
+
+def cpu_topk_decode(steps=4, k_sel=8):
+    """The top-k block decode oracle (numpy fp64, one thread) on one
+    (batch row, head) of the decode workload's shape, scaled to a whole step
+    of the batch."""
+    import numpy as np
+    import oracle
+    from dilated_sparse_attention_rat_amd import synth
+    w = synth.WORKLOADS[3]
+    T, hd = w.T, w.hd
+    x = synth.random_case(w.seed, 1, 1, T + steps, hd, w.dtype, w.qkv_std, w.g_bias)
+    f = {n: x[n].astype(np.float64) for n in "qkvg"}
+    hk_u, _ = oracle.scan(f["g"], f["k"])
+    hv_u, _ = oracle.scan(f["g"], f["v"])
+    hk, hv = oracle.round_bf16(hk_u), oracle.round_bf16(hv_u)
+    D, W = np.array(w.D[:1]), np.array(w.W[:1])
+    t0 = time.perf_counter()
+    for s in range(steps):
+        pos = T + s
+        oracle.decode_step_topk(f["q"][:, :, pos], f["k"][:, :, pos], f["v"][:, :, pos],
+                                f["g"][:, :, pos], hk_u[:, :, pos - 1], hv_u[:, :, pos - 1],
+                                hk[:, :, :pos], hv[:, :, :pos], D, W, w.scale, pos, k_sel, True)
+    per_bh = (time.perf_counter() - t0) / steps
+    return dict(us_per_step=per_bh * w.B * w.H * 1e6, unit="us per decode step", cores=1,
+                kind="oracle",
+                sample=f"oracle top-k decode (k={k_sel}, numpy fp64) of one (batch row, head) at "
+                       f"context {T}, {steps} steps, scaled by the batch's {w.B * w.H} "
+                       "(batch row, head) pairs")
 
 
 if __name__ == "__main__":
