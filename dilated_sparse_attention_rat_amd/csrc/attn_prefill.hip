@@ -627,61 +627,70 @@ void attn_prefill_kernel(const AttnParams p) {
 // and waves, so every wave sees the same mix of short (early) and long
 // (late) query rows.
 // ---------------------------------------------------------------------------
-template <typename ST, int HD>
+template <typename ST, int HD, int QB>
 __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, int D, int tb,
                                                const ST* sK, const ST* sVt,
-                                               const QueryIn<ST, HD, 1>& qin) {
-  using C = AttnCfg<ST, HD, 1>;
+                                               const QueryIn<ST, HD, QB>& qin) {
+  using C = AttnCfg<ST, HD, QB>;
   constexpr int VS = kResidentAnchors + 4;
+  constexpr int QW = 16 * QB;  // queries of the block
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
   const int T = p.T;
 
   const int a0 = p.t0;  // absolute position of local row 0
-  WaveState<ST, HD, 1> ws;
-  ws.tq[0] = a0 + tb + col;
-  ws.nlo[0] = min(ws.tq[0], a0 + T - 1) / D;
-  float d = 0.f;
+  WaveState<ST, HD, QB> ws;
 #pragma unroll
-  for (int s = 0; s < C::NS; ++s) {
-    d += frag_dot(qin.q[0][s], qin.k[0][s]);
-    ws.qf[0][s] = frag_scale(qin.q[0][s], p.scale_log2);
+  for (int nb = 0; nb < QB; ++nb) {
+    ws.tq[nb] = a0 + tb + 16 * nb + col;
+    ws.nlo[nb] = min(ws.tq[nb], a0 + T - 1) / D;
+    float d = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+      d += frag_dot(qin.q[nb][s], qin.k[nb][s]);
+      ws.qf[nb][s] = frag_scale(qin.q[nb][s], p.scale_log2);
+    }
+    d = xor16_32_sum(d);
+    ws.m[nb] = d * p.scale_log2;
+    ws.l[nb] = f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) ws.acc[nb][db] = qin.v[nb][db].f32();
   }
-  d = xor16_32_sum(d);
-  ws.m[0] = d * p.scale_log2;
-  ws.l[0] = f32x4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) ws.acc[0][db] = qin.v[0][db].f32();
-  const int n_end = (a0 + min(tb + 15, T - 1)) / D;  // anchors any query of the block sees
-  const int w_full = (a0 + tb) / D;                  // anchors every query of the block sees
+  const int n_end = (a0 + min(tb + QW - 1, T - 1)) / D;  // anchors any query of the block sees
+  const int w_full = (a0 + tb) / D;                      // anchors every query of the block sees
   for (int key0 = 0; key0 < n_end; key0 += C::BN)
-    tile_update<ST, HD, 1, false, VS>(ws, sK + key0 * C::KSTR, sVt + key0, key0, 0, key0 + C::BN > w_full, 0);
+    tile_update<ST, HD, QB, false, VS>(ws, sK + key0 * C::KSTR, sVt + key0, key0, 0,
+                                       key0 + C::BN > w_full, 0);
 
-  const float lt = ws.l[0][0];
-  const int t = ws.tq[0] - a0;  // local row
-  const float inv = 1.f / lt;
   // buffer stores: lanes of rows past T (and the lse of lanes g > 0, or a
   // null lse) use an offset outside the region, which the hardware drops
   const auto orsrc = buffer_region(reinterpret_cast<ST*>(p.o) + (int64_t)(bh / p.H) * p.o_sb +
                                    (int64_t)(bh % p.H) * p.o_sh);
   const auto lrsrc = buffer_region(p.lse != nullptr ? p.lse + bh * T : nullptr);
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    const uint32_t ob =
-        t < T ? (uint32_t)(((int64_t)t * p.o_st + 16 * db + 4 * g) * sizeof(ST)) : kDropOffset;
-    buffer_st4(orsrc, ob, ws.acc[0][db] * inv);
+  for (int nb = 0; nb < QB; ++nb) {
+    const float lt = ws.l[nb][0];
+    const int t = ws.tq[nb] - a0;  // local row
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const uint32_t ob =
+          t < T ? (uint32_t)(((int64_t)t * p.o_st + 16 * db + 4 * g) * sizeof(ST)) : kDropOffset;
+      buffer_st4(orsrc, ob, ws.acc[nb][db] * inv);
+    }
+    const uint32_t lb = (t < T && g == 0 && p.lse != nullptr) ? (uint32_t)t * 4u : kDropOffset;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((ws.m[nb] + __log2f(lt)) * kLn2), lrsrc,
+                                          lb, 0, 0);
   }
-  const uint32_t lb = (t < T && g == 0 && p.lse != nullptr) ? (uint32_t)t * 4u : kDropOffset;
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((ws.m[0] + __log2f(lt)) * kLn2), lrsrc, lb, 0, 0);
 }
 
-template <typename ST, int HD>
-__global__ __launch_bounds__(64 * kResidentWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+template <typename ST, int HD, int QB, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_resident_kernel(const AttnParams p) {
-  using C = AttnCfg<ST, HD, 1>;
+  using C = AttnCfg<ST, HD, QB>;
   constexpr int VS = kResidentAnchors + 4;
-  constexpr int NT = 64 * kResidentWaves;
+  constexpr int NT = 64 * NW;
   __shared__ __attribute__((aligned(16))) ST sK[kResidentAnchors * C::KSTR];
   __shared__ __attribute__((aligned(16))) ST sVt[HD * VS];
 
@@ -741,21 +750,22 @@ void attn_resident_kernel(const AttnParams p) {
   }
   __syncthreads();  // the only barrier: anchors are read-only from here on
 
-  // ---- 16-query blocks: block r + nra*(wave + 8k), two blocks prefetched --
+  // ---- 16*QB-query blocks: block r + nra*(wave + NW*k) ------------------
+  constexpr int QW = 16 * QB;
   const int wave = tid >> 6;
-  const int nblk = (T + 15) / 16;
-  const int stride = p.nra * kResidentWaves;
+  const int nblk = (T + QW - 1) / QW;
+  const int stride = p.nra * NW;
   const int first = r + p.nra * wave;
   const int64_t off = bh * T * HD;
   const ST* qp = reinterpret_cast<const ST*>(p.q) + (bh / p.H) * p.q_sb + (bh % p.H) * p.q_sh;
   const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
   const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
-  // the wave's blocks first + j*stride; sixteen waves per CU hide the load
+  // the wave's blocks first + j*stride; the NW waves of the CU hide the load
   // latency of each block's query inputs
   for (int bi = first; bi < nblk; bi += stride) {
-    QueryIn<ST, HD, 1> qa;
-    qa.load(qp, hkp, hvp, 16 * bi, T, p.q_st);
-    resident_block<ST, HD>(p, bh, D, 16 * bi, sK, sVt, qa);
+    QueryIn<ST, HD, QB> qa;
+    qa.load(qp, hkp, hvp, QW * bi, T, p.q_st);
+    resident_block<ST, HD, QB>(p, bh, D, QW * bi, sK, sVt, qa);
   }
 }
 
@@ -765,8 +775,8 @@ int launch_t(const AttnParams& p, hipStream_t st) {
     if constexpr (sizeof(ST) == 2) {
       const int64_t nwg = (int64_t)p.H * p.B * p.nra;
       if (nwg == 0) return 0;
-      hipLaunchKernelGGL((attn_resident_kernel<ST, HD>), dim3((unsigned)nwg),
-                         dim3(64 * kResidentWaves), 0, st, p);
+      hipLaunchKernelGGL((attn_resident_kernel<ST, HD, kResidentQB, kResidentWaves>),
+                         dim3((unsigned)nwg), dim3(64 * kResidentWaves), 0, st, p);
       return (int)hipGetLastError();
     }
     return (int)hipErrorInvalidValue;

@@ -297,15 +297,15 @@ int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
   for (int h = 0; h < H && resident; ++h)
     resident = W[h] == 0 && (t0 + T - 1) / D[h] <= kResidentAnchors;
   if (resident) {
-    // about one workgroup per CU, at least one 16-query block per wave
+    // about one workgroup per CU, at least one query block per wave
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return RAT_ERR_HIP;
     const int64_t nbh = (int64_t)B * H;
-    const int64_t nblk16 = (T + 15) / 16;
+    const int64_t nblk = (T + 16 * kResidentQB - 1) / (16 * kResidentQB);
     int64_t nra = (std::max(cus, 1) + nbh - 1) / nbh;
-    nra = std::max<int64_t>(1, std::min<int64_t>(nra, (nblk16 + kResidentWaves - 1) / kResidentWaves));
+    nra = std::max<int64_t>(1, std::min<int64_t>(nra, (nblk + kResidentWaves - 1) / kResidentWaves));
     if (nbh * nra > INT32_MAX) return RAT_ERR_UNSUPPORTED;
     p.mode = 1;
     p.nra = (int)nra;

@@ -63,6 +63,7 @@ struct ScanParams {
 // head's anchors fit in LDS (bf16).
 constexpr int kResidentAnchors = 256;
 constexpr int kResidentWaves = 16;  // waves per resident-anchor workgroup
+constexpr int kResidentQB = 1;      // 16-query blocks per wave and block
 
 struct AttnParams {
   int B, H, T;
