@@ -117,3 +117,64 @@ def test_given_selection_is_used():
     r = oracle.decode_step_topk(*args, D, W, 0.3, pos, 2, st_bf16=False, sel=other)
     assert r["sel"].tolist() == other.tolist()
     assert not np.allclose(r["o"], own["o"])
+
+
+@pytest.mark.parametrize("W", [0, 1, 37, 64, 100, 129])
+def test_eligible_blocks_by_enumeration(W):
+    """The number of eligible blocks, and the selection with k above it, equal
+    an enumeration of the blocks that end before the window start."""
+    for pos in [0, 1, 63, 64, 65, 127, 128, 129, 200, 300]:
+        args = _case(6, 1, 1, pos)
+        r = oracle.decode_step_topk(*args, np.array([3]), np.array([W]), 0.3, pos, 100,
+                                    st_bf16=False)
+        want = [m for m in range(pos // 64 + 1) if 64 * m + 63 < max(0, pos - W)]
+        assert int(r["n_elig"][0, 0]) == len(want)
+        assert sorted(int(m) for m in r["sel"][0, 0] if m >= 0) == want
+
+
+def _all_pins():
+    test_no_blocks_is_the_dilated_decode_step([4, 16], [0, 20], 300)
+    test_no_blocks_is_the_dilated_decode_step([3, 64], [7, 0], 257)
+    test_dense_heads_gain_nothing_from_blocks()
+    test_all_blocks_make_attention_dense([8, 5], [0, 64], 448)
+    for D, W, pos in [(4, 0, 300), (5, 37, 517), (64, 128, 1000), (2, 200, 260)]:
+        test_key_set_is_the_union_by_definition(D, W, pos)
+    test_selection_brute_force_and_ties()
+    test_block_means_by_loop()
+    test_given_selection_is_used()
+    for W in [0, 37, 100]:
+        test_eligible_blocks_by_enumeration(W)
+
+
+# planted mistakes in a copy of oracle/topk.py: some pin above must fail
+TOPK_MUTANTS = [
+    ("eligibility ignores the window", "ne = max(0, pos - Wh) // TOPK_BLOCK",
+     "ne = pos // TOPK_BLOCK"),
+    ("ties go to the higher block", "key=lambda m: (-scores[m], m)", "key=lambda m: (-scores[m], -m)"),
+    ("lowest scores selected", "key=lambda m: (-scores[m], m)", "key=lambda m: (scores[m], m)"),
+    ("anchors counted twice", "if p % D != D - 1]", "]"),
+    ("window dropped from the key set", "keys += list(range(lo, t))", "keys += []"),
+    ("block mean over 63 rows", ".mean(axis=3)", "[:, :, :, :63].mean(axis=3)"),
+    ("own position dropped",
+     "K = np.concatenate([hk[b, h, keys], hat_k[b, h][None]], axis=0)\n"
+     "            V = np.concatenate([hv[b, h, keys], hat_v[b, h][None]], axis=0)",
+     "K = hk[b, h, keys]\n            V = hv[b, h, keys]"),
+    ("scale dropped", "logit = scale * (K @ q[b, h])", "logit = K @ q[b, h]"),
+    ("gate roles swapped", "nsk = g * sk + (1.0 - g) * k", "nsk = (1.0 - g) * sk + g * k"),
+    ("given selection ignored", "if sel is None:", "if True:"),
+]
+
+
+@pytest.mark.parametrize("desc,orig,mut", TOPK_MUTANTS, ids=[m[0] for m in TOPK_MUTANTS])
+def test_planted_topk_mistake_is_caught(monkeypatch, desc, orig, mut):
+    import types
+    import oracle.topk as tk
+    src = open(tk.__file__).read()
+    assert src.count(orig) == 1, desc
+    mod = types.ModuleType("oracle.topk_mutant")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(orig, mut), tk.__file__, "exec"), mod.__dict__)
+    for name in ("decode_step_topk", "select_blocks", "keys_topk", "block_means"):
+        monkeypatch.setattr(oracle, name, getattr(mod, name))
+    with pytest.raises(AssertionError):
+        _all_pins()
