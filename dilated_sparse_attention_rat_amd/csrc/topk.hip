@@ -31,6 +31,7 @@ namespace rat {
 namespace {
 
 constexpr int kTU = 4;  // rows per lane group per iteration
+constexpr int kSU = 4;  // block-mean rows per lane group per scoring pass
 
 // history rows [0, T) of one (b, h) block of kTopkBlock rows and its mean
 template <typename ST, int HD>
@@ -113,19 +114,29 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const TopkParams p) {
   }
 
   // ---- scores of the eligible blocks (q . mean key state) ----------------
+  // kSU rows per lane group per pass: every load of a pass is issued before
+  // the first is used (rows past the last eligible block re-read it)
   const float* mp = p.means + bh * p.NB * HD;
-  for (int m0 = 0; m0 < ne; m0 += RPP) {
-    const int m = m0 + rg;
-    const float* row = mp + (int64_t)min(m, ne - 1) * HD + c0;
-    float d = 0.f;
+  for (int m0 = 0; m0 < ne; m0 += RPP * kSU) {
+    f32x4 f[kSU][VEC / 4];
 #pragma unroll
-    for (int i = 0; i < VEC; i += 4) {
-      const f32x4 f = *reinterpret_cast<const f32x4*>(row + i);
-      d += q[i] * f[0] + q[i + 1] * f[1] + q[i + 2] * f[2] + q[i + 3] * f[3];
+    for (int u = 0; u < kSU; ++u) {
+      const float* row = mp + (int64_t)min(m0 + u * RPP + rg, ne - 1) * HD + c0;
+#pragma unroll
+      for (int i = 0; i < VEC / 4; ++i) f[u][i] = *reinterpret_cast<const f32x4*>(row + 4 * i);
     }
 #pragma unroll
-    for (int msk = LPR / 2; msk >= 1; msk >>= 1) d += shfl_xor_f(d, msk);
-    if (cl == 0 && m < ne) s_sc[m] = d;
+    for (int u = 0; u < kSU; ++u) {
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC / 4; ++i)
+        d += q[4 * i] * f[u][i][0] + q[4 * i + 1] * f[u][i][1] + q[4 * i + 2] * f[u][i][2] +
+             q[4 * i + 3] * f[u][i][3];
+#pragma unroll
+      for (int msk = LPR / 2; msk >= 1; msk >>= 1) d += shfl_xor_f(d, msk);
+      const int m = m0 + u * RPP + rg;
+      if (cl == 0 && m < ne) s_sc[m] = d;
+    }
   }
   __syncthreads();
 
