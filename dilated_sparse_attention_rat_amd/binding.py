@@ -98,7 +98,7 @@ def lib() -> ctypes.CDLL:
                                       P, P, P, P, P, P, P, P, P, P, P, i32, P,
                                       sz, P]
         L.rat_decode_step.restype = i32
-        L.rat_topk_cache_build.argtypes = [i32, i32, i32, i64, i32, i64, P, P, P, P, P, P]
+        L.rat_topk_cache_build.argtypes = [i32, i32, i32, i64, i32, i64, i64, P, P, P, P, P, P]
         L.rat_topk_cache_build.restype = i32
         L.rat_decode_step_topk.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64, i32] + [P] * 16
         L.rat_decode_step_topk.restype = i32
@@ -362,9 +362,10 @@ def rat_decode_step(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, o,
     _check("rat_decode_step", lib().rat_decode_step(*args))
 
 
-def rat_topk_cache_build(hk, hv, hk_hist, hv_hist, block_means, stream=None):
-    """History cache of a prefill for top-k decode: rows of hk, hv [B,H,T,hd]
-    into hk_hist, hv_hist [B,H,T_cap,hd], block means [B,H,T_cap//64,hd] fp32."""
+def rat_topk_cache_build(hk, hv, hk_hist, hv_hist, block_means, t0: int = 0, stream=None):
+    """History cache of a prefill (or of the chunk at positions t0 .. t0+T-1)
+    for top-k decode: rows of hk, hv [B,H,T,hd] into hk_hist, hv_hist
+    [B,H,T_cap,hd], block means [B,H,T_cap//64,hd] fp32."""
     torch = _torch()
     B, H, T, hd = hk.shape
     st = hk.dtype
@@ -372,7 +373,7 @@ def rat_topk_cache_build(hk, hv, hk_hist, hv_hist, block_means, stream=None):
     T_cap = hk_hist.shape[2]
     NB = T_cap // TOPK_BLOCK
     args = [
-        _dtype_code(hk), B, H, T, hd, T_cap,
+        _dtype_code(hk), B, H, T, hd, T_cap, int(t0),
         _dev(hk, "hk", (B, H, T, hd), st, dev), _dev(hv, "hv", (B, H, T, hd), st, dev),
         _dev(hk_hist, "hk_hist", (B, H, T_cap, hd), st, dev),
         _dev(hv_hist, "hv_hist", (B, H, T_cap, hd), st, dev),

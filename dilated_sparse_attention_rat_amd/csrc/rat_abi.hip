@@ -459,18 +459,21 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D, const int
 }
 
 int rat_topk_cache_build(int dtype, int B, int H, int64_t T, int hd, int64_t T_cap,
-                         const void* hk, const void* hv, void* hk_hist, void* hv_hist,
-                         float* block_means, void* stream) {
+                         int64_t t0, const void* hk, const void* hv, void* hk_hist,
+                         void* hv_hist, float* block_means, void* stream) {
   if (dtype != RAT_DTYPE_BF16 && dtype != RAT_DTYPE_F32) return RAT_ERR_UNSUPPORTED;
   if (hd != 64 && hd != 128) return RAT_ERR_UNSUPPORTED;
-  if (B < 0 || H < 0 || T < 0 || T_cap < 0 || T_cap > kMaxT) return RAT_ERR_INVALID_ARG;
-  if (T > T_cap) return RAT_ERR_CAPACITY;
+  if (B < 0 || H < 0 || T < 0 || t0 < 0 || T_cap < 0 || T_cap > kMaxT)
+    return RAT_ERR_INVALID_ARG;
+  if (t0 + T > T_cap) return RAT_ERR_CAPACITY;
   if (B > 65535 || H > 65535) return RAT_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || T == 0) return RAT_OK;
   for (const void* ptr : {hk, hv, (const void*)hk_hist, (const void*)hv_hist})
     if (!ptr || !aligned16(ptr)) return RAT_ERR_INVALID_ARG;
-  if (T >= kTopkBlock && (!block_means || !aligned16(block_means))) return RAT_ERR_INVALID_ARG;
-  return map_hip(launch_topk_cache_build(dtype, hd, B, H, T, T_cap, hk, hv, hk_hist, hv_hist,
+  // a block completes in this call when it ends inside t0 .. t0+T-1
+  const bool completes = (t0 + T) / kTopkBlock > t0 / kTopkBlock;
+  if (completes && (!block_means || !aligned16(block_means))) return RAT_ERR_INVALID_ARG;
+  return map_hip(launch_topk_cache_build(dtype, hd, B, H, T, T_cap, t0, hk, hv, hk_hist, hv_hist,
                                          block_means, stream));
 }
 

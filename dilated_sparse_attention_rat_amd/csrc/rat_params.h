@@ -192,8 +192,8 @@ int launch_decode_topk(int dtype, int hd, const TopkParams& p, void* stream);
 // history cache: rows [0, T) of hk/hv ([B,H,T,hd]) into Hk/Hv ([B,H,T_cap,hd])
 // and the mean of every complete block into means ([B,H,T_cap/64,hd] fp32)
 int launch_topk_cache_build(int dtype, int hd, int B, int H, int64_t T, int64_t T_cap,
-                            const void* hk, const void* hv, void* Hk, void* Hv, float* means,
-                            void* stream);
+                            int64_t t0, const void* hk, const void* hv, void* Hk, void* Hv,
+                            float* means, void* stream);
 
 // sizes shared by the host layer and the kernels
 constexpr int kScanThreads = 256;

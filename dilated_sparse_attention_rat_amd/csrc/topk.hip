@@ -33,29 +33,33 @@ namespace {
 constexpr int kTU = 4;  // rows per lane group per iteration
 constexpr int kSU = 4;  // block-mean rows per lane group per scoring pass
 
-// history rows [0, T) of one (b, h) block of kTopkBlock rows and its mean
+// History rows t0 .. t0+T-1 that fall in one block of kTopkBlock rows of
+// one (b, h), and the block's mean once the block is complete.  Rows of the
+// block before t0 were written by an earlier call and are read back from the
+// history for the mean.
 template <typename ST, int HD>
 __global__ __launch_bounds__(256) void topk_cache_build_kernel(const ST* __restrict__ hk,
                                                                const ST* __restrict__ hv, ST* Hk,
                                                                ST* Hv, float* means, int T,
-                                                               int64_t T_cap, int64_t NB) {
+                                                               int t0, int64_t T_cap, int64_t NB) {
   constexpr int VEC = StTraits<ST>::VEC;
   constexpr int LPR = HD / VEC;  // lanes per row
   constexpr int RG = 256 / LPR;  // row groups
   __shared__ float s_sum[RG][HD];
-  const int m = blockIdx.x;
+  const int m = t0 / kTopkBlock + (int)blockIdx.x;
   const int64_t bh = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
   const int tid = threadIdx.x;
   const int rg = tid / LPR;
   const int c0 = (tid - rg * LPR) * VEC;
-  const int r0 = m * kTopkBlock;
-  const int r1 = min(T, r0 + kTopkBlock);
+  const int b0 = m * kTopkBlock;
+  const int r0 = max(b0, t0);
+  const int r1 = min(t0 + T, b0 + kTopkBlock);
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
   for (int r = r0 + rg; r < r1; r += RG) {
-    const u32x4 ku = ld_raw16(hk + (bh * T + r) * HD + c0);
-    const u32x4 vu = ld_raw16(hv + (bh * T + r) * HD + c0);
+    const u32x4 ku = ld_raw16(hk + (bh * T + (r - t0)) * HD + c0);
+    const u32x4 vu = ld_raw16(hv + (bh * T + (r - t0)) * HD + c0);
     st_raw16(Hk + (bh * T_cap + r) * HD + c0, ku);
     st_raw16(Hv + (bh * T_cap + r) * HD + c0, vu);
     float kf[VEC];
@@ -63,7 +67,13 @@ __global__ __launch_bounds__(256) void topk_cache_build_kernel(const ST* __restr
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] += kf[i];
   }
-  if (r1 - r0 < kTopkBlock) return;  // incomplete block (uniform): no mean yet
+  if (r1 - b0 < kTopkBlock) return;  // block not complete yet (uniform): no mean
+  for (int r = b0 + rg; r < r0; r += RG) {  // rows of an earlier call
+    float kf[VEC];
+    unpack16(ld_raw16(Hk + (bh * T_cap + r) * HD + c0), kf, (ST*)nullptr);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] += kf[i];
+  }
 #pragma unroll
   for (int i = 0; i < VEC; ++i) s_sum[rg][c0 + i] = acc[i];
   __syncthreads();
@@ -326,14 +336,16 @@ int launch_t(const TopkParams& p, hipStream_t st) {
 }
 
 template <typename ST, int HD>
-int launch_build_t(int B, int H, int64_t T, int64_t T_cap, const void* hk, const void* hv,
-                   void* Hk, void* Hv, float* means, hipStream_t st) {
+int launch_build_t(int B, int H, int64_t T, int64_t T_cap, int64_t t0, const void* hk,
+                   const void* hv, void* Hk, void* Hv, float* means, hipStream_t st) {
   if (B == 0 || H == 0 || T == 0) return 0;
-  const dim3 grid((unsigned)((T + kTopkBlock - 1) / kTopkBlock), (unsigned)H, (unsigned)B);
+  // the blocks that rows t0 .. t0+T-1 touch
+  const int64_t nblk = (t0 + T - 1) / kTopkBlock - t0 / kTopkBlock + 1;
+  const dim3 grid((unsigned)nblk, (unsigned)H, (unsigned)B);
   hipLaunchKernelGGL((topk_cache_build_kernel<ST, HD>), grid, dim3(256), 0, st,
                      reinterpret_cast<const ST*>(hk), reinterpret_cast<const ST*>(hv),
-                     reinterpret_cast<ST*>(Hk), reinterpret_cast<ST*>(Hv), means, (int)T, T_cap,
-                     T_cap / kTopkBlock);
+                     reinterpret_cast<ST*>(Hk), reinterpret_cast<ST*>(Hv), means, (int)T, (int)t0,
+                     T_cap, T_cap / kTopkBlock);
   return (int)hipGetLastError();
 }
 
@@ -346,14 +358,14 @@ int launch_decode_topk(int dtype, int hd, const TopkParams& p, void* stream) {
 }
 
 int launch_topk_cache_build(int dtype, int hd, int B, int H, int64_t T, int64_t T_cap,
-                            const void* hk, const void* hv, void* Hk, void* Hv, float* means,
-                            void* stream) {
+                            int64_t t0, const void* hk, const void* hv, void* Hk, void* Hv,
+                            float* means, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dtype == RAT_DTYPE_BF16)
-    return hd == 128 ? launch_build_t<bf16, 128>(B, H, T, T_cap, hk, hv, Hk, Hv, means, st)
-                     : launch_build_t<bf16, 64>(B, H, T, T_cap, hk, hv, Hk, Hv, means, st);
-  return hd == 128 ? launch_build_t<float, 128>(B, H, T, T_cap, hk, hv, Hk, Hv, means, st)
-                   : launch_build_t<float, 64>(B, H, T, T_cap, hk, hv, Hk, Hv, means, st);
+    return hd == 128 ? launch_build_t<bf16, 128>(B, H, T, T_cap, t0, hk, hv, Hk, Hv, means, st)
+                     : launch_build_t<bf16, 64>(B, H, T, T_cap, t0, hk, hv, Hk, Hv, means, st);
+  return hd == 128 ? launch_build_t<float, 128>(B, H, T, T_cap, t0, hk, hv, Hk, Hv, means, st)
+                   : launch_build_t<float, 64>(B, H, T, T_cap, t0, hk, hv, Hk, Hv, means, st);
 }
 
 }  // namespace rat

@@ -254,20 +254,23 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D,
  * the block); the k_blocks highest are selected (equal scores: the lower
  * block first).
  *
- * rat_topk_cache_build: the history cache of a prefill.  Copies rows 0 .. T-1
- * of hk, hv [B, H, T, hd] ST (the prefill's stored states) into hk_hist,
- * hv_hist [B, H, T_cap, hd] ST, and writes the mean of every complete block
- * m < T / RAT_TOPK_BLOCK of hk into block_means [B, H, T_cap /
- * RAT_TOPK_BLOCK, hd] fp32 (other rows untouched).  Requires T <= T_cap
- * (else RAT_ERR_CAPACITY) and B, H <= 65535.  block_means may be NULL when
- * T < RAT_TOPK_BLOCK.
+ * rat_topk_cache_build: the history cache of a prefill or of one chunk of a
+ * chunked prefill.  hk, hv [B, H, T, hd] ST hold the stored states of
+ * positions t0 .. t0+T-1 (t0 = 0 for a whole prefill); they are copied into
+ * rows t0 .. t0+T-1 of hk_hist, hv_hist [B, H, T_cap, hd] ST, and the mean
+ * of every block that ends in t0 .. t0+T-1 is written to block_means
+ * [B, H, T_cap / RAT_TOPK_BLOCK, hd] fp32 (other rows untouched; the rows of
+ * such a block before t0 are read from the history, so the chunks must be
+ * built in order).  Requires t0 >= 0 and t0 + T <= T_cap (else
+ * RAT_ERR_CAPACITY) and B, H <= 65535.  block_means may be NULL when no
+ * block ends in the call's rows.
  */
 #define RAT_TOPK_BLOCK 64
 #define RAT_TOPK_MAX_K 64
 int rat_topk_cache_build(int dtype, int B, int H, int64_t T, int hd,
-                         int64_t T_cap, const void* hk, const void* hv,
-                         void* hk_hist, void* hv_hist, float* block_means,
-                         void* stream);
+                         int64_t T_cap, int64_t t0, const void* hk,
+                         const void* hv, void* hk_hist, void* hv_hist,
+                         float* block_means, void* stream);
 
 /*
  * rat_decode_step_topk: one decode step at position pos, as rat_decode_step

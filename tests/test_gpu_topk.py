@@ -126,7 +126,13 @@ def test_topk_decode_steps(case):
     inp = synth.random_case(len(label) * 11 + T, B, H, T + steps, hd, dtype, std, 3.0)
     D, W = np.array(D, np.int32), np.array(W, np.int32)
     o, sel, c, hist = _gpu_chain(inp, T, steps, D, W, T_cap, k_sel, dtype)
+    _check_steps(inp, T, steps, D, W, T_cap, k_sel, dtype, o, sel, c, hist)
 
+
+def _check_steps(inp, T, steps, D, W, T_cap, k_sel, dtype, o, sel, c, hist):
+    """Decode steps at positions T .. T+steps-1 (GPU output o, selections sel,
+    final cache c and history hist) against the oracle over the whole input."""
+    B, H, _, hd = inp["q"].shape
     n = T + steps
     f = {x: inp[x][:, :, :n].astype(np.float64) for x in "qkvg"}
     hk_u, sk = oracle.scan(f["g"], f["k"])
@@ -175,6 +181,70 @@ def test_topk_decode_steps(case):
             p = np.arange(na) * D[h] + D[h] - 1
             chk(check_state_ulp, f"Kc[{b},{h}]", Kc[b, off[h]:off[h] + na], hk[b, h, p], dtype)
     chk.done()
+
+
+CHUNK_CASES = [
+    # label, B, H, chunks, hd, D, W, dtype, steps, T_cap, k
+    ("chunks-bf16", 1, 2, [150, 170, 40], 128, [4, 2], [0, 30], "bf16", 30, 420, 3),
+    ("chunks-f32-64", 2, 2, [64, 100], 64, [8, 1], [16, 0], "f32", 20, 200, 2),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_topk_decode_after_chunked_prefill(case):
+    """A chunked prefill (continuation entry points) whose history is built
+    chunk by chunk (the chunk start t0 given; blocks that straddle a chunk
+    boundary get their mean when the later chunk completes them), then top-k
+    decode steps, against the oracle over the whole sequence."""
+    import dilated_sparse_attention_rat_amd as rat
+    label, B, H, chunks, hd, D, W, dtype, steps, T_cap, k_sel = case
+    T = sum(chunks)
+    say(f"[topk] {label}: B={B} H={H} chunks={chunks} steps={steps} D={D} W={W} {dtype}")
+    std = 1.0 if dtype == "f32" else hd ** -0.5
+    inp = synth.random_case(len(label) * 13 + T, B, H, T + steps, hd, dtype, std, 3.0)
+    D, W = np.array(D, np.int32), np.array(W, np.int32)
+    st = torch_dtype(dtype)
+    c = rat.alloc_cache(B, H, hd, T_cap, D, W, st, "cuda", fill=float("nan"))
+    hist = rat.alloc_topk_history(B, H, hd, T_cap, st, "cuda", fill=float("nan"))
+    rings = [(c["k_ring"], c["v_ring"]),
+             (torch.full_like(c["k_ring"], float("nan")) if c["k_ring"] is not None else None,
+              torch.full_like(c["v_ring"], float("nan")) if c["v_ring"] is not None else None)]
+    states = [(c["state_k"], c["state_v"]),
+              (torch.zeros_like(c["state_k"]), torch.zeros_like(c["state_v"]))]
+    t0, cur = 0, 0
+    for T_i in chunks:
+        k, v, g = (to_dev(np.ascontiguousarray(inp[x][:, :, t0:t0 + T_i]), dtype) for x in "kvg")
+        hk, hv = torch.empty_like(k), torch.empty_like(v)
+        ws = rat.scan_workspace(B, H, T_i, hd, "cuda")
+        (kr, vr), (pk, pv) = rings[cur], rings[1 - cur]
+        (sk, sv), (psk, psv) = states[cur], states[1 - cur]
+        rat.rat_scan_prefill_continue(k, v, g, D, W, T_cap, t0, psk, psv, c["Kc"], c["Vc"], sk,
+                                      sv, ws, hk=hk, hv=hv,
+                                      k_ring_in=pk if t0 > 0 else None,
+                                      v_ring_in=pv if t0 > 0 else None, k_ring=kr, v_ring=vr)
+        rat.rat_topk_cache_build(hk, hv, hist["hk_hist"], hist["hv_hist"], hist["block_means"],
+                                 t0=t0)
+        torch.cuda.synchronize()
+        assert int(ws[2].item()) == 0
+        t0 += T_i
+        cur = 1 - cur
+    (kr, vr), (sk, sv) = rings[1 - cur], states[1 - cur]
+    os_, sels = [], []
+    for s in range(steps):
+        pos = T + s
+        q, k, v, g = (to_dev(inp[x][:, :, pos], dtype) for x in "qkvg")
+        o = torch.empty_like(q)
+        sel = torch.full((B, H, k_sel), -7, dtype=torch.int32, device="cuda")
+        rat.rat_decode_step_topk(q, k, v, g, sk, sv, c["Kc"], c["Vc"], kr, vr, hist["hk_hist"],
+                                 hist["hv_hist"], hist["block_means"], o, D, W, pos, T_cap,
+                                 k_sel, sel_out=sel)
+        os_.append(o)
+        sels.append(sel)
+    torch.cuda.synchronize()
+    o = to_np(torch.stack(os_, dim=2))
+    sel = torch.stack(sels, dim=2).cpu().numpy()
+    _check_steps(inp, T, steps, D, W, T_cap, k_sel, dtype, o, sel,
+                 dict(state_k=sk, state_v=sv, Kc=c["Kc"]), hist)
 
 
 def test_topk_matches_plain_decode_when_nothing_is_selected():

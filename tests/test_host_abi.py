@@ -254,16 +254,20 @@ def test_decode_validation(L):
     assert _dec(L, B=0) == rb.RAT_OK
 
 
-def _tk_build(L, dtype=0, B=1, H=2, T=64, hd=64, T_cap=128, ptr=FAKE, means=FAKE):
-    return L.rat_topk_cache_build(dtype, B, H, T, hd, T_cap, _p(ptr), _p(ptr), _p(ptr), _p(ptr),
-                                  _p(means) if means else None, None)
+def _tk_build(L, dtype=0, B=1, H=2, T=64, hd=64, T_cap=128, t0=0, ptr=FAKE, means=FAKE):
+    return L.rat_topk_cache_build(dtype, B, H, T, hd, T_cap, t0, _p(ptr), _p(ptr), _p(ptr),
+                                  _p(ptr), _p(means) if means else None, None)
 
 
 def test_topk_cache_build_validation(L):
     assert _tk_build(L, dtype=4) == rb.RAT_ERR_UNSUPPORTED
     assert _tk_build(L, hd=32) == rb.RAT_ERR_UNSUPPORTED
     assert _tk_build(L, T=129) == rb.RAT_ERR_CAPACITY
+    assert _tk_build(L, T=64, t0=65) == rb.RAT_ERR_CAPACITY        # t0 + T > T_cap
     assert _tk_build(L, T=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_build(L, t0=-1) == rb.RAT_ERR_INVALID_ARG
+    assert _tk_build(L, T=10, t0=60, means=0) == rb.RAT_ERR_INVALID_ARG  # block 0 ends here
+
     assert _tk_build(L, ptr=0) == rb.RAT_ERR_INVALID_ARG
     assert _tk_build(L, ptr=FAKE + 4) == rb.RAT_ERR_INVALID_ARG
     assert _tk_build(L, means=0) == rb.RAT_ERR_INVALID_ARG          # a complete block needs means
