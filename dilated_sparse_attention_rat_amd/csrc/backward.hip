@@ -321,6 +321,134 @@ void bwd_dq_kernel(const BwdParams p) {
   }
 }
 
+// dq with the anchors resident (no head has a window and every head's
+// anchors fit in LDS, bf16): a workgroup stages all of its head's anchors
+// (rows aD+D-1 of hk and hv) once, then its NW waves take 16-query blocks
+// r + nra*(wave + NW*j) independently -- no barrier after the staging.  Per
+// block the arithmetic is that of bwd_dq_kernel over the anchor tiles.
+template <typename ST, int HD, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void bwd_dq_resident_kernel(const BwdParams p) {
+  using C = BwdCfg<ST, HD>;
+  constexpr int NT = 64 * NW;
+  static_assert(C::TR, "bf16 only: the dq product reads K^T with transposing LDS reads");
+  __shared__ __attribute__((aligned(16))) ST sK[kResidentAnchors * C::RSTR];
+  __shared__ __attribute__((aligned(16))) ST sV[kResidentAnchors * C::RSTR];
+
+  const int nbh = p.B * p.H;
+  const int bhi = blockIdx.x % nbh;  // the nra workgroups of a head are nbh apart
+  const int r = blockIdx.x / nbh;
+  const int h = bhi % p.H;
+  const int T = p.T;
+  const int D = p.ht.D[h];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int64_t bh = bhi;
+  const int64_t base = bh * T * HD;
+  const ST* qp = reinterpret_cast<const ST*>(p.q) + base;
+  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + base;
+  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + base;
+  const ST* op = reinterpret_cast<const ST*>(p.o) + base;
+  const ST* dop = reinterpret_cast<const ST*>(p.dO) + base;
+
+  // ---- stage anchors a < (T-1)/D, padded to whole tiles with row nan-1 ----
+  const int nan = (T - 1) / D;
+  if (nan > 0) {
+    const int rows = (nan + C::BN - 1) / C::BN * C::BN;
+    for (int idx = tid; idx < rows * C::CPR; idx += NT) {
+      const int row = idx / C::CPR;
+      const int c = idx - row * C::CPR;
+      const int64_t src = ((int64_t)min(row, nan - 1) * D + D - 1) * HD + c * C::VEC;
+      st_raw16(sK + row * C::RSTR + c * C::VEC, ld_raw16(hkp + src));
+      st_raw16(sV + row * C::RSTR + c * C::VEC, ld_raw16(hvp + src));
+    }
+  }
+  __syncthreads();  // the only barrier: the anchors are read-only from here on
+
+  const int nblk = (T + 15) / 16;
+  for (int bi = r + p.nra * wave; bi < nblk; bi += p.nra * NW) {
+    const int tw0 = 16 * bi;
+    const int tq = tw0 + col;
+    const bool valid = tq < T;
+    const int64_t row = (int64_t)min(tq, T - 1) * HD;
+
+    // the lane's query: fragments, own position, delta
+    Frag<ST> qf[C::NS], dof[C::NS];
+    float s_own = 0.f, dp_own = 0.f, delta = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+      qf[s] = frag_ld8(qp + row + 32 * s + 8 * g);
+      dof[s] = frag_ld8(dop + row + 32 * s + 8 * g);
+      s_own += frag_dot(qf[s], frag_ld8(hkp + row + 32 * s + 8 * g));
+      dp_own += frag_dot(dof[s], frag_ld8(hvp + row + 32 * s + 8 * g));
+      delta += frag_dot(dof[s], frag_ld8(op + row + 32 * s + 8 * g));
+    }
+    s_own = xor16_32_sum(s_own);
+    dp_own = xor16_32_sum(dp_own);
+    delta = xor16_32_sum(delta);
+    const float lse2 = p.lse[bh * T + min(tq, T - 1)] * kLog2e;
+    const float p_own = __builtin_amdgcn_exp2f(s_own * p.scale_log2 - lse2);
+    const float ds_own = p_own * (dp_own - delta);
+    if (valid && g == 0) {
+      p.delta[bh * T + tq] = delta;
+      *reinterpret_cast<f32x2*>(p.own + 2 * (bh * T + tq)) = f32x2{p.scale * ds_own, p_own};
+    }
+    f32x4 acc[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[db] = ds_own * ld4_f32(hkp + row + 16 * db + 4 * g);
+    Frag<ST> qs[C::NS];
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) qs[s] = frag_scale(qf[s], p.scale_log2);
+
+    // anchors a < nlo are visible to the lane's query (no window)
+    const int nlo = min(tq, T - 1) / D;
+    const int w_end = min(tw0 + 15, T - 1) / D;  // anchors any query of the block sees
+    const int w_full = tw0 / D;                  // anchors every query of the block sees
+    for (int key0 = 0; key0 < w_end; key0 += C::BN) {
+      const bool need_mask = key0 + C::BN > w_full;
+      const ST* tk = sK + key0 * C::RSTR;
+      const ST* tv = sV + key0 * C::RSTR;
+      f32x4 S[C::NMB], dP[C::NMB];
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) {
+        S[mb] = f32x4{-lse2, -lse2, -lse2, -lse2};
+        dP[mb] = f32x4{-delta, -delta, -delta, -delta};
+      }
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+        for (int mb = 0; mb < C::NMB; ++mb) {
+          mma16(S[mb], frag_ld8(tk + (16 * mb + col) * C::RSTR + 32 * s + 8 * g), qs[s]);
+          mma16(dP[mb], frag_ld8(tv + (16 * mb + col) * C::RSTR + 32 * s + 8 * g), dof[s]);
+        }
+      f32x4 dS[C::NMB];
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool vis = !need_mask || (valid && key0 + 16 * mb + 4 * g + e < nlo);
+          const float pe = vis ? __builtin_amdgcn_exp2f(S[mb][e]) : 0.f;
+          dS[mb][e] = pe * dP[mb][e];
+        }
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        const Frag<ST> bfr = frag_from(dS[2 * kk], dS[2 * kk + 1], (ST*)nullptr);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          mma16(acc[db], frag_rows<ST, HD>(tk, nullptr, kk, db, col, g), bfr);
+      }
+    }
+    if (valid) {
+      ST* dqp = reinterpret_cast<ST*>(p.dq) + base + (int64_t)tq * HD;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) st4(dqp + 16 * db + 4 * g, p.scale * acc[db]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 2. state gradients from the keys' side
 // ---------------------------------------------------------------------------
@@ -681,7 +809,15 @@ template <typename ST, int HD>
 int launch_t(const BwdParams& p, hipStream_t st) {
   const int nq = (p.T + 63) / 64;
   const int ngrp = (p.B * p.H + kXcds - 1) / kXcds * kXcds;  // (b, h) groups, padded
-  hipLaunchKernelGGL((bwd_dq_kernel<ST, HD>), dim3(ngrp * nq), dim3(256), 0, st, p);
+  if constexpr (sizeof(ST) == 2) {
+    if (p.nra > 0)
+      hipLaunchKernelGGL((bwd_dq_resident_kernel<ST, HD, kBwdResidentWaves>),
+                         dim3(p.B * p.H * p.nra), dim3(64 * kBwdResidentWaves), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<ST, HD>), dim3(ngrp * nq), dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<ST, HD>), dim3(ngrp * nq), dim3(256), 0, st, p);
+  }
   if (p.nkt > 0)
     hipLaunchKernelGGL((bwd_dkv_kernel<ST, HD>), dim3(ngrp * p.nkt), dim3(256), 0, st, p);
   const int ncb = (p.nchunk + RCfg<ST, HD>::CPB - 1) / RCfg<ST, HD>::CPB;

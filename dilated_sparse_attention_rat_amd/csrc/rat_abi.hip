@@ -644,6 +644,23 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
   if ((int64_t)B * H * L.nchunk > INT32_MAX || nkt > INT32_MAX) return RAT_ERR_UNSUPPORTED;
   p.nkt = (int)nkt;
   p.nsplit = nsplit;
+  // dq with the anchors resident in LDS: bf16, no window, every head's
+  // anchors fit; about one workgroup per CU, at least one block per wave
+  bool resident = dtype == RAT_DTYPE_BF16;
+  for (int h = 0; h < H && resident; ++h)
+    resident = W[h] == 0 && (T - 1) / D[h] <= kResidentAnchors;
+  if (resident) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return RAT_ERR_HIP;
+    const int64_t nbh = (int64_t)B * H;
+    const int64_t nblk = (T + 15) / 16;
+    int64_t nra = (std::max(cus, 1) + nbh - 1) / nbh;
+    nra = std::max<int64_t>(
+        1, std::min<int64_t>(nra, (nblk + kBwdResidentWaves - 1) / kBwdResidentWaves));
+    if (nbh * nra <= INT32_MAX) p.nra = (int)nra;
+  }
   p.kc_split = (int64_t)B * R * hd;
   p.q = q;
   p.k = k;

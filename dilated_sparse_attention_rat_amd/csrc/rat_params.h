@@ -64,6 +64,7 @@ struct ScanParams {
 constexpr int kResidentAnchors = 256;
 constexpr int kResidentWaves = 16;  // waves per resident-anchor workgroup
 constexpr int kResidentQB = 1;      // 16-query blocks per wave and block
+constexpr int kBwdResidentWaves = 12;  // waves per workgroup of the resident-anchor dq kernel
 
 struct AttnParams {
   int B, H, T;
@@ -153,6 +154,7 @@ struct BwdParams {
   int nchunk;        // reverse-scan chunks of 64 positions per sequence
   int nkt;           // workgroups per head in the key-side grid (max over heads)
   int nsplit;        // workgroups sharing the queries of one anchor tile
+  int nra;           // > 0: dq with the anchors resident in LDS, nra workgroups per (b, h)
   int64_t kc_split;  // elements of one partial anchor-gradient buffer (B*R*hd)
   const void* q;
   const void* k;

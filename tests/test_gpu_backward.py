@@ -74,6 +74,10 @@ CASES = [
     ("T1", 1, 2, 1, 128, [4, 1], [0, 3], "bf16"),
     ("D-beyond-T", 1, 2, 50, 64, [64, 100], [0, 0], "f32"),
     ("T129-dense", 1, 1, 129, 128, [1], [0], "bf16"),
+    # windowless bf16 with at most 256 anchors per head: dq with resident anchors
+    ("bf16-resident", 2, 3, 1000, 128, [4, 16, 8], [0, 0, 0], "bf16"),
+    ("bf16-64-resident", 1, 2, 517, 64, [3, 5], [0, 0], "bf16"),
+    ("resident-no-anchor", 1, 2, 40, 128, [64, 100], [0, 0], "bf16"),
 ]
 
 
