@@ -21,9 +21,9 @@
 // adds), k rounds of a workgroup arg-max select the blocks, then the
 // anchors, ring slots and the selected blocks' rows are streamed with an
 // online softmax as in the plain decode step (16-byte loads, one row per
-// 8-32 lanes, 4 rows in flight per lane group); after every read the step writes o, the state, the ring slot, the
-// anchor row, the history row pos and, when pos ends a block, that block's
-// mean.
+// 8-32 lanes, 4 rows in flight per lane group); after every read the step
+// writes o, the state, the ring slot, the anchor row, the history row pos
+// and, when pos ends a block, that block's mean.
 #include "rat_device.h"
 
 namespace rat {
