@@ -786,7 +786,20 @@ def cpu_baseline(w, target_s):
                 sample=f"oracle prefill (scan + attention, fp64, OpenMP over heads) of {done_bh} "
                        f"of {w.B * w.H} (batch row, head) sequences at T={w.T}, {spent:.1f} s; "
                        "tokens scaled by the fraction of sequences done",
-                seconds=spent, topk_decode=cpu_topk_decode())
+                seconds=spent, cpu_model=cpu_model(), nproc=os.cpu_count(),
+                topk_decode=cpu_topk_decode())
+
+
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_topk_decode(steps=4, k_sel=8):
