@@ -619,7 +619,8 @@ void attn_prefill_kernel(const AttnParams p) {
 // ---------------------------------------------------------------------------
 // Resident-anchor kernel: no window and at most kResidentAnchors anchors per
 // head (e.g. T = 4096 at D = 16), bf16.  A workgroup loads its head's anchor
-// rows into LDS once (K row-major, V transposed: 136 KB at hd = 128) and its
+// rows into LDS once (K and V row-major: 140 KB at hd = 128; V's transposed
+// MFMA fragments come from ds_read_b64_tr_b16) and its
 // 16 waves then stream 16-query blocks independently -- no barrier and no
 // global K/V traffic per block; with four waves per SIMD, the waves waiting
 // for their next block's query rows (q, own key, own value) overlap the
@@ -629,10 +630,9 @@ void attn_prefill_kernel(const AttnParams p) {
 // ---------------------------------------------------------------------------
 template <typename ST, int HD, int QB>
 __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, int D, int tb,
-                                               const ST* sK, const ST* sVt,
+                                               const ST* sK, const ST* sV,
                                                const QueryIn<ST, HD, QB>& qin) {
   using C = AttnCfg<ST, HD, QB>;
-  constexpr int VS = kResidentAnchors + 4;
   constexpr int QW = 16 * QB;  // queries of the block
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
@@ -660,7 +660,7 @@ __device__ __forceinline__ void resident_block(const AttnParams& p, int64_t bh, 
   const int n_end = (a0 + min(tb + QW - 1, T - 1)) / D;  // anchors any query of the block sees
   const int w_full = (a0 + tb) / D;                      // anchors every query of the block sees
   for (int key0 = 0; key0 < n_end; key0 += C::BN)
-    tile_update<ST, HD, QB, false, VS>(ws, sK + key0 * C::KSTR, sVt + key0, key0, 0,
+    tile_update<ST, HD, QB, true, C::VRSTR>(ws, sK + key0 * C::KSTR, sV + key0 * C::VRSTR, key0, 0,
                                        key0 + C::BN > w_full, 0);
 
   // buffer stores: lanes of rows past T (and the lse of lanes g > 0, or a
@@ -689,10 +689,9 @@ template <typename ST, int HD, int QB, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_resident_kernel(const AttnParams p) {
   using C = AttnCfg<ST, HD, QB>;
-  constexpr int VS = kResidentAnchors + 4;
   constexpr int NT = 64 * NW;
   __shared__ __attribute__((aligned(16))) ST sK[kResidentAnchors * C::KSTR];
-  __shared__ __attribute__((aligned(16))) ST sVt[HD * VS];
+  __shared__ __attribute__((aligned(16))) ST sV[kResidentAnchors * C::VRSTR];
 
   const int L = blockIdx.x;
   const int per_rank = p.B * p.nra;
@@ -726,24 +725,17 @@ void attn_resident_kernel(const AttnParams p) {
                    ld_raw16(kcp + (int64_t)a * HD + c16 * C::VEC));
         }
       }
-      // V transposed: work item = 4 anchors x VEC channels
-      static_assert((C::VTITEMS / (C::BN / 4)) * C::VEC == HD, "items cover hd channels");
-      for (int idx = tid; idx < C::VTITEMS; idx += NT) {
-        const int dg = idx / (C::BN / 4);
-        const int kg = idx - dg * (C::BN / 4);
-        u32x4 v[4];
+      // V row-major like K (its transposed fragments are read with
+      // ds_read_b64_tr_b16)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          v[rr] = ld_raw16(vcp + (int64_t)min(C::BN * j + 4 * kg + rr, nan - 1) * HD + dg * C::VEC);
-        ST* dst = sVt + (dg * C::VEC) * VS + C::BN * j + 4 * kg;
-#pragma unroll
-        for (int e = 0; e < C::VEC; ++e) {
-          const int w = e >> 1;
-          const int sh = (e & 1) * 16;
-          const uint32_t x0 = (v[0][w] >> sh) & 0xffffu, x1 = (v[1][w] >> sh) & 0xffffu;
-          const uint32_t x2 = (v[2][w] >> sh) & 0xffffu, x3 = (v[3][w] >> sh) & 0xffffu;
-          u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
-          *reinterpret_cast<u32x2*>(dst + e * VS) = pk;
+      for (int i = 0; i < (C::KITEMS + NT - 1) / NT; ++i) {
+        const int idx = tid + NT * i;
+        if (idx < C::KITEMS) {
+          const int row = idx / C::CPR;
+          const int c16 = idx - row * C::CPR;
+          const int a = min(C::BN * j + row, nan - 1);
+          st_raw16(sV + (C::BN * j + row) * C::VRSTR + c16 * C::VEC,
+                   ld_raw16(vcp + (int64_t)a * HD + c16 * C::VEC));
         }
       }
     }
@@ -765,7 +757,7 @@ void attn_resident_kernel(const AttnParams p) {
   for (int bi = first; bi < nblk; bi += stride) {
     QueryIn<ST, HD, QB> qa;
     qa.load(qp, hkp, hvp, QW * bi, T, p.q_st);
-    resident_block<ST, HD, QB>(p, bh, D, QW * bi, sK, sVt, qa);
+    resident_block<ST, HD, QB>(p, bh, D, QW * bi, sK, sV, qa);
   }
 }
 
