@@ -1,33 +1,37 @@
 """Benchmark of the RAT+ hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--graph]
-                    [--no-cpu-baseline] [--no-decode-workload] [--calibration-copy MIB]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--configs 1,2,4]
+                    [--graph] [--no-cpu-baseline] [--no-decode-workload] [--calibration-copy MIB]
 
-A step is one pass of the whole hot path over one batch of the prefill
-workload (default: the 1.5B-like shape B=4, H=16, hd=128, T=4096, D=16, no
-window): the recurrence scan with fused anchor compaction, the dilated
-attention over the anchor cache, and one decode step that appends token T to
-every sequence.  Inputs are synthetic (seeded), resident in HBM before the
-timed region, and alternate between two copies so no step re-reads the
-previous step's data from the 256 MB last-level cache.
+A step is one pass of the whole hot path over one batch of the headline
+prefill workload (default: the largest prefill configuration, the head-wise
+hybrid B=2, H=32, hd=128, T=8192 with heads 0-1 dense and heads 2-31 at D=4):
+the recurrence scan with fused anchor compaction, the dilated attention over
+the anchor cache, and one decode step that appends token T to every
+sequence.  Inputs are synthetic (seeded), resident in HBM before the timed
+region, and alternate between two copies so no step re-reads the previous
+step's data from the 256 MB last-level cache.
 
 Printed: ONE JSON line.  ``value`` is prefill tokens per second of the whole
 step, B*T / (wall time of K steps / K), the K steps bracketed by device
 synchronisations; the three launches of a step are enqueued one by one
-(``--graph``: captured once into a HIP graph per input copy and replayed,
-which measured slightly slower here).
-Per-kernel times come from a second, instrumented pass of K eager steps with
-HIP events recorded between the kernels on the stream they are launched on
-(the event markers themselves cost a few microseconds per step, which is why
-they are kept out of the pass that gives ``value``).  The
-decode-step time of the metric is measured on the decode workload (batch 64,
-32 heads, context 32768, D=64, W=128, 256 steps) and reported beside it, as
-is a chunked prefill (the long-prefill workload in four chunks through the
-continuation entry points, against the same sequence in one call) and the
-prefill backward (dq, dk, dv, dg) of the step's workload, and one whole RAT+
-layer over it (projections as GEMMs around the prefill, d_model = H*hd).
-``roofline`` is for the kernel that takes the most time in the step;
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
+(``--graph``: captured once into a HIP graph per input copy and replayed).
+Per-kernel times come from each kernel launched K times back to back between
+one pair of HIP events on its launch stream; ``kernels`` holds the headline
+workload's, ``configs`` the scan and attention of every prefill workload
+(1.5B-like, long prefill with window, head-wise hybrid), each with its
+algorithmic bytes and FLOPs and a roofline entry against the roof that binds
+it.  Every scan workspace's error word (a bounded wait that gave up) is read
+after each pass; a set word turns the line into an error and the exit code
+non-zero.  The decode-step time of the metric is measured on the decode
+workload (batch 64, 32 heads, context 32768, D=64, W=128, 256 steps) and
+reported beside it, as are the decode with top-k block selection, a chunked
+prefill (the long-prefill workload in four chunks through the continuation
+entry points, against the same sequence in one call), the prefill backward
+and one whole RAT+ layer (on the 1.5B-like workload by default).
+``roofline`` is for the kernel that takes the most time in the headline
+step; ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+work, on all host cores and on one.
 """
 from __future__ import annotations
 
@@ -68,7 +72,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=4,
+                    help="prefill workload of the headline step (default: the largest, the "
+                         "head-wise hybrid B=2 H=32 T=8192)")
+    ap.add_argument("--configs", type=lambda v: [int(x) for x in v.split(",") if x],
+                    default=[1, 2, 4],
+                    help="prefill workloads whose scan and attention are also timed per kernel")
+    ap.add_argument("--side-workload", type=int, default=1,
+                    help="prefill workload of the backward and layer legs")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph instead of three launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,6 +209,171 @@ def traffic_from_profiles(kernel_file, launch_key):
 
 
 # ---------------------------------------------------------------------------
+class ScanError(RuntimeError):
+    """A scan's bounded wait gave up (workspace word 2 set): invalid results."""
+
+
+def roof_for(kind, nbytes, flops, us):
+    """Roofline entry of one kernel: the binding roof is the one whose time
+    at peak is longer (HBM bytes at 8 TB/s or useful FLOPs at the bf16 MFMA
+    peak); the scan is priced on HBM only."""
+    t = us * 1e-6
+    gbs = nbytes / t / 1e9
+    if kind == "scan" or flops is None:
+        return dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=gbs / HBM_PEAK_GBS)
+    tf = flops / t / 1e12
+    if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
+        return dict(bound="mfma", achieved=tf, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=tf / MFMA_BF16_PEAK_TFLOPS)
+    return dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=gbs / HBM_PEAK_GBS)
+
+
+class PrefillRig:
+    """Two resident input copies of one prefill workload (so consecutive
+    launches never re-read the previous launch's data from the 256 MB
+    last-level cache), their outputs, caches and scan workspaces, and the
+    launches of the path: scan, attention and one decode step at position T."""
+
+    def __init__(self, rat, synth, torch, wid, decode=True):
+        w = synth.WORKLOADS[wid]
+        assert w.decode_steps == 0, "a prefill workload"
+        self.rat, self.torch, self.w, self.wid = rat, torch, w, wid
+        dev = "cuda"
+        st = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.es = 2 if w.dtype == "bf16" else 4
+        self.B, self.H, self.T, self.hd = w.B, w.H, w.T, w.hd
+        self.D, self.W = list(w.D), list(w.W)
+        self.T_cap = w.T + 1 if decode else w.T
+        B, H, T, hd = self.B, self.H, self.T, self.hd
+        x = synth.prefill_inputs(w)
+        self.sets = []
+        for copy in range(2):
+            s = {n: torch.from_numpy(x[n]).to(dev).to(st) for n in "qkvg"}
+            s["hk"] = torch.empty_like(s["k"])
+            s["hv"] = torch.empty_like(s["v"])
+            s["o"] = torch.empty_like(s["q"])
+            s["lse"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+            s["cache"] = rat.alloc_cache(B, H, hd, self.T_cap, self.D, self.W, st, dev)
+            s["ws"] = rat.scan_workspace(B, H, T, hd, dev)
+            if decode:
+                dx = synth.draw((B, H, 1, hd), w.seed + 77, w.qkv_std, w.g_bias, w.dtype)
+                s["dec"] = {n: torch.from_numpy(dx[n][:, :, 0]).to(dev).to(st) for n in "qkvg"}
+                s["do"] = torch.empty_like(s["dec"]["q"])
+                s["dws"] = rat.decode_workspace(B, H, hd, self.T_cap, self.D, self.W, dev)
+            self.sets.append(s)
+        del x
+        self.stream = torch.cuda.current_stream()
+
+    def scan(self, s):
+        c = s["cache"]
+        self.rat.rat_scan_prefill(s["k"], s["v"], s["g"], self.D, self.W, self.T_cap, c["Kc"],
+                                  c["Vc"], c["state_k"], c["state_v"], s["ws"], hk=s["hk"],
+                                  hv=s["hv"], k_ring=c["k_ring"], v_ring=c["v_ring"])
+
+    def attn(self, s):
+        c = s["cache"]
+        self.rat.rat_dilated_attn_prefill(s["q"], s["hk"], s["hv"], c["Kc"], c["Vc"], self.D,
+                                          self.W, self.T_cap, s["o"], s["lse"])
+
+    def dec(self, s):
+        c, d = s["cache"], s["dec"]
+        self.rat.rat_decode_step(d["q"], d["k"], d["v"], d["g"], c["state_k"], c["state_v"],
+                                 c["Kc"], c["Vc"], c["k_ring"], c["v_ring"], s["do"], self.D,
+                                 self.W, self.T, self.T_cap, workspace=s["dws"])
+
+    def step(self, s, ev=None):
+        fns = (self.scan, self.attn, self.dec)
+        if ev is not None:
+            ev[0].record(self.stream)
+        for i, fn in enumerate(fns):
+            fn(s)
+            if ev is not None:
+                ev[i + 1].record(self.stream)
+
+    def check(self, what):
+        """Raise ScanError if a scan wait of any launch so far timed out (the
+        error word is sticky: it stays set until the workspace is zeroed)."""
+        self.torch.cuda.synchronize()
+        for s in self.sets:
+            if int(s["ws"][2].item()) != 0:
+                raise ScanError(f"{self.w.name}: a scan wait timed out during {what}")
+
+    def kernel_ms(self, fn, spin, K, reps=3):
+        """Mean time per launch of fn, K launches back to back between one
+        pair of HIP events on the launch stream; fastest of reps passes (a
+        one-time host stall while queueing, once seen at about 40 ms, would
+        otherwise land inside a single pass)."""
+        torch = self.torch
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            # keep the GPU busy while the host queues the K launches: one
+            # untimed launch of the same kernel when a launch outlasts the
+            # host's enqueue time, a device spin for the short decode step
+            if spin:
+                torch.cuda._sleep(max(SPIN_CYCLES, K * 150_000))
+            else:
+                fn(self.sets[1])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            for i in range(K):
+                fn(self.sets[i % 2])
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / K
+            best = ms if best is None else min(best, ms)
+        return best
+
+    def kernels(self, K, with_decode=True):
+        """Per-kernel times, algorithmic bytes and FLOPs, and roofline entries."""
+        w, es = self.w, self.es
+        scan_us = self.kernel_ms(self.scan, False, K) * 1e3
+        attn_us = self.kernel_ms(self.attn, False, K) * 1e3
+        self.check("the per-kernel passes")
+        sb, ab, af = scan_bytes(w, es), attn_bytes(w, es), attn_flops(w)
+        ks = {
+            "scan": dict(us=scan_us, bytes=sb, gbs=sb / scan_us / 1e3, kernel="scan_kernel",
+                         roofline=roof_for("scan", sb, None, scan_us)),
+            "attention": dict(us=attn_us, bytes=ab, flops=af, gbs=ab / attn_us / 1e3,
+                              tflops=af / attn_us / 1e6, kernel=attn_kernel_name(w),
+                              roofline=roof_for("attention", ab, af, attn_us)),
+        }
+        ks["scan"]["roofline"]["traffic"] = traffic_from_profiles("scan.hip", f"scan_w{self.wid}")
+        ks["attention"]["roofline"]["traffic"] = traffic_from_profiles(
+            "attn_prefill.hip", f"attn_w{self.wid}")
+        ks["attention"]["mfma_frac_useful"] = af / attn_us / 1e6 / MFMA_BF16_PEAK_TFLOPS
+        ks["attention"]["hbm_frac"] = ab / attn_us / 1e3 / HBM_PEAK_GBS
+        if with_decode:
+            dec_us = self.kernel_ms(self.dec, True, K) * 1e3
+            db = decode_bytes(self.B, self.H, self.hd, self.D, self.W, self.T, es)
+            ks["decode_step"] = dict(us=dec_us, bytes=db, gbs=db / dec_us / 1e3)
+        return ks
+
+    def describe(self):
+        w = self.w
+        return (f"{w.name}: B={w.B} H={w.H} hd={w.hd} T={w.T} D={head_list(w.D)} "
+                f"W={head_list(w.W)}")
+
+
+def bench_prefill_config(rat, synth, torch, wid, K):
+    """Scan and attention of one prefill workload, each timed K launches back
+    to back; tokens per second of the two kernels."""
+    rig = PrefillRig(rat, synth, torch, wid, decode=False)
+    for i in range(2):
+        rig.scan(rig.sets[i])
+        rig.attn(rig.sets[i])
+    rig.check("the warm-up")
+    ks = rig.kernels(K, with_decode=False)
+    tok = rig.B * rig.T
+    res = dict(workload=rig.describe(), tok_s_kernels=tok / ((ks["scan"]["us"] + ks["attention"]["us"]) * 1e-6),
+               **ks)
+    del rig
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,7 +391,6 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    dev = "cuda:0"
     torch.cuda.set_device(0)
     # the first device spin of a process is not a reliable spin (its kernel
     # is loaded then); issue one here so the spins ahead of timed regions are
@@ -223,56 +398,27 @@ def main():
     torch.cuda.synchronize()
     rat.lib()  # fail loudly if the HIP library is missing
 
+    try:
+        line = run(args, rat, synth, torch, np)
+    except ScanError as e:
+        print(json.dumps({"metric": METRIC, "value": None, "unit": "tok/s", "n_gpus": 1,
+                          "error": str(e)}))
+        sys.exit(3)
+    print(json.dumps(line))
+
+
+METRIC = "prefill tok/s + decode step µs per RAT+ layer; % of HBM / MFMA bf16 peak"
+
+
+def run(args, rat, synth, torch, np):
     w = synth.WORKLOADS[args.workload]
-    assert w.decode_steps == 0, "the step workload must be a prefill workload"
-    st = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    es = 2 if w.dtype == "bf16" else 4
-    B, H, T, hd = w.B, w.H, w.T, w.hd
-    D, W = list(w.D), list(w.W)
-    T_cap = T + 1
-
-    # ---- inputs (two copies), outputs and caches resident in HBM ----------
-    x = synth.prefill_inputs(w)
-    sets = []
-    for copy in range(2):
-        s = {n: torch.from_numpy(x[n]).to(dev).to(st) for n in "qkvg"}
-        s["hk"] = torch.empty_like(s["k"])
-        s["hv"] = torch.empty_like(s["v"])
-        s["o"] = torch.empty_like(s["q"])
-        s["lse"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-        s["cache"] = rat.alloc_cache(B, H, hd, T_cap, D, W, st, dev)
-        s["ws"] = rat.scan_workspace(B, H, T, hd, dev)
-        dx = synth.draw((B, H, 1, hd), w.seed + 77, w.qkv_std, w.g_bias, w.dtype)
-        s["dec"] = {n: torch.from_numpy(dx[n][:, :, 0]).to(dev).to(st) for n in "qkvg"}
-        s["do"] = torch.empty_like(s["dec"]["q"])
-        s["dws"] = rat.decode_workspace(B, H, hd, T_cap, D, W, dev)
-        sets.append(s)
-    del x
-    stream = torch.cuda.current_stream()
-
-    def step(s, ev=None):
-        c = s["cache"]
-        if ev is not None:
-            ev[0].record(stream)
-        rat.rat_scan_prefill(s["k"], s["v"], s["g"], D, W, T_cap, c["Kc"], c["Vc"], c["state_k"],
-                             c["state_v"], s["ws"], hk=s["hk"], hv=s["hv"], k_ring=c["k_ring"],
-                             v_ring=c["v_ring"])
-        if ev is not None:
-            ev[1].record(stream)
-        rat.rat_dilated_attn_prefill(s["q"], s["hk"], s["hv"], c["Kc"], c["Vc"], D, W, T_cap,
-                                     s["o"], s["lse"])
-        if ev is not None:
-            ev[2].record(stream)
-        d = s["dec"]
-        rat.rat_decode_step(d["q"], d["k"], d["v"], d["g"], c["state_k"], c["state_v"], c["Kc"],
-                            c["Vc"], c["k_ring"], c["v_ring"], s["do"], D, W, T, T_cap,
-                            workspace=s["dws"])
-        if ev is not None:
-            ev[3].record(stream)
+    rig = PrefillRig(rat, synth, torch, args.workload)
+    B, T = rig.B, rig.T
+    sets, stream = rig.sets, rig.stream
 
     if args.calibration_copy > 0:
         n = args.calibration_copy * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         for _ in range(3):
             torch.mul(a, 1.0, out=b)
@@ -280,8 +426,8 @@ def main():
         del a, b
 
     for i in range(args.warmup):
-        step(sets[i % 2])
-    torch.cuda.synchronize()
+        rig.step(sets[i % 2])
+    rig.check("the warm-up")
 
     # one graph per input copy: the step's three launches, replayed as a unit
     graphs = None
@@ -290,7 +436,7 @@ def main():
         for s in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(s)
+                rig.step(s)
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % 2].replay()
@@ -304,106 +450,47 @@ def main():
         if graphs is not None:
             graphs[i % 2].replay()
         else:
-            step(sets[i % 2])
+            rig.step(sets[i % 2])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    rig.check("the timed steps")
 
     # ---- instrumented pass: K eager steps with HIP events between kernels --
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(K):
-        step(sets[i % 2], evs[i])
+        rig.step(sets[i % 2], evs[i])
     torch.cuda.synchronize()
     wall_instr = time.perf_counter() - t1
+    rig.check("the instrumented steps")
     del graphs
-    step_scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    step_attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    step_dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    in_step = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3 for j in range(3)]
 
-    # ---- per-kernel pass: each kernel K times back to back between one pair
-    # of events (the event cost is amortised over K launches, so the mean
-    # launch time is comparable with a kernel trace) ------------------------
-    def run_scan(s):
-        c = s["cache"]
-        rat.rat_scan_prefill(s["k"], s["v"], s["g"], D, W, T_cap, c["Kc"], c["Vc"], c["state_k"],
-                             c["state_v"], s["ws"], hk=s["hk"], hv=s["hv"], k_ring=c["k_ring"],
-                             v_ring=c["v_ring"])
-
-    def run_attn(s):
-        c = s["cache"]
-        rat.rat_dilated_attn_prefill(s["q"], s["hk"], s["hv"], c["Kc"], c["Vc"], D, W, T_cap,
-                                     s["o"], s["lse"])
-
-    def run_dec(s):
-        c, d = s["cache"], s["dec"]
-        rat.rat_decode_step(d["q"], d["k"], d["v"], d["g"], c["state_k"], c["state_v"], c["Kc"],
-                            c["Vc"], c["k_ring"], c["v_ring"], s["do"], D, W, T, T_cap,
-                            workspace=s["dws"])
-
-    def kernel_ms(fn, spin, reps=3):
-        # fastest of a few passes: a one-time host stall while queueing (the
-        # runtime has shown one of about 40 ms) would otherwise land in the
-        # window of a single pass
-        return min(kernel_pass(fn, spin) for _ in range(reps))
-
-    def kernel_pass(fn, spin):
-        torch.cuda.synchronize()
-        # keep the GPU busy while the host queues the K launches: one untimed
-        # launch of the same kernel when a launch outlasts the host's enqueue
-        # time (scan, attention; the scan is persistent and sized to the whole
-        # device, so nothing else should run beside it), a device spin for
-        # the short decode step
-        if spin:
-            torch.cuda._sleep(max(SPIN_CYCLES, K * 150_000))
-        else:
-            fn(sets[1])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(K):
-            fn(sets[i % 2])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
-
-    scan_ms = [kernel_ms(run_scan, False)]
-    attn_ms = [kernel_ms(run_attn, False)]
-    dec_ms = [kernel_ms(run_dec, True)]
+    # ---- per-kernel pass: each kernel K times back to back ----------------
+    kernels = rig.kernels(K)
+    for name, us in zip(("scan", "attention", "decode_step"), in_step):
+        kernels[name]["us_in_step"] = us
     ms_per_step = wall * 1e3 / K
     tok = B * T
     value = tok / (ms_per_step / 1e3)
+    t_scan, t_attn = kernels["scan"]["us"], kernels["attention"]["us"]
 
-    sb, ab, af = scan_bytes(w, es), attn_bytes(w, es), attn_flops(w)
-    db = decode_bytes(B, H, hd, D, W, T, es)
-    t_scan = float(np.mean(scan_ms)) / 1e3
-    t_attn = float(np.mean(attn_ms)) / 1e3
-    t_dec = float(np.mean(dec_ms)) / 1e3
-    kernels = {
-        "scan": dict(us=t_scan * 1e6, bytes=sb, gbs=sb / t_scan / 1e9,
-                     us_in_step=float(np.mean(step_scan_ms)) * 1e3),
-        "attention": dict(us=t_attn * 1e6, bytes=ab, flops=af, gbs=ab / t_attn / 1e9,
-                          tflops=af / t_attn / 1e12,
-                          us_in_step=float(np.mean(step_attn_ms)) * 1e3),
-        "decode_step": dict(us=t_dec * 1e6, bytes=db, gbs=db / t_dec / 1e9,
-                            us_in_step=float(np.mean(step_dec_ms)) * 1e3),
-    }
+    # roofline of the kernel that takes the most time in the step
     dom = max(("scan", "attention"), key=lambda k: kernels[k]["us"])
-    if dom == "scan":
-        roof = dict(bound="hbm", achieved=kernels["scan"]["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    kernel="scan_kernel", traffic=traffic_from_profiles("scan.hip", f"scan_w{args.workload}"))
-    elif kernels["attention"]["tflops"] / MFMA_BF16_PEAK_TFLOPS > kernels["attention"]["gbs"] / HBM_PEAK_GBS:
-        # attention nearer its MFMA roof than its HBM roof: priced against the
-        # bf16 MFMA peak on its useful (dilated) FLOPs
-        roof = dict(bound="mfma", achieved=kernels["attention"]["tflops"], peak=MFMA_BF16_PEAK_TFLOPS,
-                    unit="TFLOP/s", kernel=attn_kernel_name(w), traffic=None)
-    else:
-        roof = dict(bound="hbm", achieved=kernels["attention"]["gbs"], peak=HBM_PEAK_GBS,
-                    unit="GB/s", kernel=attn_kernel_name(w),
-                    traffic=traffic_from_profiles("attn_prefill.hip", f"attn_w{args.workload}"))
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    kernels["attention"]["mfma_frac_useful"] = kernels["attention"]["tflops"] / MFMA_BF16_PEAK_TFLOPS
-    kernels["scan"]["hbm_frac"] = kernels["scan"]["gbs"] / HBM_PEAK_GBS
-    kernels["attention"]["hbm_frac"] = kernels["attention"]["gbs"] / HBM_PEAK_GBS
+    roof = dict(kernels[dom]["roofline"])
+    roof["kernel"] = kernels[dom]["kernel"]
+    roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel")}
+    headline = dict(workload=rig.describe(), tok_s_kernels=tok / ((t_scan + t_attn) * 1e-6),
+                    **{k: kernels[k] for k in ("scan", "attention")})
+    del rig, sets
+    torch.cuda.empty_cache()
+
+    # ---- the other prefill workloads: scan and attention per config --------
+    configs = {str(args.workload): headline}
+    for wid in args.configs:
+        if wid != args.workload:
+            configs[str(wid)] = bench_prefill_config(rat, synth, torch, wid, K)
 
     # ---- decode workload: µs per decode step ------------------------------
     decode_info = None
@@ -415,14 +502,13 @@ def main():
     chunked_info = None
     if not args.no_chunked:
         chunked_info = bench_chunked(rat, synth, torch, np)
+    side = synth.WORKLOADS[args.side_workload]
     backward_info = None
     if not args.no_backward:
-        backward_info = bench_backward(rat, synth, torch, np, w)
+        backward_info = bench_backward(rat, synth, torch, np, side)
     layer_info = None
     if not args.no_layer:
-        layer_info = bench_layer(rat, synth, torch, np, w)
-
-    del sets
+        layer_info = bench_layer(rat, synth, torch, np, side)
     torch.cuda.empty_cache()
 
     # ---- CPU oracle baseline (bounded sample of the same step) -----------
@@ -430,8 +516,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
 
-    line = {
-        "metric": "prefill tok/s + decode step µs per RAT+ layer; % of HBM / MFMA bf16 peak",
+    return {
+        "metric": METRIC,
         "value": value,
         "unit": "tok/s",
         "n_gpus": 1,
@@ -449,17 +535,17 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: B={B} H={H} hd={hd} T={T} D={head_list(D)} W={head_list(W)} "
-                        "(scan + dilated attention prefill + 1 decode step per step)",
-            "global_batch": B,
-            "seq_len": T,
+            "workload": f"{rig_name(w)} (scan + dilated attention prefill + 1 decode step per step)",
+            "global_batch": w.B,
+            "seq_len": w.T,
             "parallelism": "single GPU",
             "decode_workload": "decode: batch 64, H=32, hd=128, context 32768, D=64, W=128, "
                                "256 steps",
         },
-        "prefill_tok_s_kernels_only": tok / (t_scan + t_attn),
+        "prefill_tok_s_kernels_only": tok / ((t_scan + t_attn) * 1e-6),
         "decode_us_per_step": decode_info["us_mean"] if decode_info else None,
         "kernels": kernels,
+        "configs": configs,
         "decode_workload": decode_info,
         "topk_decode_workload": topk_info,
         "chunked_prefill": chunked_info,
@@ -468,7 +554,11 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line))
+
+
+def rig_name(w):
+    return (f"{w.name}: B={w.B} H={w.H} hd={w.hd} T={w.T} D={head_list(w.D)} "
+            f"W={head_list(w.W)}")
 
 
 def attn_kernel_name(w) -> str:
@@ -494,6 +584,9 @@ def bench_decode_workload(rat, synth, torch, np):
                              cache["state_v"][b:b + 1], ws, k_ring=cache["k_ring"][b:b + 1],
                              v_ring=cache["v_ring"][b:b + 1])
         del kvg
+    torch.cuda.synchronize()
+    if int(ws[2].item()) != 0:
+        raise ScanError("decode workload: a wait of a context scan timed out")
     inputs = [synth.decode_step_inputs(w, s) for s in range(steps)]
     outs = torch.empty((B, H, hd), dtype=torch.bfloat16, device="cuda")
     dws = rat.decode_workspace(B, H, hd, T_cap, D, W, "cuda")
@@ -545,6 +638,9 @@ def bench_topk_decode(rat, synth, torch, np, k_sel=8):
                                  hist["block_means"][b:b + 1])
         del kvg
     del hk, hv
+    torch.cuda.synchronize()
+    if int(ws[2].item()) != 0:
+        raise ScanError("top-k decode workload: a wait of a context scan timed out")
     inputs = [synth.decode_step_inputs(w, s) for s in range(steps)]
     outs = torch.empty((B, H, hd), dtype=st, device="cuda")
     torch.cuda.synchronize()
@@ -653,7 +749,8 @@ def bench_chunked(rat, synth, torch, np, reps=5, nchunks=4):
                us_chunked=med(tot_chunked), us_whole=med(tot_whole),
                tok_s_chunked=B * T / (med(tot_chunked) * 1e-6),
                tok_s_whole=B * T / (med(tot_whole) * 1e-6))
-    assert int(ws[2].item()) == 0 and int(ws_f[2].item()) == 0, "scan wait timed out"
+    if int(ws[2].item()) != 0 or int(ws_f[2].item()) != 0:
+        raise ScanError("chunked prefill: a scan wait timed out")
     del t, ch, c, rings, states, hk, hv, o, hk_f, hv_f, o_f
     torch.cuda.empty_cache()
     return res
@@ -676,6 +773,9 @@ def bench_backward(rat, synth, torch, np, w, reps=10):
     o = torch.empty_like(t["q"])
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
     rat.rat_dilated_attn_prefill(t["q"], hk, hv, c["Kc"], c["Vc"], D, W, T, o, lse)
+    torch.cuda.synchronize()
+    if int(ws[2].item()) != 0:
+        raise ScanError("backward: a wait of the forward scan timed out")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(w.seed + 99)
     dO = torch.randn(t["q"].shape, generator=gen, device="cuda").to(st)
@@ -744,6 +844,8 @@ def bench_layer(rat, synth, torch, np, w, reps=5):
         run()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
+    if int(ws[2].item()) != 0:  # the scan workspace heads the layer workspace
+        raise ScanError("layer: a scan wait timed out")
     us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
     med = us[reps // 2]
     gemm_flops = 5 * 2 * B * T * dm * dm
@@ -757,36 +859,63 @@ def bench_layer(rat, synth, torch, np, w, reps=5):
 
 
 def cpu_baseline(w, target_s):
-    """Time the CPU oracle (as it stands) on whole (batch row, head) slices of
-    the step's prefill workload until about target_s seconds of work or the
-    whole workload, and scale to tokens of the full layer."""
+    """Time the CPU oracle (as it stands) on whole (batch row, head)
+    sequences of the headline prefill workload: the scan and the dilated
+    attention of one head per thread, repeated over further heads until
+    about target_s seconds or the whole workload; then one head on a single
+    core.  Each time is scaled to tokens of the full workload by the
+    fraction of its attention FLOPs the sample did (heads differ in cost in
+    a hybrid)."""
     import numpy as np
     import oracle
     from dilated_sparse_attention_rat_amd import synth
     x = synth.prefill_inputs(w)
+    total = attn_flops(w)
+    flops_bh = {h: 4 * w.hd * keyset_total(w.T, w.D[h], w.W[h]) for h in range(w.H)}
+    # heads in descending cost, so each group of threads runs heads of equal cost
+    order = [(b, h) for b in range(w.B) for h in sorted(range(w.H), key=lambda h: -flops_bh[h])]
+
+    def run(pairs):
+        for b in sorted({b for b, _ in pairs}):
+            hs = [h for bb, h in pairs if bb == b]
+            f = {n: x[n][b:b + 1, hs].astype(np.float64) for n in "qkvg"}
+            oracle.prefill(f["q"], f["k"], f["v"], f["g"], [w.D[h] for h in hs],
+                           [w.W[h] for h in hs], w.scale, w.dtype == "bf16")
+
     nthr = max(1, oracle.num_threads())
-    done_bh = 0
-    spent = 0.0
-    for b in range(w.B):
-        f = {n: x[n][b:b + 1].astype(np.float64) for n in "qkvg"}
-        for h0 in range(0, w.H, nthr):
-            sl = slice(h0, min(w.H, h0 + nthr))
-            t0 = time.perf_counter()
-            oracle.prefill(f["q"][:, sl], f["k"][:, sl], f["v"][:, sl], f["g"][:, sl],
-                           list(w.D[sl]), list(w.W[sl]), w.scale, w.dtype == "bf16")
-            spent += time.perf_counter() - t0
-            done_bh += sl.stop - sl.start
-            if spent >= target_s:
-                break
-        if spent >= target_s:
-            break
-    frac = done_bh / (w.B * w.H)
-    tok_equiv = w.B * w.T * frac
-    return dict(value=tok_equiv / spent, unit="tok/s", cores=nthr, kind="oracle",
-                sample=f"oracle prefill (scan + attention, fp64, OpenMP over heads) of {done_bh} "
-                       f"of {w.B * w.H} (batch row, head) sequences at T={w.T}, {spent:.1f} s; "
-                       "tokens scaled by the fraction of sequences done",
+    done, spent, i = [], 0.0, 0
+    while i < len(order) and spent < target_s:
+        grp = order[i:i + nthr]
+        t0 = time.perf_counter()
+        run(grp)
+        spent += time.perf_counter() - t0
+        done += grp
+        i += nthr
+    frac = sum(flops_bh[h] for _, h in done) / total
+    value = w.B * w.T * frac / spent
+    # one core, one head of the lightest kind
+    one = [min(order, key=lambda bh: flops_bh[bh[1]])]
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        run(one)
+        s1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(nthr)
+    frac1 = flops_bh[one[0][1]] / total
+    heads = sorted({h for _, h in done})
+    return dict(value=value, unit="tok/s", cores=nthr, kind="oracle",
+                sample=f"oracle prefill (scan + attention, fp64, OpenMP over heads) of "
+                       f"{len(done)} of {w.B * w.H} (batch row, head) sequences at T={w.T} "
+                       f"(heads {head_list(heads) if len(heads) < 4 else f'{heads[0]}..{heads[-1]}'}), "
+                       f"{spent:.1f} s; tokens scaled by the fraction of the workload's attention "
+                       "FLOPs done",
                 seconds=spent, cpu_model=cpu_model(), nproc=os.cpu_count(),
+                single_core=dict(value=w.B * w.T * frac1 / s1, unit="tok/s", cores=1,
+                                 seconds=s1,
+                                 sample=f"one (batch row, head) sequence (head {one[0][1]}, "
+                                        f"D={w.D[one[0][1]]}) on one thread, scaled the same "
+                                        "way"),
                 topk_decode=cpu_topk_decode())
 
 

@@ -716,20 +716,22 @@ rocblas_handle blas_handle(int& err) {
   return h;
 }
 
-// layer workspace: q, k, v and the gate pre-activation token-major
-// [B,T,H,hd] (the projections' output), hk, hv [B,H,T,hd], o token-major
-// (all ST), then the scan workspace
+// layer workspace: the scan workspace first (its header, with the launch
+// epoch and the error word, then sits at offset 0 whatever the call's size,
+// so a buffer zeroed once serves calls of any size that fits), then q, k, v
+// and the gate pre-activation token-major [B,T,H,hd] (the projections'
+// output), hk, hv [B,H,T,hd] and o token-major (all ST)
 struct LayerLayout {
-  int64_t act = 0, off_scan = 0, scan_bytes = 0, bytes = 0;
+  int64_t act = 0, off_act = 0, scan_bytes = 0, bytes = 0;
 };
 
 bool layer_layout(int dtype, int B, int H, int64_t T, int hd, LayerLayout& L) {
   const int64_t es = dtype == RAT_DTYPE_BF16 ? 2 : 4;
   L.act = ((int64_t)B * H * T * hd * es + 255) / 256 * 256;
-  L.off_scan = 7 * L.act;
   L.scan_bytes = rat_scan_workspace_bytes(B, H, T, hd);
   if (L.scan_bytes < 0) return false;
-  L.bytes = L.off_scan + L.scan_bytes;
+  L.off_act = (L.scan_bytes + 255) / 256 * 256;
+  L.bytes = L.off_act + 7 * L.act;
   return true;
 }
 
@@ -768,13 +770,14 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const 
   if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < L.bytes)
     return RAT_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  void* q = ws;
-  void* k = ws + L.act;
-  void* v = ws + 2 * L.act;
-  void* g = ws + 3 * L.act;
-  void* hk = ws + 4 * L.act;
-  void* hv = ws + 5 * L.act;
-  void* o = ws + 6 * L.act;
+  char* act = ws + L.off_act;
+  void* q = act;
+  void* k = act + L.act;
+  void* v = act + 2 * L.act;
+  void* g = act + 3 * L.act;
+  void* hk = act + 4 * L.act;
+  void* hv = act + 5 * L.act;
+  void* o = act + 6 * L.act;
   int herr;
   rocblas_handle hb = blas_handle(herr);
   if (herr != RAT_OK) return herr;
@@ -800,7 +803,7 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const 
   }
   // recurrence with the gate sigmoid(g + b_g) fused into its loads
   st = scan_impl(dtype, B, H, T, hd, D, W, T_cap, 0, k, v, g, nullptr, nullptr, hk, hv, Kc, Vc,
-                 nullptr, nullptr, k_ring, v_ring, state_k, state_v, ws + L.off_scan,
+                 nullptr, nullptr, k_ring, v_ring, state_k, state_v, ws,
                  (size_t)L.scan_bytes, stream, b_g, true);
   if (st != RAT_OK) return st;
   // dilated attention; o written token-major for the output projection

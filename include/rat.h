@@ -99,7 +99,10 @@ int64_t rat_ring_rows(int H, const int32_t* W, int64_t* offsets_out);
  * word 0: launch epoch; word 2: error word; then completion counters), the
  * rest holds the tagged chunk aggregates.  The error word is != 0 after a
  * call in which a chunk gave up waiting for a predecessor's aggregate (the
- * results of that call are invalid).  The scan kernel is persistent: its
+ * results of that call are invalid).  It is sticky: no later call clears
+ * it, so a non-zero word means some call since the workspace was last
+ * zero-filled failed; a caller that finds it set discards those results and
+ * zero-fills the whole workspace before its next use.  The scan kernel is persistent: its
  * grid never exceeds what the device holds at once, and with the device to
  * itself every workgroup is resident immediately; if other streams keep CUs
  * busy past the (bounded) wait, the call reports it here instead of
@@ -336,8 +339,10 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd,
 
 /*
  * Bytes of device workspace rat_layer_prefill needs.  Zero-fill it once
- * before its first use (it holds a scan workspace); afterwards it is ready
- * for every later call.  Pure host function; bytes (> 0) or a negative code.
+ * before its first use (it starts with a scan workspace, at offset 0 for
+ * every size, so its error word is uint32 word 2 of the buffer); afterwards
+ * it is ready for every later call, of this size or smaller.  Pure host
+ * function; bytes (> 0) or a negative code.
  */
 int64_t rat_layer_workspace_bytes(int dtype, int B, int H, int64_t T, int hd);
 
@@ -361,8 +366,8 @@ int64_t rat_layer_workspace_bytes(int dtype, int B, int H, int64_t T, int hd);
  * rocBLAS handle there (kept until the process ends), and rocBLAS manages
  * its own device memory.  Calls from several host threads are safe (the
  * handle's stream is set under a lock).
- * workspace: rat_layer_workspace_bytes bytes (q, k, v, the gate
- * pre-activation, the states and o, then a scan workspace).
+ * workspace: rat_layer_workspace_bytes bytes (a scan workspace, then q, k,
+ * v, the gate pre-activation, the states and o).
  */
 int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm,
                       const int32_t* D, const int32_t* W, float scale,

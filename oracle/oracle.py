@@ -64,6 +64,7 @@ def load(path: str) -> ctypes.CDLL:
     L.rat_oracle_backward.argtypes = [i32, i32, i32, i32, P, P, f64, P, P, P,
                                       P, P, i32, P, P, P, P]
     L.rat_oracle_num_threads.restype = i32
+    L.rat_oracle_set_threads.argtypes = [i32]
     return L
 
 
@@ -107,6 +108,11 @@ def _p(a):
 
 def num_threads() -> int:
     return int(lib().rat_oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's loops over (b, h) from here on (timing only)."""
+    lib().rat_oracle_set_threads(int(n))
 
 
 def round_bf16(x) -> np.ndarray:

@@ -294,6 +294,17 @@ int rat_oracle_num_threads(void) {
 #endif
 }
 
+/* Threads used by the parallel loops over (b, h) from here on (timing of the
+   baseline on one core; the results do not depend on it). */
+void rat_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ */
 /* Backward of the prefill (reverse-mode derivative of the definitions  */
 /* above), for a loss L whose gradient with respect to o is dO.  The    */

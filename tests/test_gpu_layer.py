@@ -85,7 +85,48 @@ def test_layer_matches_oracle(case):
         chk(check_rel, "lse", to_np(lse), ref["lse"], dtype)
         chk(check_rel, "state_k", to_np(cache["state_k"]), ref["state_k"], dtype)
         chk(check_rel, "state_v", to_np(cache["state_v"]), ref["state_v"], dtype)
+        assert int(ws[2].item()) == 0, "scan workspace reports a timed-out wait"
         chk.done()
+
+
+def test_layer_workspace_reused_at_smaller_sizes():
+    """One layer workspace, zeroed once, serves a call and then calls at a
+    smaller T and a smaller B: the scan workspace heads it at a fixed
+    offset, so its epoch and completion counters stay valid across sizes."""
+    import dilated_sparse_attention_rat_amd as rat
+    H, hd, dm = 3, 128, 256
+    D, W = np.array([4, 1, 16], np.int32), np.array([0, 37, 3], np.int32)
+    rng = np.random.default_rng(77)
+    HD = H * hd
+
+    def r(shape, std):
+        return oracle.round_bf16((rng.standard_normal(shape) * std).astype(np.float32)).astype(np.float32)
+
+    wq, wk, wv = (r((dm, HD), hd ** -0.5 / np.sqrt(dm)) for _ in range(3))
+    wg = r((dm, HD), 1.0 / np.sqrt(dm))
+    bg = np.full(HD, 3.0, np.float32)
+    wo = r((HD, dm), 1.0 / np.sqrt(HD))
+    dev = lambda a: to_dev(a, "bf16")
+    ws = rat.layer_workspace(rat.binding._dtype_code(torch.empty(0, dtype=torch.bfloat16)), 2, H,
+                             600, hd, "cuda")
+    chk = Checks()
+    for B, T in ((2, 600), (2, 257), (1, 600), (1, 90)):
+        say(f"[layer] workspace reuse: B={B} T={T}")
+        x = r((B, T, dm), 1.0)
+        cache = rat.alloc_cache(B, H, hd, T, D, W, torch.bfloat16, "cuda")
+        out = torch.empty((B, T, dm), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+        rat.rat_layer_prefill(dev(x), dev(wq), dev(wk), dev(wv), dev(wg),
+                              torch.from_numpy(bg).cuda(), dev(wo), out, D, W, H, hd, T, cache, ws,
+                              lse=lse)
+        torch.cuda.synchronize()
+        assert int(ws[2].item()) == 0, "scan workspace reports a timed-out wait"
+        ref = oracle.layer_prefill(x, wq, wk, wv, wg, bg, wo, H, hd, D, W, hd ** -0.5, True)
+        chk(check_rel, "out", to_np(out), ref["out"], "bf16")
+        chk(check_rel, "lse", to_np(lse), ref["lse"], "bf16")
+        chk(check_rel, "state_k", to_np(cache["state_k"]), ref["state_k"], "bf16")
+        chk(check_rel, "state_v", to_np(cache["state_v"]), ref["state_v"], "bf16")
+    chk.done()
 
 
 def test_layer_workload_size_sampled():
