@@ -32,13 +32,14 @@ EXPORTED = [
     "rat_version", "rat_status_string", "rat_anchor_rows", "rat_ring_rows",
     "rat_scan_workspace_bytes", "rat_scan_prefill", "rat_dilated_attn_prefill",
     "rat_scan_prefill_continue", "rat_dilated_attn_prefill_continue",
-    "rat_decode_workspace_bytes", "rat_decode_step",
+    "rat_decode_workspace_bytes", "rat_decode_step", "rat_decode_step_noalloc",
     "rat_prefill_backward_workspace_bytes", "rat_prefill_backward",
     "rat_layer_workspace_bytes", "rat_layer_prefill",
     "rat_topk_cache_build", "rat_decode_step_topk",
 ]
 
 TOPK_BLOCK = 64   # RAT_TOPK_BLOCK
+NOALLOC_SCRATCH_BYTES = 16 << 20  # RAT_NOALLOC_SCRATCH_BYTES
 TOPK_MAX_K = 64   # RAT_TOPK_MAX_K
 
 
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
                                       P, P, P, P, P, P, P, P, P, P, P, i32, P,
                                       sz, P]
         L.rat_decode_step.restype = i32
+        L.rat_decode_step_noalloc.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64] + [P] * 11 + [i32, P]
+        L.rat_decode_step_noalloc.restype = i32
         L.rat_topk_cache_build.argtypes = [i32, i32, i32, i64, i32, i64, i64, P, P, P, P, P, P]
         L.rat_topk_cache_build.restype = i32
         L.rat_decode_step_topk.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64, i32] + [P] * 16
@@ -360,6 +363,31 @@ def rat_decode_step(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, o,
         _stream(stream, dev),
     ]
     _check("rat_decode_step", lib().rat_decode_step(*args))
+
+
+def rat_decode_step_noalloc(q, k, v, g, state_k, state_v, Kc, Vc, k_ring, v_ring, o,
+                            D, W, pos: int, T_cap: int, scale: float = 0.0,
+                            num_splits: int = 0, stream=None):
+    """rat_decode_step with the split-K partials in the library's own device
+    array (no workspace argument; calls on one device must not overlap)."""
+    torch = _torch()
+    B, H, hd = q.shape
+    st = q.dtype
+    dev = q.device
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    R, _ = rat_anchor_rows(H, T_cap, Dh)
+    WS, _ = rat_ring_rows(H, Wh)
+    args = [
+        _dtype_code(q), B, H, hd, _ptr(Dh), _ptr(Wh), float(scale), pos, T_cap,
+        _dev(q, "q", (B, H, hd), st, dev), _dev(k, "k", (B, H, hd), st, dev),
+        _dev(v, "v", (B, H, hd), st, dev), _dev(g, "g", (B, H, hd), st, dev),
+        _dev(state_k, "state_k", (B, H, hd), torch.float32, dev),
+        _dev(state_v, "state_v", (B, H, hd), torch.float32, dev),
+        _opt(Kc, "Kc", (B, R, hd), st, dev), _opt(Vc, "Vc", (B, R, hd), st, dev),
+        _opt(k_ring, "k_ring", (B, WS, hd), st, dev), _opt(v_ring, "v_ring", (B, WS, hd), st, dev),
+        _dev(o, "o", (B, H, hd), st, dev), int(num_splits), _stream(stream, dev),
+    ]
+    _check("rat_decode_step_noalloc", lib().rat_decode_step_noalloc(*args))
 
 
 def rat_topk_cache_build(hk, hv, hk_hist, hv_hist, block_means, t0: int = 0, stream=None):

@@ -408,11 +408,73 @@ int64_t rat_decode_workspace_bytes(int B, int H, int hd, int64_t T_cap, const in
   return (int64_t)B * H * s * (hd + 2) * 4;
 }
 
+}  // extern "C"
+
+namespace {
+// The decode step of rat_decode_step and rat_decode_step_noalloc.  With
+// scratch set, the split-K partials go to the library's own device array
+// (workspace, workspace_bytes: its address on this device and its size).
+int decode_impl(int dtype, int B, int H, int hd, const int32_t* D, const int32_t* W, float scale,
+                int64_t pos, int64_t T_cap, const void* q, const void* k, const void* v,
+                const void* g, float* state_k, float* state_v, void* Kc, void* Vc, void* k_ring,
+                void* v_ring, void* o, int num_splits, void* workspace, size_t workspace_bytes,
+                void* stream, bool scratch);
+}  // namespace
+
+extern "C" {
+
 int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D, const int32_t* W,
                     float scale, int64_t pos, int64_t T_cap, const void* q, const void* k,
                     const void* v, const void* g, float* state_k, float* state_v, void* Kc,
                     void* Vc, void* k_ring, void* v_ring, void* o, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(dtype, B, H, hd, D, W, scale, pos, T_cap, q, k, v, g, state_k, state_v, Kc,
+                     Vc, k_ring, v_ring, o, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+int rat_decode_step_noalloc(int dtype, int B, int H, int hd, const int32_t* D, const int32_t* W,
+                            float scale, int64_t pos, int64_t T_cap, const void* q,
+                            const void* k, const void* v, const void* g, float* state_k,
+                            float* state_v, void* Kc, void* Vc, void* k_ring, void* v_ring,
+                            void* o, int num_splits, void* stream) {
+  return decode_impl(dtype, B, H, hd, D, W, scale, pos, T_cap, q, k, v, g, state_k, state_v, Kc,
+                     Vc, k_ring, v_ring, o, num_splits, nullptr, 0, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Split-K partials of rat_decode_step_noalloc: one array per device, kept
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a handle); its device address comes from
+// hipGetSymbolAddress, once per device.
+__device__ __align__(256) float scratch[RAT_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RAT_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RAT_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return RAT_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return RAT_OK;
+}
+
+int decode_impl(int dtype, int B, int H, int hd, const int32_t* D, const int32_t* W, float scale,
+                int64_t pos, int64_t T_cap, const void* q, const void* k, const void* v,
+                const void* g, float* state_k, float* state_v, void* Kc, void* Vc, void* k_ring,
+                void* v_ring, void* o, int num_splits, void* workspace, size_t workspace_bytes,
+                void* stream, bool scratch) {
   int st = check_common(dtype, B, H, hd, D, W);
   if (st != RAT_OK) return st;
   if (T_cap < 0 || T_cap > kMaxT || pos < 0 || num_splits < 0 || num_splits > 1024)
@@ -433,6 +495,12 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D, const int
   const int s = decode_splits(B, H, T_cap, D, W, num_splits);
   if (s > 1) {
     const int64_t need = (int64_t)B * H * s * (hd + 2) * 4;
+    if (scratch) {
+      if (need > (int64_t)RAT_NOALLOC_SCRATCH_BYTES) return RAT_ERR_WORKSPACE;
+      st = scratch_address(&workspace);
+      if (st != RAT_OK) return st;
+      workspace_bytes = RAT_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || !aligned16(workspace) || (int64_t)workspace_bytes < need)
       return RAT_ERR_WORKSPACE;
   }
@@ -457,6 +525,10 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D, const int
   p.part = static_cast<float*>(workspace);
   return map_hip(launch_decode(dtype, hd, p, stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 int rat_topk_cache_build(int dtype, int B, int H, int64_t T, int hd, int64_t T_cap,
                          int64_t t0, const void* hk, const void* hv, void* hk_hist,

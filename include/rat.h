@@ -247,6 +247,29 @@ int rat_decode_step(int dtype, int B, int H, int hd, const int32_t* D,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * rat_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, semantics and results as
+ * rat_decode_step (same kernels, same split choice).  The split-K partials
+ * go to a device array of RAT_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every device it runs on, from its first use there until the process
+ * ends; the call itself allocates nothing.  A call whose partials would not
+ * fit, B*H*splits*(hd+2)*4 > RAT_NOALLOC_SCRATCH_BYTES, returns
+ * RAT_ERR_WORKSPACE and launches nothing.  All calls on one device share
+ * that array: two calls that can run at the same time on one device (other
+ * streams, other threads) race and must not overlap.  The array needs no
+ * clearing (every partial is written before it is read).
+ */
+#define RAT_NOALLOC_SCRATCH_BYTES (16u << 20)
+int rat_decode_step_noalloc(int dtype, int B, int H, int hd, const int32_t* D,
+                            const int32_t* W, float scale, int64_t pos,
+                            int64_t T_cap, const void* q, const void* k,
+                            const void* v, const void* g, float* state_k,
+                            float* state_v, void* Kc, void* Vc, void* k_ring,
+                            void* v_ring, void* o, int num_splits,
+                            void* stream);
+
+/*
  * Decode combined with top-k block selection (RAT+ abstract, v1: RAT+
  * sparsified to top-k block attention; deep dive, section 四: dilation and
  * top-k block selection combine, the anchors covering the whole past and the

@@ -254,6 +254,25 @@ def test_decode_validation(L):
     assert _dec(L, B=0) == rb.RAT_OK
 
 
+def test_decode_noalloc_validation(L):
+    """The no-allocation decode validates like rat_decode_step and rejects
+    split-K partials beyond its device array before anything is launched."""
+    def dec(dtype=0, B=1, H=2, hd=64, pos=5, T_cap=16, splits=0, q=FAKE):
+        d, w, dp, wp = _tables(H, 4, 0)
+        return L.rat_decode_step_noalloc(dtype, B, H, hd, dp, wp, 0.0, pos, T_cap, _p(q), _p(),
+                                         _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(),
+                                         splits, None)
+
+    assert dec(pos=16, T_cap=16) == rb.RAT_ERR_CAPACITY
+    assert dec(dtype=9) == rb.RAT_ERR_UNSUPPORTED
+    assert dec(q=0) == rb.RAT_ERR_INVALID_ARG
+    assert dec(splits=-2) == rb.RAT_ERR_INVALID_ARG
+    # 64 * 64 (b, h) x 64 splits x (128 + 2) fp32 = 136 MB > the 16 MiB array
+    assert 64 * 64 * 64 * 130 * 4 > rb.NOALLOC_SCRATCH_BYTES
+    assert dec(B=64, H=64, hd=128, T_cap=1 << 16, splits=64) == rb.RAT_ERR_WORKSPACE
+    assert dec(B=0) == rb.RAT_OK
+
+
 def _tk_build(L, dtype=0, B=1, H=2, T=64, hd=64, T_cap=128, t0=0, ptr=FAKE, means=FAKE):
     return L.rat_topk_cache_build(dtype, B, H, T, hd, T_cap, t0, _p(ptr), _p(ptr), _p(ptr),
                                   _p(ptr), _p(means) if means else None, None)
