@@ -59,16 +59,14 @@ int fill_tables(int H, int64_t T_cap, const int32_t* D, const int32_t* W, HeadTa
 int map_hip(int e) { return e == 0 ? RAT_OK : RAT_ERR_HIP; }
 
 // Workspace of the scan: header, then per tree node an aggregate (A, Bk, Bv:
-// 3*hd values, each a 64-bit tagged word), then per chunk a slot for the k
-// and v states after it (2*hd tagged words; written for the last chunk of
-// each block).  Level l has ceil(nchunk / 8^l) nodes per sequence; levels
-// are added until the top one has at most 8 nodes.
+// 3*hd values, each a 64-bit tagged word).  Level l has ceil(nchunk / 8^l) nodes per
+// sequence; levels are added until the top one has at most 8 nodes.
 struct ScanLayout {
   int64_t nchunk = 0, nticket = 0, entries = 0;
   int nlevels = 0;
   int nodes[kScanMaxLevels] = {};
   int64_t lbase[kScanMaxLevels] = {};
-  int64_t agg_off = 0, incl_off = 0, bytes = 0;
+  int64_t agg_off = 0, bytes = 0;
 };
 
 bool scan_layout(int B, int H, int64_t T, int hd, int dtype, ScanLayout& L) {
@@ -89,9 +87,7 @@ bool scan_layout(int B, int H, int64_t T, int hd, int dtype, ScanLayout& L) {
   }
   auto up = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
   L.agg_off = kScanHeaderBytes;
-  // block states: one slot per chunk (the block size is chosen at launch)
-  L.incl_off = up(L.agg_off + L.entries * 3 * hd * 8);
-  L.bytes = up(L.incl_off + (int64_t)B * H * L.nchunk * 2 * hd * 8);
+  L.bytes = up(L.agg_off + L.entries * 3 * hd * 8);
   return true;
 }
 
@@ -190,7 +186,6 @@ int scan_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
     char* ws = static_cast<char*>(workspace);
     p.hdr = reinterpret_cast<uint32_t*>(ws);
     p.agg = reinterpret_cast<uint64_t*>(ws + L.agg_off);
-    p.incl = reinterpret_cast<uint64_t*>(ws + L.incl_off);
     p.nticket = (int)L.nticket;
     p.nchunk = (int)L.nchunk;
     p.nlevels = L.nlevels;

@@ -56,11 +56,6 @@ struct ScanParams {
                                 // ([B,H,T,hd]: H*T*hd, T*hd, hd)
   uint32_t* hdr;    // workspace header (kScanHeaderBytes)
   uint64_t* agg;    // [entries][3][hd]: (tag << 32 | fp32) of A, Bk, Bv
-  uint64_t* incl;   // [nseq][nchunk][2][hd]: (tag << 32 | fp32) of the k and v
-                    // states after the last chunk of a block
-  int mblk;         // chunks of one sequence per block (a power of two); the
-                    // launch's rounds of G tickets hold whole blocks
-  int blk_levels;   // tree levels inside a block: those with 8^l < mblk
   HeadTables ht;
 };
 

@@ -151,61 +151,6 @@ __device__ __forceinline__ void fold_nodes(const ScanParams& p, int64_t e0, int 
   }
 }
 
-// The carry-in of a chunk: the state st (2*HD tagged words, the k and v
-// states after the previous block; nullptr: keep the running state) and
-// then the n (< radix) consecutive nodes [e0, e0 + n) composed onto the
-// running state (Bk, Bv) of one channel, all loaded in one batch and
-// re-loaded until every tag in the wave is current; every wait is bounded.
-template <int HD>
-__device__ __forceinline__ void fold_state_nodes(const ScanParams& p, const uint64_t* st,
-                                                 int64_t e0, int n, int half, float& Bk,
-                                                 float& Bv, uint32_t tag, int lane) {
-  if (n <= 0 && st == nullptr) return;
-  uint64_t w[kScanRadix - 1][3];
-  uint64_t sw[2] = {0, 0};
-  uint32_t spins = 0;
-  while (true) {
-    bool ok = true;
-    if (st != nullptr) {
-      sw[0] = ld_tagged(st + 64 * half + lane);
-      sw[1] = ld_tagged(st + HD + 64 * half + lane);
-    }
-#pragma unroll
-    for (int i = 0; i < kScanRadix - 1; ++i) {
-      if (i < n) {
-        const uint64_t* d = p.agg + (e0 + i) * 3 * HD + 64 * half + lane;
-        w[i][0] = ld_tagged(d);
-        w[i][1] = ld_tagged(d + HD);
-        w[i][2] = ld_tagged(d + 2 * HD);
-      }
-    }
-    if (st != nullptr) ok = (uint32_t)(sw[0] >> 32) == tag && (uint32_t)(sw[1] >> 32) == tag;
-#pragma unroll
-    for (int i = 0; i < kScanRadix - 1; ++i)
-      if (i < n)
-        ok = ok && (uint32_t)(w[i][0] >> 32) == tag && (uint32_t)(w[i][1] >> 32) == tag &&
-             (uint32_t)(w[i][2] >> 32) == tag;
-    if (__all(ok)) break;
-    if (++spins > kSpinLimit) {
-      if (lane == 0) st_relaxed_u32(p.hdr + kErrorWord, 1u);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  if (st != nullptr) {
-    Bk = __uint_as_float((uint32_t)sw[0]);
-    Bv = __uint_as_float((uint32_t)sw[1]);
-  }
-#pragma unroll
-  for (int i = 0; i < kScanRadix - 1; ++i) {
-    if (i < n) {
-      const float a = __uint_as_float((uint32_t)w[i][0]);
-      Bk = a * Bk + __uint_as_float((uint32_t)w[i][1]);
-      Bv = a * Bv + __uint_as_float((uint32_t)w[i][2]);
-    }
-  }
-}
-
 template <typename ST, int HD, int S>
 struct ChunkRows {
   u32x4 k[S], v[S], g[S];
@@ -240,133 +185,113 @@ __device__ __forceinline__ void load_rows(const ScanParams& p, uint32_t ticket,
   }
 }
 
-// The gate of one row: g itself, or (GATE) sigmoid(g + bias) with g the
-// gate's pre-activation and the head's per-channel bias.
-template <int VEC, bool GATE>
-__device__ __forceinline__ void apply_gate(float (&gf)[VEC], const float (&gbias)[VEC]) {
-  if constexpr (GATE) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i)
-      gf[i] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(gf[i] + gbias[i]) * kLog2e));
-  }
-}
-
-template <typename ST, int HD, bool GATE>
-__device__ __forceinline__ void load_gate_bias(const ScanParams& p, int h, int c0,
-                                               float (&gbias)[StTraits<ST>::VEC]) {
-  if constexpr (GATE) {
-#pragma unroll
-    for (int i = 0; i < StTraits<ST>::VEC; ++i) gbias[i] = p.gate_bias[h * HD + c0 + i];
-  }
-}
-
-// Row-group maps of one chunk in LDS: one set per chunk in flight.
-template <int RG, int HD>
-struct PrefixSet {
-  float A[RG][HD];
-  float Bk[RG][HD];
-  float Bv[RG][HD];
-  float tot[3][HD];  // the whole chunk's map (A, Bk, Bv)
-};
-
-// Phase A of the pipeline.  Pass 1 of ticket tn (rows rn): each lane reduces
-// its rows to an affine map, the row-groups' maps go to LDS set `sn`, then
-//  * waves 0..NH-1 scan the row-groups of set sn (exclusive prefix, kept for
-//    pass 2) and publish the chunk's aggregate and, for the owner of a node's
-//    last child, the node;
-//  * waves 2..2+NH-1 compose, concurrently, the carry-in of ticket tc (the
-//    chunk whose pass 2 follows) into s_hk / s_hv.
-// Publication never waits on a carry, so no chain forms along the sequence:
-// every tree node depends on input data only.  The carry is the in-order
-// composition, top tree level first, of the complete nodes that precede the
-// chunk (at most radix-1 per level): a fixed order, so the result is bitwise
-// deterministic.  Ticket tc was published one pipeline step earlier than its
-// carry is composed, and so were the chunks of its round before it, so the
-// carry's loads normally find every node already there.
-template <typename ST, int HD, int S, bool GATE>
-__device__ __forceinline__ void scan_phase_a(const ScanParams& p, uint32_t tag, bool pub,
-                                             uint32_t tn, const ChunkRows<ST, HD, S>& rn,
-                                             PrefixSet<kScanThreads / (HD / StTraits<ST>::VEC), HD>& sn,
-                                             bool carry, uint32_t tc,
-                                             const PrefixSet<kScanThreads / (HD / StTraits<ST>::VEC), HD>& sc,
-                                             float* s_hk, float* s_hv) {
+// One chunk: pass 1, tree publication and carry, then pass 2.  `between`
+// runs after the carry is known and before pass 2: the caller issues the
+// next chunk's loads there, so that no tree load waits behind them (vector
+// memory counters complete in order) while pass 2 still overlaps them.
+template <typename ST, int HD, int S, bool GATE, typename F>
+__device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket, uint32_t tag,
+                                           const ChunkRows<ST, HD, S>& rw, float (*s_A)[HD],
+                                           float (*s_Bk)[HD], float (*s_Bv)[HD], float* s_hk,
+                                           float* s_hv, F&& between) {
   constexpr int VEC = StTraits<ST>::VEC;
   constexpr int LPR = HD / VEC;           // lanes per row
   constexpr int RG = kScanThreads / LPR;  // row-groups per chunk
   constexpr int LC = RG * S;              // rows per chunk
-  constexpr int NH = HD / 64;             // channel halves
   const int tid = threadIdx.x;
+  const int chunk = (int)(ticket / (uint32_t)p.nseq);
+  const int seq = (int)(ticket % (uint32_t)p.nseq);
+  const int b = seq / p.H;
+  const int h = seq - b * p.H;
+  const int T = p.T;
   const int r = tid / LPR;
-  const int c0 = (tid - r * LPR) * VEC;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-
-  if (pub) {
-    const int chunk = (int)(tn / (uint32_t)p.nseq);
-    const int seq = (int)(tn % (uint32_t)p.nseq);
-    const int h = seq % p.H;
-    const int tbase = chunk * LC + r * S;
-    float gbias[VEC];
-    load_gate_bias<ST, HD, GATE>(p, h, c0, gbias);
-    float A[VEC], Bk[VEC], Bv[VEC];
+  const int cl = tid - r * LPR;
+  const int c0 = cl * VEC;
+  const int tbase = chunk * LC + r * S;
+  const int64_t seq_base = (int64_t)seq * T * HD;
+  const u32x4* rk = rw.k;
+  const u32x4* rv = rw.v;
+  const u32x4* rg = rw.g;
+  // GATE: g holds the gate's pre-activation; the gate is sigmoid(g + bias)
+  // with the head's per-channel bias (fused here instead of a separate pass)
+  float gbias[VEC];
+  if constexpr (GATE) {
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      A[i] = 1.f;
-      Bk[i] = 0.f;
-      Bv[i] = 0.f;
+    for (int i = 0; i < VEC; ++i) gbias[i] = p.gate_bias[h * HD + c0 + i];
+  }
+  auto gate = [&](float (&gf)[VEC]) {
+    if constexpr (GATE) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i)
+        gf[i] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(gf[i] + gbias[i]) * kLog2e));
     }
+  };
+
+  // ---- pass 1: affine map of this lane's rows ----------------------------
+  float A[VEC], Bk[VEC], Bv[VEC];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (tbase + s < p.T) {
-        float gf[VEC], kf[VEC], vf[VEC];
-        unpack16(rn.g[s], gf, (ST*)nullptr);
-        apply_gate<VEC, GATE>(gf, gbias);
-        unpack16(rn.k[s], kf, (ST*)nullptr);
-        unpack16(rn.v[s], vf, (ST*)nullptr);
+  for (int i = 0; i < VEC; ++i) {
+    A[i] = 1.f;
+    Bk[i] = 0.f;
+    Bv[i] = 0.f;
+  }
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          A[i] *= gf[i];
-          Bk[i] = gf[i] * Bk[i] + (1.f - gf[i]) * kf[i];
-          Bv[i] = gf[i] * Bv[i] + (1.f - gf[i]) * vf[i];
-        }
+  for (int s = 0; s < S; ++s) {
+    const int t = tbase + s;
+    if (t < T) {
+      float gf[VEC], kf[VEC], vf[VEC];
+      unpack16(rg[s], gf, (ST*)nullptr);
+      gate(gf);
+      unpack16(rk[s], kf, (ST*)nullptr);
+      unpack16(rv[s], vf, (ST*)nullptr);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        A[i] *= gf[i];
+        Bk[i] = gf[i] * Bk[i] + (1.f - gf[i]) * kf[i];
+        Bv[i] = gf[i] * Bv[i] + (1.f - gf[i]) * vf[i];
       }
     }
+  }
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      sn.A[r][c0 + i] = A[i];
-      sn.Bk[r][c0 + i] = Bk[i];
-      sn.Bv[r][c0 + i] = Bv[i];
-    }
+  for (int i = 0; i < VEC; ++i) {
+    s_A[r][c0 + i] = A[i];
+    s_Bk[r][c0 + i] = Bk[i];
+    s_Bv[r][c0 + i] = Bv[i];
   }
   __syncthreads();
 
-  if (wave < NH) {
-    if (pub) {
-      const int chunk = (int)(tn / (uint32_t)p.nseq);
-      const int seq = (int)(tn % (uint32_t)p.nseq);
+  // ---- waves 0..NH-1: row-group scan of half j, publish chunk and parents -
+  // ---- waves 2..2+NH-1, concurrently: carry-in of half j -------------------
+  // Publication never waits on a carry, so no chain forms along the
+  // sequence: every tree node depends on input data only.  The carry is the
+  // in-order composition, top tree level first, of the complete nodes that
+  // precede this chunk (at most radix-1 per level): a fixed order, so the
+  // result is bitwise deterministic.
+  {
+    constexpr int NH = HD / 64;  // channel halves
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    if (wave < NH) {
       const int half = wave;
       const int c = 64 * half + lane;
       float ra = 1.f, rbk = 0.f, rbv = 0.f;
       for (int rr = 0; rr < RG; ++rr) {
-        const float a = sn.A[rr][c], bk = sn.Bk[rr][c], bv = sn.Bv[rr][c];
-        sn.A[rr][c] = ra;  // exclusive prefix of the row-groups
-        sn.Bk[rr][c] = rbk;
-        sn.Bv[rr][c] = rbv;
+        const float a = s_A[rr][c], bk = s_Bk[rr][c], bv = s_Bv[rr][c];
+        s_A[rr][c] = ra;  // exclusive prefix of the row-groups
+        s_Bk[rr][c] = rbk;
+        s_Bv[rr][c] = rbv;
         rbk = a * rbk + bk;
         rbv = a * rbv + bv;
         ra = ra * a;
       }
-      sn.tot[0][c] = ra;
-      sn.tot[1][c] = rbk;
-      sn.tot[2][c] = rbv;
       // A node of level l+1 is the in-order composition of its radix
       // children; the chunk that owns the last child computes and publishes
-      // it.  Only the levels a carry inside a block folds are published.
+      // it.
       int64_t node = chunk;
-      for (int lv = 0; lv < p.blk_levels; ++lv) {
+      for (int lv = 0; lv < p.nlevels; ++lv) {
         const int64_t lvl0 = p.lbase[lv] + (int64_t)seq * p.nodes[lv];
         publish_node<HD>(p, lvl0 + node, half, ra, rbk, rbv, tag, lane);
-        if (lv + 1 >= p.blk_levels || (node % kScanRadix) != kScanRadix - 1) break;
+        if (lv + 1 >= p.nlevels || (node % kScanRadix) != kScanRadix - 1) break;
         float fA = 1.f, fBk = 0.f, fBv = 0.f;
         fold_nodes<HD>(p, lvl0 + node - (kScanRadix - 1), kScanRadix - 1, half, fA, fBk, fBv,
                        tag, lane);
@@ -375,157 +300,104 @@ __device__ __forceinline__ void scan_phase_a(const ScanParams& p, uint32_t tag, 
         ra = fA * ra;
         node /= kScanRadix;
       }
-    }
-  } else if (wave >= 2 && wave < 2 + NH) {
-    if (carry) {
-      const int chunk = (int)(tc / (uint32_t)p.nseq);
-      const int seq = (int)(tc % (uint32_t)p.nseq);
+    } else if (wave >= 2 && wave < 2 + NH) {
       const int half = wave - 2;
-      const int c = 64 * half + lane;
-      // The carry-in of chunk `chunk` of block kb: the state after block
-      // kb-1 (for kb = 0 the state before row 0: zero for a prefill, the
-      // given state for a continuation), then the tree nodes that cover
-      // the block's chunks before this one, top level first.
-      const int kb = chunk / p.mblk;
-      const int bs = kb * p.mblk;
-      float hin_k = 0.f, hin_v = 0.f;
-      const uint64_t* st = nullptr;
-      if (kb > 0) {
-        st = p.incl + ((int64_t)seq * p.nchunk + (kb - 1)) * 2 * HD;
-      } else if (p.sk_in != nullptr) {
-        hin_k = p.sk_in[(int64_t)seq * HD + c];
-        hin_v = p.sv_in[(int64_t)seq * HD + c];
-      }
-      for (int lv = p.blk_levels - 1; lv >= 0; --lv) {
+      // the state before row 0: zero for a prefill, the given state for a
+      // continuation; the nodes before this chunk are composed onto it
+      float one = 1.f;
+      float hin_k = p.sk_in != nullptr ? p.sk_in[(int64_t)seq * HD + 64 * half + lane] : 0.f;
+      float hin_v = p.sv_in != nullptr ? p.sv_in[(int64_t)seq * HD + 64 * half + lane] : 0.f;
+      for (int lv = p.nlevels - 1; lv >= 0; --lv) {
         const int64_t nd = (int64_t)chunk >> (kScanRadixLog2 * lv);
-        const int64_t first = max(nd & ~(int64_t)(kScanRadix - 1), (int64_t)bs >> (kScanRadixLog2 * lv));
+        const int64_t first = nd & ~(int64_t)(kScanRadix - 1);
         const int64_t lvl0 = p.lbase[lv] + (int64_t)seq * p.nodes[lv];
-        fold_state_nodes<HD>(p, st, lvl0 + first, (int)(nd - first), half, hin_k, hin_v, tag, lane);
-        st = nullptr;  // the block state is taken with the top level's nodes
+        fold_nodes<HD>(p, lvl0 + first, (int)(nd - first), half, one, hin_k, hin_v, tag, lane);
       }
-      if (st != nullptr)  // no level inside the block (one chunk per block)
-        fold_state_nodes<HD>(p, st, 0, 0, half, hin_k, hin_v, tag, lane);
-      s_hk[c] = hin_k;
-      s_hv[c] = hin_v;
-      // the last chunk of a block publishes the state after it (its carry-in
-      // through the chunk's whole map) for the next block's carries
-      if (chunk % p.mblk == p.mblk - 1 && chunk + 1 < p.nchunk) {
-        const float a = sc.tot[0][c];
-        uint64_t* d = p.incl + ((int64_t)seq * p.nchunk + kb) * 2 * HD + c;
-        st_tagged(d, tag, a * hin_k + sc.tot[1][c]);
-        st_tagged(d + HD, tag, a * hin_v + sc.tot[2][c]);
-      }
+      s_hk[64 * half + lane] = hin_k;
+      s_hv[64 * half + lane] = hin_v;
     }
   }
   __syncthreads();
-}
+  between();
 
-// Phase B: pass 2 of ticket tc (rows rc, its row-group prefix in set sc, its
-// carry-in in s_hk / s_hv): the sequential recurrence from the carry-in, with
-// hk/hv, anchor rows, ring slots and the final fp32 state streamed out.
-template <typename ST, int HD, int S, bool GATE>
-__device__ __forceinline__ void scan_phase_b(const ScanParams& p, uint32_t tc,
-                                             const ChunkRows<ST, HD, S>& rc,
-                                             const PrefixSet<kScanThreads / (HD / StTraits<ST>::VEC), HD>& sc,
-                                             const float* s_hk, const float* s_hv) {
-  constexpr int VEC = StTraits<ST>::VEC;
-  constexpr int LPR = HD / VEC;
-  constexpr int RG = kScanThreads / LPR;
-  constexpr int LC = RG * S;
-  const int tid = threadIdx.x;
-  const int chunk = (int)(tc / (uint32_t)p.nseq);
-  const int seq = (int)(tc % (uint32_t)p.nseq);
-  const int b = seq / p.H;
-  const int h = seq - b * p.H;
-  const int T = p.T;
-  const int r = tid / LPR;
-  const int c0 = (tid - r * LPR) * VEC;
-  const int tbase = chunk * LC + r * S;
-  const int64_t seq_base = (int64_t)seq * T * HD;
-  float gbias[VEC];
-  load_gate_bias<ST, HD, GATE>(p, h, c0, gbias);
-  float sk[VEC], sv[VEC];
+  // ---- pass 2: sequential recurrence from the carry-in, stream outputs ---
+  {
+    float sk[VEC], sv[VEC];
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) {
-    const int c = c0 + i;
-    sk[i] = sc.A[r][c] * s_hk[c] + sc.Bk[r][c];
-    sv[i] = sc.A[r][c] * s_hv[c] + sc.Bv[r][c];
-  }
-  const int D = p.ht.D[h];
-  const int W = p.ht.W[h];
-  ST* hkp = reinterpret_cast<ST*>(p.hk);
-  ST* hvp = reinterpret_cast<ST*>(p.hv);
-  ST* Kcp = reinterpret_cast<ST*>(p.Kc);
-  ST* Vcp = reinterpret_cast<ST*>(p.Vc);
-  ST* krp = reinterpret_cast<ST*>(p.kr);
-  ST* vrp = reinterpret_cast<ST*>(p.vr);
-  const int64_t arow0 = (int64_t)b * p.R + p.ht.aoff[h];
-  const int64_t rrow0 = (int64_t)b * p.WS + p.ht.roff[h];
-  const int tabs = p.t0 + tbase;  // absolute position of row tbase
-  int aq = tabs / D;              // anchor index candidate of row tbase
-  int ar = tabs - aq * D;         // phase of row tbase
+    for (int i = 0; i < VEC; ++i) {
+      const int c = c0 + i;
+      sk[i] = s_A[r][c] * s_hk[c] + s_Bk[r][c];
+      sv[i] = s_A[r][c] * s_hv[c] + s_Bv[r][c];
+    }
+    const int D = p.ht.D[h];
+    const int W = p.ht.W[h];
+    ST* hkp = reinterpret_cast<ST*>(p.hk);
+    ST* hvp = reinterpret_cast<ST*>(p.hv);
+    ST* Kcp = reinterpret_cast<ST*>(p.Kc);
+    ST* Vcp = reinterpret_cast<ST*>(p.Vc);
+    ST* krp = reinterpret_cast<ST*>(p.kr);
+    ST* vrp = reinterpret_cast<ST*>(p.vr);
+    const int64_t arow0 = (int64_t)b * p.R + p.ht.aoff[h];
+    const int64_t rrow0 = (int64_t)b * p.WS + p.ht.roff[h];
+    const int tabs = p.t0 + tbase;  // absolute position of row tbase
+    int aq = tabs / D;              // anchor index candidate of row tbase
+    int ar = tabs - aq * D;         // phase of row tbase
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int t = tbase + s;
-    if (t < T) {
-      float gf[VEC], kf[VEC], vf[VEC];
-      unpack16(rc.g[s], gf, (ST*)nullptr);
-      apply_gate<VEC, GATE>(gf, gbias);
-      unpack16(rc.k[s], kf, (ST*)nullptr);
-      unpack16(rc.v[s], vf, (ST*)nullptr);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        sk[i] = gf[i] * sk[i] + (1.f - gf[i]) * kf[i];
-        sv[i] = gf[i] * sv[i] + (1.f - gf[i]) * vf[i];
-      }
-      const u32x4 ok = pack16(sk, (ST*)nullptr);
-      const u32x4 ov = pack16(sv, (ST*)nullptr);
-      if (hkp != nullptr) {
-        const int64_t off = seq_base + (int64_t)t * HD + c0;
-        st_raw16(hkp + off, ok);
-        st_raw16(hvp + off, ov);
-      }
-      if (ar == D - 1) {
-        const int64_t off = (arow0 + aq) * HD + c0;
-        st_raw16(Kcp + off, ok);
-        st_raw16(Vcp + off, ov);
-      }
-      if (W > 0 && t >= T - W) {
-        const int64_t off = (rrow0 + ((p.t0 + t) % W)) * HD + c0;
-        st_raw16(krp + off, ok);
-        st_raw16(vrp + off, ov);
-      }
-      if (t == T - 1) {
-        const int64_t off = (int64_t)seq * HD + c0;
+    for (int s = 0; s < S; ++s) {
+      const int t = tbase + s;
+      if (t < T) {
+        float gf[VEC], kf[VEC], vf[VEC];
+        unpack16(rg[s], gf, (ST*)nullptr);
+        gate(gf);
+        unpack16(rk[s], kf, (ST*)nullptr);
+        unpack16(rv[s], vf, (ST*)nullptr);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-          p.sk[off + i] = sk[i];
-          p.sv[off + i] = sv[i];
+          sk[i] = gf[i] * sk[i] + (1.f - gf[i]) * kf[i];
+          sv[i] = gf[i] * sv[i] + (1.f - gf[i]) * vf[i];
+        }
+        const u32x4 ok = pack16(sk, (ST*)nullptr);
+        const u32x4 ov = pack16(sv, (ST*)nullptr);
+        if (hkp != nullptr) {
+          const int64_t off = seq_base + (int64_t)t * HD + c0;
+          st_raw16(hkp + off, ok);
+          st_raw16(hvp + off, ov);
+        }
+        if (ar == D - 1) {
+          const int64_t off = (arow0 + aq) * HD + c0;
+          st_raw16(Kcp + off, ok);
+          st_raw16(Vcp + off, ov);
+        }
+        if (W > 0 && t >= T - W) {
+          const int64_t off = (rrow0 + ((p.t0 + t) % W)) * HD + c0;
+          st_raw16(krp + off, ok);
+          st_raw16(vrp + off, ov);
+        }
+        if (t == T - 1) {
+          const int64_t off = (int64_t)seq * HD + c0;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            p.sk[off + i] = sk[i];
+            p.sv[off + i] = sv[i];
+          }
         }
       }
-    }
-    if (++ar == D) {
-      ar = 0;
-      ++aq;
+      if (++ar == D) {
+        ar = 0;
+        ++aq;
+      }
     }
   }
+
 }
 
 // Persistent kernel: the grid is sized to the number of workgroups that can
-// be resident at once, so every workgroup runs concurrently.  Workgroup w
-// processes tickets w, w + G, w + 2G, ... in order; ticket t is chunk t / nseq
-// of sequence t % nseq.  A chunk waits only on nodes of earlier chunks of its
-// own sequence, i.e. on smaller tickets, so the smallest unfinished ticket
-// can always proceed (no deadlock), and no ticket counter (atomic) is needed.
-// Every workgroup reads the epoch first; the last one to finish advances it,
-// so the epoch is this launch's tag.
-//
-// Pipeline, per step (tickets t, t+G, t+2G in three register buffers):
-//   phase A: pass 1 of t+G and its publication || the carry-in of t;
-//   then the loads of t+2G (into the buffer pass 2 of t-G freed);
-//   phase B: pass 2 of t.
-// So a ticket is published one step before its carry is composed, and the
-// tree round trip of a chunk overlaps the next chunk's pass 1.
+// be resident at once, so every workgroup runs concurrently.  Workgroup w processes tickets w, w + G, w + 2G, ... in
+// order; ticket t is chunk t / nseq of sequence t % nseq.  A chunk waits only
+// on nodes of earlier chunks of its own sequence, i.e. on smaller tickets, so
+// the smallest unfinished ticket can always proceed (no deadlock), and no
+// ticket counter (atomic) is needed.  Every workgroup reads the epoch first;
+// the last one to finish advances it, so the epoch is this launch's tag.
 template <typename ST, int HD, int S, bool GATE>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void scan_kernel(const ScanParams p) {
@@ -533,55 +405,39 @@ void scan_kernel(const ScanParams p) {
   constexpr int LPR = HD / VEC;
   constexpr int RG = kScanThreads / LPR;
   static_assert(HD % 64 == 0 && LPR <= 64, "layout");
-  __shared__ PrefixSet<RG, HD> s_set[2];
+  __shared__ float s_A[RG][HD];
+  __shared__ float s_Bk[RG][HD];
+  __shared__ float s_Bv[RG][HD];
   __shared__ float s_hk[HD];
   __shared__ float s_hv[HD];
   __shared__ uint32_t s_epoch;
 
   const int tid = threadIdx.x;
-  const uint32_t G = gridDim.x;
-  const uint32_t n = (uint32_t)p.nticket;
-  uint32_t t = blockIdx.x;
-  // (loads are unconditional -- past the end they re-load the last ticket
-  // and are ignored -- so the compiler counts outstanding loads exactly)
-  ChunkRows<ST, HD, S> r0, r1, r2;
-  load_rows<ST, HD, S>(p, min(t, n - 1), r0);
-  load_rows<ST, HD, S>(p, min(t + G, n - 1), r1);
-  // the epoch after the first rows' loads: its round trip (every workgroup
-  // reads the same word) overlaps their arrival
   if (tid == 0) s_epoch = ld_acquire_u32(p.hdr + kEpochWord);
   __syncthreads();
   const uint32_t epoch = s_epoch;
   const uint32_t tag = (epoch % 0x3FFFFFFFu) + 1u;
+  const uint32_t G = gridDim.x;
 
-  if (t < n) {
-    scan_phase_a<ST, HD, S, GATE>(p, tag, true, t, r0, s_set[0], false, t, s_set[1], s_hk, s_hv);
-    // one pipeline step: ticket t in `cur` (set sc), t+G in `nxt`; the loads
-    // of t+2G go to `far` after the carry is known (vector memory operations
-    // complete in order, so a carry load issued after them would wait for
-    // them) and before pass 2, whose time covers their latency
-    auto step = [&](const ChunkRows<ST, HD, S>& cur, const ChunkRows<ST, HD, S>& nxt,
-                    ChunkRows<ST, HD, S>& far, int sc) {
-      const uint32_t t1 = t + G;
-      scan_phase_a<ST, HD, S, GATE>(p, tag, t1 < n, t1, nxt, s_set[sc ^ 1], true, t, s_set[sc],
-                                    s_hk, s_hv);
-      load_rows<ST, HD, S>(p, min(t + 2 * G, n - 1), far);
-      scan_phase_b<ST, HD, S, GATE>(p, t, cur, s_set[sc], s_hk, s_hv);
-      __syncthreads();  // set sc and the carry are reused by the next step
-      t = t1;
-    };
-    int sc = 0;
-    while (true) {
-      step(r0, r1, r2, sc);
-      sc ^= 1;
-      if (t >= n) break;
-      step(r1, r2, r0, sc);
-      sc ^= 1;
-      if (t >= n) break;
-      step(r2, r0, r1, sc);
-      sc ^= 1;
-      if (t >= n) break;
-    }
+  // Two register buffers: the rows of the next chunk are loaded while the
+  // current chunk streams its outputs.
+  const uint32_t n = (uint32_t)p.nticket;
+  ChunkRows<ST, HD, S> ra, rb;
+  uint32_t ticket = blockIdx.x;
+  if (ticket < n) load_rows<ST, HD, S>(p, ticket, ra);
+  while (ticket < n) {
+    const uint32_t t1 = ticket + G;
+    // (prefetches are unconditional -- past the end they re-load the last
+    // ticket and are ignored -- so outstanding loads are counted exactly)
+    scan_chunk<ST, HD, S, GATE>(p, ticket, tag, ra, s_A, s_Bk, s_Bv, s_hk, s_hv,
+                          [&] { load_rows<ST, HD, S>(p, min(t1, n - 1), rb); });
+    __syncthreads();  // LDS is reused by the next chunk
+    if (t1 >= n) break;
+    const uint32_t t2 = t1 + G;
+    scan_chunk<ST, HD, S, GATE>(p, t1, tag, rb, s_A, s_Bk, s_Bv, s_hk, s_hv,
+                          [&] { load_rows<ST, HD, S>(p, min(t2, n - 1), ra); });
+    __syncthreads();
+    ticket = t2;
   }
 
   // retire: two-level done count; the last workgroup advances the epoch
@@ -678,26 +534,13 @@ int launch_scan_t(const ScanParams& p, hipStream_t st) {
   // costs about 20 us of queue drain per launch.)  If other streams hold
   // CUs, the late workgroups start when those finish; a wait that outlasts
   // the spin bound is reported in the workspace error word, never a hang.
-  // Rounds of G tickets hold whole blocks: G = nseq * mblk with mblk the
-  // largest power of two that fits the device (one chunk per block when the
-  // sequences outnumber the resident workgroups).
-  ScanParams q = p;
-  int64_t g = lim;
-  q.mblk = 1;
-  if (p.nseq <= lim) {
-    while ((int64_t)p.nseq * q.mblk * 2 <= lim) q.mblk *= 2;
-    g = (int64_t)p.nseq * q.mblk;
-  }
-  q.blk_levels = 0;
-  for (int64_t span = 1; span < q.mblk && q.blk_levels < p.nlevels; span *= kScanRadix)
-    ++q.blk_levels;
-  const unsigned grid = (unsigned)std::min<int64_t>(p.nticket, g);
+  const unsigned grid = (unsigned)std::min<int64_t>(p.nticket, lim);
   if (gated)
     hipLaunchKernelGGL((scan_kernel<ST, HD, kScanRowsPerThread, true>), dim3(grid),
-                       dim3(kScanThreads), 0, st, q);
+                       dim3(kScanThreads), 0, st, p);
   else
     hipLaunchKernelGGL((scan_kernel<ST, HD, kScanRowsPerThread, false>), dim3(grid),
-                       dim3(kScanThreads), 0, st, q);
+                       dim3(kScanThreads), 0, st, p);
   return (int)hipGetLastError();
 }
 
