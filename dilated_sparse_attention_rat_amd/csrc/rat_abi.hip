@@ -9,9 +9,6 @@
 #include <cstdint>
 #include <cstring>
 
-#include <rocblas/rocblas.h>
-
-#include <map>
 #include <mutex>
 
 #include "rat.h"
@@ -763,31 +760,10 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
-// layer prefill: projections (rocBLAS GEMMs) around the scan and attention
+// layer prefill: projections (the library's own MFMA GEMM) around the scan
+// and attention
 // ---------------------------------------------------------------------------
 namespace {
-
-// one rocBLAS handle per device, created on the first layer call there
-rocblas_handle blas_handle(int& err) {
-  static std::mutex mu;
-  static std::map<int, rocblas_handle> handles;
-  err = RAT_OK;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    err = RAT_ERR_HIP;
-    return nullptr;
-  }
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = handles.find(dev);
-  if (it != handles.end()) return it->second;
-  rocblas_handle h = nullptr;
-  if (rocblas_create_handle(&h) != rocblas_status_success) {
-    err = RAT_ERR_HIP;
-    return nullptr;
-  }
-  handles[dev] = h;
-  return h;
-}
 
 // layer workspace: the scan workspace first (its header, with the launch
 // epoch and the error word, then sits at offset 0 whatever the call's size,
@@ -838,6 +814,10 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const 
   const int64_t HD = (int64_t)H * hd;
   if ((int64_t)B * T > INT32_MAX || HD > INT32_MAX || T * HD > INT32_MAX)
     return RAT_ERR_UNSUPPORTED;
+  // the bf16 GEMM moves 16-byte pieces of rows (8 elements) and has at most
+  // 65535 row tiles of 256
+  if (dtype == RAT_DTYPE_BF16 && (dm % 8 != 0 || (int64_t)B * T > 65535LL * 256))
+    return RAT_ERR_UNSUPPORTED;
   LayerLayout L;
   if (!layer_layout(dtype, B, H, T, hd, L)) return RAT_ERR_UNSUPPORTED;
   if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < L.bytes)
@@ -851,29 +831,28 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const 
   void* hk = act + 4 * L.act;
   void* hv = act + 5 * L.act;
   void* o = act + 6 * L.act;
-  int herr;
-  rocblas_handle hb = blas_handle(herr);
-  if (herr != RAT_OK) return herr;
-  static std::mutex blas_mu;  // the shared handle's stream is set per call
-  const rocblas_datatype dt = dtype == RAT_DTYPE_BF16 ? rocblas_datatype_bf16_r
-                                                       : rocblas_datatype_f32_r;
-  const float one = 1.f, zero = 0.f;
-  {
-    std::lock_guard<std::mutex> lock(blas_mu);
-    if (rocblas_set_stream(hb, reinterpret_cast<hipStream_t>(stream)) != rocblas_status_success)
-      return RAT_ERR_HIP;
-    // projections token-major, [B*T, H*hd] = x [B*T, dm] W [dm, H*hd]: one
-    // GEMM each (column-major: Y^T = W^T x^T, W with ld H*hd, x with ld dm)
-    const void* wts[4] = {w_q, w_k, w_v, w_g};
-    void* dst[4] = {q, k, v, g};
-    for (int pj = 0; pj < 4; ++pj) {
-      rocblas_status r = rocblas_gemm_ex(
-          hb, rocblas_operation_none, rocblas_operation_none, (int)HD, (int)(B * T), dm, &one,
-          wts[pj], dt, (int)HD, x, dt, dm, &zero, dst[pj], dt, (int)HD, dst[pj], dt, (int)HD,
-          rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-      if (r != rocblas_status_success) return RAT_ERR_HIP;
-    }
-  }
+  // projections token-major, [B*T, H*hd] = x [B*T, dm] W [dm, H*hd]: one
+  // grouped GEMM for q, k, v and the gate pre-activation
+  GemmParams gp;
+  std::memset(&gp, 0, sizeof(gp));
+  gp.M = (int)(B * T);
+  gp.K = dm;
+  gp.Ng = (int)HD;
+  gp.ngroups = 4;
+  gp.A = x;
+  gp.lda = dm;
+  gp.B[0] = w_q;
+  gp.B[1] = w_k;
+  gp.B[2] = w_v;
+  gp.B[3] = w_g;
+  gp.ldb = HD;
+  gp.C[0] = q;
+  gp.C[1] = k;
+  gp.C[2] = v;
+  gp.C[3] = g;
+  gp.ldc = HD;
+  st = map_hip(launch_gemm(dtype, gp, stream));
+  if (st != RAT_OK) return st;
   // recurrence with the gate sigmoid(g + b_g) fused into its loads
   st = scan_impl(dtype, B, H, T, hd, D, W, T_cap, 0, k, v, g, nullptr, nullptr, hk, hv, Kc, Vc,
                  nullptr, nullptr, k_ring, v_ring, state_k, state_v, ws,
@@ -883,18 +862,20 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const 
   st = attn_impl(dtype, B, H, T, hd, D, W, scale, T_cap, 0, q, hk, hv, Kc, Vc, nullptr, nullptr,
                  o, lse, stream, true, true);
   if (st != RAT_OK) return st;
-  {
-    std::lock_guard<std::mutex> lock(blas_mu);
-    if (rocblas_set_stream(hb, reinterpret_cast<hipStream_t>(stream)) != rocblas_status_success)
-      return RAT_ERR_HIP;
-    // out [B*T, dm] = o [B*T, H*hd] W_o [H*hd, dm]; column-major: out^T =
-    // W_o^T o^T with W_o (ld dm) and o (ld H*hd)
-    rocblas_status r = rocblas_gemm_ex(hb, rocblas_operation_none, rocblas_operation_none, dm,
-                                       (int)(B * T), (int)HD, &one, w_o, dt, dm, o, dt, (int)HD,
-                                       &zero, out, dt, dm, out, dt, dm, rocblas_datatype_f32_r,
-                                       rocblas_gemm_algo_standard, 0, 0);
-    if (r != rocblas_status_success) return RAT_ERR_HIP;
-  }
+  // out [B*T, dm] = o [B*T, H*hd] W_o [H*hd, dm]
+  std::memset(&gp, 0, sizeof(gp));
+  gp.M = (int)(B * T);
+  gp.K = (int)HD;
+  gp.Ng = dm;
+  gp.ngroups = 1;
+  gp.A = o;
+  gp.lda = HD;
+  gp.B[0] = w_o;
+  gp.ldb = dm;
+  gp.C[0] = out;
+  gp.ldc = dm;
+  st = map_hip(launch_gemm(dtype, gp, stream));
+  if (st != RAT_OK) return st;
   return RAT_OK;
 }
 

@@ -180,7 +180,21 @@ struct BwdParams {
   HeadTables ht;
 };
 
+// Projection GEMM: C_g = A B_g for groups g < ngroups, B_g [K, Ng] and
+// C_g [M, Ng] row-major; column n of the grouped product is column n % Ng
+// of group n / Ng.
+struct GemmParams {
+  int M, K, Ng, ngroups;
+  const void* A;     // [M, K], row stride lda
+  int64_t lda;
+  const void* B[4];  // [K, Ng] each, row stride ldb
+  int64_t ldb;
+  void* C[4];        // [M, Ng] each, row stride ldc
+  int64_t ldc;
+};
+
 // launchers (one per kernel family); return hipError_t as int
+int launch_gemm(int dtype, const GemmParams& p, void* stream);
 int launch_scan(int dtype, int hd, const ScanParams& p, void* stream);
 // Continuation: copy the ring slots of positions [max(0, t0+T-W), t0) that
 // stay in the window from ring_in to ring_out (the scan writes the rest).

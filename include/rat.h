@@ -383,12 +383,10 @@ int64_t rat_layer_workspace_bytes(int dtype, int B, int H, int64_t T, int hd);
  *        b_g [H*hd] fp32; w_o [H*hd, dm] ST.
  * Writes out [B, T, dm] ST; lse [B, H, T] fp32 (nullable); Kc, Vc, k_ring,
  *        v_ring, state_k, state_v as rat_scan_prefill.
- * The projections run as rocBLAS GEMMs (bf16 or fp32 in and out, fp32
- * accumulation) on the same stream.  Unlike the other entry points this one
- * uses a library with state of its own: the first call on a device creates a
- * rocBLAS handle there (kept until the process ends), and rocBLAS manages
- * its own device memory.  Calls from several host threads are safe (the
- * handle's stream is set under a lock).
+ * The projections run on the library's own MFMA GEMM (bf16 or fp32 in and
+ * out, fp32 accumulation) on the same stream; like every other entry point
+ * this one allocates nothing and keeps no state.  bf16 requires dm % 8 == 0
+ * and B*T <= 65535*256 (else RAT_ERR_UNSUPPORTED).
  * workspace: rat_layer_workspace_bytes bytes (a scan workspace, then q, k,
  * v, the gate pre-activation, the states and o).
  */

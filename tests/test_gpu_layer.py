@@ -1,4 +1,4 @@
-"""GPU parity of one RAT+ layer over a prefill (projections as rocBLAS GEMMs,
+"""GPU parity of one RAT+ layer over a prefill (projections on the library's MFMA GEMM,
 the gate fused into the scan, dilated attention, output projection) against
 the oracle's layer, through the C ABI.
 
@@ -45,6 +45,10 @@ CASES = [
     ("bf16-hybrid", 2, 3, 300, 128, 256, [4, 1, 16], [0, 37, 3], "bf16"),
     ("bf16-64-resident", 1, 4, 640, 64, 192, [16, 8, 16, 32], [0, 0, 0, 0], "bf16"),
     ("f32-64", 2, 2, 130, 64, 96, [3, 5], [4, 0], "f32"),
+    # d_model not a multiple of the GEMM's 32-wide K step: the input
+    # projections take the register-staged GEMM (the output projection, K =
+    # H*hd, the direct-to-LDS one); rows and columns past the tiles
+    ("bf16-dm200-ragged", 1, 3, 333, 64, 200, [2, 7, 1], [0, 9, 0], "bf16"),
 ]
 
 

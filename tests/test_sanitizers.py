@@ -61,7 +61,7 @@ def test_host_abi_under_asan_ubsan():
           os.path.join(HERE, "abi_driver.cpp"), "-o", drv])
     exe = os.path.join(OUT, "abi_driver")
     _run([clangxx, "-fsanitize=address,undefined", drv, *objs, "-o", exe,
-          f"-L{ROCM}/lib", "-lamdhip64", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib"])
+          f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib"])
     # the HIP runtime keeps allocations until exit: leak checking off here
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
