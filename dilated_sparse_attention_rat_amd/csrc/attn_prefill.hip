@@ -588,15 +588,30 @@ void attn_prefill_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::KSTR];
   __shared__ __attribute__((aligned(16))) ST sV[C::VLDS];
 
-  // block -> (head rank, batch row, pair): heads in cost order, so the
-  // heaviest blocks are dispatched first; consecutive blocks land on
-  // different XCDs, which spreads every head's work over the whole chip
+  // block -> (unit, pair), a unit being one (head rank, batch row), units in
+  // descending cost.  Workgroup i runs on XCD i % 8, and each XCD has its own
+  // L2, so the pairs of a unit are kept on few XCDs: in every group of eight
+  // consecutive units, XCD x runs the first half of unit x's pairs and the
+  // second half of unit 7-x's.  A unit's anchor rows and band tiles are then
+  // fetched into two L2s rather than all eight, and the cost per XCD stays
+  // level even where a group mixes heavy and light heads.  The units past
+  // the last full group are dealt round-robin.
   const int L = blockIdx.x;
-  const int per_rank = p.B * p.np;
-  const int rank = L / per_rank;
-  const int rem = L - rank * per_rank;
-  const int b = rem / p.np;
-  const int pr = rem - b * p.np;
+  const int grouped = (p.B * p.H) / 8 * 8 * p.np;
+  int u, pr;
+  if (L < grouped) {
+    const int x = L & 7;
+    const int s = L >> 3;
+    const int grp = s / p.np;
+    pr = s - grp * p.np;
+    u = 8 * grp + (pr < (p.np + 1) / 2 ? x : 7 - x);
+  } else {
+    const int r = L - grouped;
+    u = grouped / p.np + r / p.np;
+    pr = r - (r / p.np) * p.np;
+  }
+  const int rank = u / p.B;
+  const int b = u - rank * p.B;
   const int h = p.perm[rank];
 
   const int qa = p.nq - 1 - pr;  // heavy tile first, then its partner
