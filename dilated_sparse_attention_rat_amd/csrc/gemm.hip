@@ -155,58 +155,91 @@ void gemm_bf16_kernel(const GemmParams p) {
   }
 }
 
-// Direct-to-LDS variant (bf16, K % 32 == 0): every K step's tiles are
-// fetched with global_load_lds_dwordx4 (lane l's 16 bytes land at the
-// instruction's LDS base + 16 l, checked on the device), so no register
-// staging: a ring of three LDS stages holds the step being computed and the
-// two whose loads are in flight.  Here k slot (g, j) of a fragment is
-// k = 8g + j: A^T fragments are single 16-byte reads and the transposing B^T
-// reads take rows 8g .. 8g+7.  The tiles are unpadded and XOR-swizzled so
-// that the reads stay conflict-free: in the A tile (64 bytes per row)
-// 16-byte chunk c of row r sits at c ^ ((r >> 2) & 3); in the B tile (256
-// bytes per row) at c ^ 2 f(r), f(r) = (r & 3) | ((r >> 1) & 4), which is
-// distinct over the eight rows one 32-lane pass of a transposing read
-// touches.
-typedef __attribute__((address_space(3))) void lds_void_t;
-constexpr int kGemmStages = 3;
-constexpr int kGemmAStage = kGemmBM * kGemmBK;  // elements
-constexpr int kGemmBStage = kGemmBK * kGemmBN;
+// Direct-to-LDS variant (bf16, K % 32 == 0): workgroup tile 256 (n) x 256
+// (m), 4 waves of 128 x 128, one workgroup per CU, on
+// v_mfma_f32_32x32x16_bf16.  A lone wave per SIMD keeps the matrix pipe full
+// with the 32 x 32 form (the 16 x 16 form reaches about 57% of the bf16 rate
+// from one wave, measured), and has 512 registers, so its 128 x 128 fp32
+// accumulators (256 registers) sit in the accumulation registers; per FLOP
+// the tile reads half the LDS bytes and half the global bytes of a
+// 128-wide tile.  Every K step's tiles are fetched with
+// global_load_lds_dwordx4 (lane l's 16 bytes land at the instruction's LDS
+// base + 16 l, checked on the device), so no register staging: a ring of
+// four LDS stages (32 KB each) holds the step being computed and the three
+// whose loads are in flight.
+//  * Fragments: MFMA lane l covers row l % 32 of its operand and k slots
+//    8 (l / 32) + s.  A^T fragments are single 16-byte reads of the
+//    row-major A tile [256 m][32 k]; B^T fragments come out of two
+//    transposing reads of the B tile (two halves of [32 k][128 n], one per
+//    wave column), 16-lane group G reading k rows 8 (G / 2) + 0..3 (then 4
+//    on) of columns 16 (G % 2) + 0..15.
+//  * Swizzles (tiles unpadded): A row r holds 16-byte chunk c at
+//    c ^ ((r >> 2) & 3), so 16 lanes reading 16 rows cover all banks; B row
+//    r holds chunk c at c ^ 4 (r & 3), so the 4 rows x 64 bytes of one
+//    32-lane transposing pass fall on distinct banks.
+//  * Accumulator element i of lane l is C^T row n = 8 (i / 4) + 4 (l / 32)
+//    + i % 4, column m = l % 32; the epilogue regroups them through LDS into
+//    whole 16-byte row pieces (A, B and C rows 16-byte aligned: pointers
+//    16-byte aligned, ld* and Ng multiples of 8).
+constexpr int kWideBN = 256;
+constexpr int kWideBM = 256;
+constexpr int kWideHalf = kGemmBK * 128;          // elements of one B half
+constexpr int kWideAStage = kWideBM * kGemmBK;  // elements
+constexpr int kWideBStage = 2 * kWideHalf;
 
-// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt at its maximum), and a workgroup
-// barrier that is a compiler-level fence only: the direct-to-LDS loads are
-// waited for explicitly, and a __syncthreads() would also wait for the
-// loads still in flight for later steps.
-#define RAT_WAIT_VM_LGKM(n) __builtin_amdgcn_s_waitcnt(0x0070 | (n))
+// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt at its maximum; n < 64), and a
+// workgroup barrier that is a compiler-level fence only: the direct-to-LDS
+// loads are waited for explicitly, and a __syncthreads() would also wait for
+// the loads still in flight for later steps.
+#define RAT_WAIT_VM_LGKM(n) \
+  __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// global_load_lds_dwordx4 from this lane's src to LDS base dst (+ 16 bytes
+// per lane).  Written out rather than through the builtin: the compiler
+// cannot tell which LDS stage a builtin load writes, and waits for every one
+// in flight before each LDS read.  Nothing is returned in registers (the
+// address is read at issue); completion is waited for with vmcnt before the
+// barrier that publishes a stage.  One wait state separates the M0 write
+// from its use.
+__device__ __forceinline__ void dma16(const void* src, const bf16* dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_dma_kernel(const GemmParams p) {
-  // one array per stage, indexed statically: the compiler then sees that a
-  // fragment read of stage s does not alias the loads in flight into the
-  // other two (it would otherwise wait for all of them before every read)
-  __shared__ __attribute__((aligned(1024))) bf16 sA0[kGemmAStage];
-  __shared__ __attribute__((aligned(1024))) bf16 sA1[kGemmAStage];
-  __shared__ __attribute__((aligned(1024))) bf16 sA2[kGemmAStage];
-  __shared__ __attribute__((aligned(1024))) bf16 sB0[kGemmBStage];
-  __shared__ __attribute__((aligned(1024))) bf16 sB1[kGemmBStage];
-  __shared__ __attribute__((aligned(1024))) bf16 sB2[kGemmBStage];
+  // one array per stage, indexed statically
+  __shared__ __attribute__((aligned(1024))) bf16 sA0[kWideAStage];
+  __shared__ __attribute__((aligned(1024))) bf16 sA1[kWideAStage];
+  __shared__ __attribute__((aligned(1024))) bf16 sA2[kWideAStage];
+  __shared__ __attribute__((aligned(1024))) bf16 sA3[kWideAStage];
+  __shared__ __attribute__((aligned(1024))) bf16 sB0[kWideBStage];
+  __shared__ __attribute__((aligned(1024))) bf16 sB1[kWideBStage];
+  __shared__ __attribute__((aligned(1024))) bf16 sB2[kWideBStage];
+  __shared__ __attribute__((aligned(1024))) bf16 sB3[kWideBStage];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int col = lane & 15;
-  const int g = lane >> 4;
-  const int n0 = blockIdx.x * kGemmBN;
-  const int m0 = blockIdx.y * kGemmBM;
-  const int wn = wave & 1;
-  const int wm = wave >> 1;
+  const int n0 = blockIdx.x * kWideBN;
+  const int m0 = blockIdx.y * kWideBM;
+  const int wn = wave & 1;   // wave's n offset 128*wn (its B half)
+  const int wm = wave >> 1;  // wave's m offset 128*wm
   const int N = p.ngroups * p.Ng;
 
-  // this lane's sources: A instructions j < 4 cover rows 16 (4 wave + j) ..
-  // +15 of the tile, B instructions j < 2 rows 4 (2 wave + j) .. +3
+  // this lane's sources: A instruction j < 4 covers rows 16 (4 wave + j) ..
+  // +15 of the tile; B instruction j < 4 is number q = 4 wave + j of the
+  // sixteen, rows 4 (q % 8) .. +3 of half q / 8
   const bf16* asrc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -215,85 +248,148 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
     const int m = min(m0 + row, p.M - 1);
     asrc[j] = reinterpret_cast<const bf16*>(p.A) + (int64_t)m * p.lda + 8 * c;
   }
-  const bf16* bsrc[2];
+  const bf16* bsrc[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 4 * (2 * wave + j) + (lane >> 4);
-    const int c = (lane & 15) ^ (2 * ((row & 3) | ((row >> 1) & 4)));
-    const int n = min(n0 + 8 * c, N - 8);
+  for (int j = 0; j < 4; ++j) {
+    const int q = 4 * wave + j;
+    const int row = 4 * (q & 7) + (lane >> 4);
+    const int c = (lane & 15) ^ (4 * (row & 3));
+    const int n = min(n0 + 128 * (q >> 3) + 8 * c, N - 8);
     const int grp = n / p.Ng;
     bsrc[j] = reinterpret_cast<const bf16*>(p.B[grp]) + (int64_t)row * p.ldb + (n - grp * p.Ng);
   }
-  auto issue = [&](bf16* sa, bf16* sb, int ks) {
+  auto issue = [&](bf16* __restrict__ sa, bf16* __restrict__ sb, int ks) {
     const int64_t k0 = (int64_t)ks * kGemmBK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[j] + k0),
-                                       (lds_void_t*)(sa + (4 * wave + j) * 16 * kGemmBK), 16, 0, 0);
+    for (int j = 0; j < 4; ++j) dma16(asrc[j] + k0, sa + (4 * wave + j) * 16 * kGemmBK);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[j] + k0 * p.ldb),
-                                       (lds_void_t*)(sb + (2 * wave + j) * 4 * kGemmBN), 16, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const int q = 4 * wave + j;
+      dma16(bsrc[j] + k0 * p.ldb, sb + (q >> 3) * kWideHalf + (q & 7) * 4 * 128);
+    }
   };
 
-  f32x4 acc[4][8];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const bf16* sa, const bf16* sb) {
-    Frag<bf16> af[8];
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int r = 128 * wm + 16 * mb + col;
-      af[mb] = frag_ld8(sa + r * kGemmBK + 8 * (g ^ ((r >> 2) & 3)));
+      for (int e = 0; e < 16; ++e) acc[nb][mb][e] = 0.f;
+
+  // fragments of k half kh (k 16 kh .. +15 of the step): A^T of 32-row
+  // block mb, B^T of 32-column block nb
+  const int l32 = lane & 31;
+  const int lh = lane >> 5;
+  const int G = lane >> 4;
+  const int tj = (lane >> 2) & 3;
+  const int tq = lane & 3;
+  const int bofs = wn * kWideHalf + (8 * (G >> 1) + tj) * 128 + 4 * (tq & 1);
+  auto read_a = [&](const bf16* __restrict__ sa, int kh, Frag<bf16>* af) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int r = 128 * wm + 32 * mb + l32;
+      af[mb] = frag_ld8(sa + r * kGemmBK + 8 * ((2 * kh + lh) ^ ((r >> 2) & 3)));
     }
+  };
+  auto read_b = [&](const bf16* __restrict__ sb, int kh, Frag<bf16>* bf) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      // rows 8g + (col >> 2) and, one read later, 4 rows on (same swizzle)
-      const int kr = 8 * g + (col >> 2);
-      const int c = 8 * wn + 2 * nb + ((col & 3) >> 1);
-      const int f = (kr & 3) | ((kr >> 1) & 4);
-      const Frag<bf16> bfr =
-          frag_ld_tr(sb + kr * kGemmBN + 8 * (c ^ (2 * f)) + 4 * (col & 1), 4 * kGemmBN);
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) mma16(acc[nb][mb], bfr, af[mb]);
+      const int c = 4 * nb + 2 * (G & 1) + (tq >> 1);
+      bf[nb] = frag_ld_tr(sb + bofs + kh * 16 * 128 + 8 * (c ^ (4 * tj)), 4 * 128);
     }
+  };
+  auto mma_half = [&](const Frag<bf16>* bf, const Frag<bf16>* af) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[nb].v, af[mb].v, acc[nb][mb], 0, 0, 0);
   };
 
   const int nks = p.K / kGemmBK;
-  // step s computes stage s % 3: once this wave's loads of step s are done
-  // (at most the next step's six outstanding) the barrier makes every wave's
-  // part visible and frees stage (s + 2) % 3, read at step s - 1, for the
-  // loads of step s + 2
-  auto step = [&](int s, const bf16* sa, const bf16* sb, bf16* na, bf16* nb2) {
-    if (s + 1 < nks)
-      RAT_WAIT_VM_LGKM(6);
-    else
-      RAT_WAIT_VM_LGKM(0);
-    lds_barrier();
-    if (s + 2 < nks) issue(na, nb2, s + 2);
-    if (s < nks) compute(sa, sb);
+  // Step s computes stage s % 4: its first k half from fragments read ahead,
+  // its second from fragments read at the step's start.  Between the two,
+  // once this thread's loads of step s + 1 are done (those of step s + 2,
+  // eight, may still be in flight), the barrier makes every wave's part of
+  // step s + 1 visible and frees stage (s + 3) % 4, last read at step s - 1,
+  // for the loads of step s + 3; the first half's fragments of step s + 1
+  // are then read under the second half's MFMAs, and the barrier wait sits
+  // under the first half's.
+  Frag<bf16> af0[4], bf0[4];
+  auto step = [&](int s, const bf16* __restrict__ sa, const bf16* __restrict__ sb,
+                  const bf16* __restrict__ sa1, const bf16* __restrict__ sb1,
+                  bf16* __restrict__ na, bf16* __restrict__ nb2) {
+    if (s >= nks) return;
+    Frag<bf16> af1[4], bf1[4];
+    read_a(sa, 1, af1);
+    read_b(sb, 1, bf1);
+    mma_half(bf0, af0);
+    if (s + 1 < nks) {
+      if (s + 2 < nks)
+        RAT_WAIT_VM_LGKM(8);
+      else
+        RAT_WAIT_VM_LGKM(0);
+      lds_barrier();
+      if (s + 3 < nks) issue(na, nb2, s + 3);
+      read_a(sa1, 0, af0);
+      read_b(sb1, 0, bf0);
+    }
+    mma_half(bf1, af1);
   };
   issue(sA0, sB0, 0);
   if (nks > 1) issue(sA1, sB1, 1);
-  for (int s0 = 0; s0 < nks; s0 += 3) {
-    step(s0, sA0, sB0, sA2, sB2);
-    step(s0 + 1, sA1, sB1, sA0, sB0);
-    step(s0 + 2, sA2, sB2, sA1, sB1);
+  if (nks > 2) issue(sA2, sB2, 2);
+  if (nks > 2)
+    RAT_WAIT_VM_LGKM(16);
+  else if (nks > 1)
+    RAT_WAIT_VM_LGKM(8);
+  else
+    RAT_WAIT_VM_LGKM(0);
+  lds_barrier();
+  read_a(sA0, 0, af0);
+  read_b(sB0, 0, bf0);
+  for (int s0 = 0; s0 < nks; s0 += 4) {
+    step(s0, sA0, sB0, sA1, sB1, sA3, sB3);
+    step(s0 + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+    step(s0 + 2, sA2, sB2, sA3, sB3, sA1, sB1);
+    step(s0 + 3, sA3, sB3, sA0, sB0, sA2, sB2);
   }
 
+  // Epilogue through LDS: element 4 e + i of lane l in block (nb, mb) is
+  // C[m][n + i] with m = 128 wm + 32 mb + l % 32, n = 128 wn + 32 nb + 8 e +
+  // 4 (l / 32) (tile coordinates), i.e. 8-byte pieces of 32 different rows
+  // per store instruction.  Each wave instead writes one 32-row block at a
+  // time into its own LDS region (rows 136 elements apart, so the 32 rows of
+  // one write pass spread over the banks and every row starts 16-byte
+  // aligned), then reads it back as 16-byte row pieces and stores 4 whole
+  // 256-byte row segments per instruction.  Every stage's loads were waited
+  // for in the loop; the barrier frees the stage buffers of all waves.
+  __syncthreads();
+  constexpr int kCS = 136;  // staging row stride (elements)
+  bf16* sC = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n = n0 + 64 * wn + 16 * nb + 4 * g;
-    if (n >= N) continue;
-    const int grp = n / p.Ng;
-    bf16* cbase = reinterpret_cast<bf16*>(p.C[grp]) + (n - grp * p.Ng);
+  for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int m = m0 + 128 * wm + 16 * mb + col;
-      if (m < p.M) st4(cbase + (int64_t)m * p.ldc, acc[nb][mb]);
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x4 v = {acc[nb][mb][4 * e], acc[nb][mb][4 * e + 1], acc[nb][mb][4 * e + 2],
+                         acc[nb][mb][4 * e + 3]};
+        st4(sC + l32 * kCS + 32 * nb + 8 * e + 4 * lh, v);
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      const int c8 = 8 * (lane & 15);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sC + row * kCS + c8);
+      const int m = m0 + 128 * wm + 32 * mb + row;
+      const int n = n0 + 128 * wn + c8;
+      if (m < p.M && n < N) {
+        const int grp = n / p.Ng;
+        bf16* dst = reinterpret_cast<bf16*>(p.C[grp]) + (int64_t)m * p.ldc + (n - grp * p.Ng);
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
     }
   }
 }
@@ -321,12 +417,15 @@ int launch_gemm(int dtype, const GemmParams& p, void* stream) {
   const int64_t N = (int64_t)p.ngroups * p.Ng;
   if (p.M == 0 || N == 0) return 0;
   if (dtype == RAT_DTYPE_BF16) {
-    const dim3 grid((unsigned)((N + kGemmBN - 1) / kGemmBN),
-                    (unsigned)((p.M + kGemmBM - 1) / kGemmBM));
-    if (p.K % kGemmBK == 0 && p.K > 0)
+    if (p.K % kGemmBK == 0 && p.K > 0) {
+      const dim3 grid((unsigned)((N + kWideBN - 1) / kWideBN),
+                      (unsigned)((p.M + kWideBM - 1) / kWideBM));
       hipLaunchKernelGGL(gemm_bf16_dma_kernel, grid, dim3(256), 0, st, p);
-    else
+    } else {
+      const dim3 grid((unsigned)((N + kGemmBN - 1) / kGemmBN),
+                      (unsigned)((p.M + kGemmBM - 1) / kGemmBM));
       hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, st, p);
+    }
   } else {
     const int64_t n = (int64_t)p.M * N;
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
