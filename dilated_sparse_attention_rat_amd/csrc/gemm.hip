@@ -9,8 +9,11 @@
 // output is projected back; zhichai.net deep dive "RAT+ 深度拆解", section
 // 2.1 -- the forget gate is input dependent (a projection of x).
 //
-// Design (bf16, gfx950):
-//  * the kernel computes C^T = B^T A^T on v_mfma_f32_16x16x32_bf16, so an
+// Design (bf16, gfx950): the main kernel is gemm_bf16_dma_kernel below
+// (K % 32 == 0): 256 x 256 tiles on 32x32x16 MFMAs at one wave per SIMD,
+// direct-to-LDS loads, output regrouped through LDS.  gemm_bf16_kernel
+// covers any K % 8 == 0:
+//  * it computes C^T = B^T A^T on v_mfma_f32_16x16x32_bf16, so an
 //    accumulator lane holds four consecutive columns n of one row m of C
 //    (one 8-byte store) -- the same orientation as O^T = V^T P^T in the
 //    attention kernels;
@@ -19,8 +22,9 @@
 //    out of row-major A tiles [256 m][32 k] with two 8-byte reads each, in
 //    the k order of the transposing read;
 //  * workgroup tile 128 (n) x 256 (m), 4 waves of 64 x 128, K steps of 32;
-//    LDS double-buffered (one barrier per K step), the global loads of step
-//    s+1 in flight while step s is computed; two workgroups per CU;
+//    one register staging buffer, LDS double-buffered (one barrier per K
+//    step), the global loads of step s+1 in flight while step s is
+//    computed; two workgroups per CU;
 //  * rows past M and columns past N re-read the last valid one (their
 //    outputs are not stored); K is zero-padded to the step (K % 8 == 0).
 // fp32 storage runs a plain FMA kernel (no MFMA), for correctness checks.
