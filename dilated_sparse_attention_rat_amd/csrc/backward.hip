@@ -27,7 +27,8 @@
 //     (h^v_{t-1} - v) with the stored states (h_{-1} = 0).  Chunks of 64
 //     positions, 16-byte accesses per lane as in the forward scan: per-chunk
 //     affine maps, a carry pass over chunks, then the chunks again from
-//     their carries.
+//     their carries.  With several partial anchor gradients, a small kernel
+//     first sums them into the first buffer.
 // The storage rounding of the states enters the derivative as the identity.
 #include "rat_device.h"
 
@@ -632,25 +633,77 @@ struct RCfg {
   static constexpr int CPB = 256 / LPR;     // chunks per workgroup
 };
 
-// the state gradients of position t for the lane's VEC channels: own term
-// (scalars from kernel 1 times q_t and dO_t), window gradient (W > 0) and, at
-// an anchor position, the partial sums of the anchor's gradient
+// Every lane walks its chunk's rows one after another (the recurrence is
+// sequential within a chunk), so the loads of kRBatch consecutive rows are
+// issued together and only then consumed: one memory round trip per batch
+// instead of one per row.
+constexpr int kRBatch = 8;
+
+// Partial anchor gradients summed into split 0 (splits in a fixed order, so
+// the result is deterministic); the reverse scan then reads one buffer.
+__global__ __launch_bounds__(256) void bwd_anchor_sum_kernel(float* dKc, float* dVc, int64_t n4,
+                                                             int nsplit) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4* k = reinterpret_cast<f32x4*>(dKc);
+  f32x4* v = reinterpret_cast<f32x4*>(dVc);
+  f32x4 sk = k[i], sv = v[i];
+  for (int s = 1; s < nsplit; ++s) {
+    sk += k[i + s * n4];
+    sv += v[i + s * n4];
+  }
+  k[i] = sk;
+  v[i] = sv;
+}
+
+// One row's inputs of the state gradient: q_t and dO_t (for the own term),
+// the two own-position scalars and, at an anchor position, the anchor's
+// gradient (split 0 after the sum above).
+template <typename ST>
+struct RowIn {
+  static constexpr int VEC = StTraits<ST>::VEC;
+  u32x4 q, o;
+  f32x2 own;
+  f32x4 ak[VEC / 4], av[VEC / 4];
+};
+
 template <typename ST, int HD>
-__device__ __forceinline__ void dh_row(const BwdParams& p, int b, int h, int64_t bh, int t, int c0,
-                                       int W, int D, float (&k)[StTraits<ST>::VEC],
-                                       float (&v)[StTraits<ST>::VEC]) {
+__device__ __forceinline__ void row_load(const BwdParams& p, int64_t bh, int t, int c0,
+                                         int64_t arow, bool anchor, RowIn<ST>& in) {
   constexpr int VEC = StTraits<ST>::VEC;
   const int64_t i = (bh * p.T + t) * HD + c0;
-  const f32x2 own = *reinterpret_cast<const f32x2*>(p.own + 2 * (bh * p.T + t));
+  in.own = *reinterpret_cast<const f32x2*>(p.own + 2 * (bh * p.T + t));
+  in.q = ld_raw16(reinterpret_cast<const ST*>(p.q) + i);
+  in.o = ld_raw16(reinterpret_cast<const ST*>(p.dO) + i);
+  if (anchor) {
+    const int64_t r = arow * HD + c0;
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) {
+      in.ak[j] = *reinterpret_cast<const f32x4*>(p.dKc + r + 4 * j);
+      in.av[j] = *reinterpret_cast<const f32x4*>(p.dVc + r + 4 * j);
+    }
+  }
+}
+
+// the state gradients of position t for the lane's VEC channels: own term
+// (scalars from kernel 1 times q_t and dO_t), window gradient (W > 0) and, at
+// an anchor position, the anchor's gradient
+template <typename ST, int HD>
+__device__ __forceinline__ void dh_from(const BwdParams& p, int64_t bh, int t, int c0, int W,
+                                        bool anchor, const RowIn<ST>& in,
+                                        float (&k)[StTraits<ST>::VEC],
+                                        float (&v)[StTraits<ST>::VEC]) {
+  constexpr int VEC = StTraits<ST>::VEC;
   float qv[VEC], ov[VEC];
-  unpack16(ld_raw16(reinterpret_cast<const ST*>(p.q) + i), qv, (ST*)nullptr);
-  unpack16(ld_raw16(reinterpret_cast<const ST*>(p.dO) + i), ov, (ST*)nullptr);
+  unpack16(in.q, qv, (ST*)nullptr);
+  unpack16(in.o, ov, (ST*)nullptr);
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    k[e] = own[0] * qv[e];
-    v[e] = own[1] * ov[e];
+    k[e] = in.own[0] * qv[e];
+    v[e] = in.own[1] * ov[e];
   }
   if (W > 0) {
+    const int64_t i = (bh * p.T + t) * HD + c0;
 #pragma unroll
     for (int e = 0; e < VEC; e += 4) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(p.dhk + i + e);
@@ -662,19 +715,11 @@ __device__ __forceinline__ void dh_row(const BwdParams& p, int b, int h, int64_t
       }
     }
   }
-  if (t % D == D - 1) {
-    const int64_t r = ((int64_t)b * p.R + p.ht.aoff[h] + t / D) * HD + c0;
-    for (int s = 0; s < p.nsplit; ++s) {
+  if (anchor) {
 #pragma unroll
-      for (int e = 0; e < VEC; e += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(p.dKc + s * p.kc_split + r + e);
-        const f32x4 c = *reinterpret_cast<const f32x4*>(p.dVc + s * p.kc_split + r + e);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          k[e + j] += a[j];
-          v[e + j] += c[j];
-        }
-      }
+    for (int e = 0; e < VEC; ++e) {
+      k[e] += in.ak[e / 4][e % 4];
+      v[e] += in.av[e / 4][e % 4];
     }
   }
 }
@@ -692,6 +737,7 @@ __global__ __launch_bounds__(256) void bwd_rscan_agg_kernel(const BwdParams p) {
   const int D = p.ht.D[h];
   const int W = p.ht.W[h];
   const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t arow0 = (int64_t)b * p.R + p.ht.aoff[h];
   const ST* gp = reinterpret_cast<const ST*>(p.g) + bh * T * HD + c0;
   const int s = ch * kRChunk;
   const int e = min(T, s + kRChunk) - 1;
@@ -702,17 +748,32 @@ __global__ __launch_bounds__(256) void bwd_rscan_agg_kernel(const BwdParams p) {
     lk[j] = 0.f;
     lv[j] = 0.f;
   }
-  for (int t = e; t >= s; --t) {
-    float gn[VEC];
-    unpack16(ld_raw16(gp + (int64_t)min(t + 1, T - 1) * HD), gn, (ST*)nullptr);
-    float dk[VEC], dv[VEC];
-    dh_row<ST, HD>(p, b, h, bh, t, c0, W, D, dk, dv);
+  for (int t1 = e; t1 >= s; t1 -= kRBatch) {
+    // loads of rows t1, t1-1, ... (clamped to the chunk; the clamped ones
+    // are not used)
+    u32x4 gn[kRBatch];
+    RowIn<ST> in[kRBatch];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      const float gj = t + 1 < T ? gn[j] : 0.f;
-      lk[j] = dk[j] + gj * lk[j];
-      lv[j] = dv[j] + gj * lv[j];
-      A[j] *= gj;
+    for (int u = 0; u < kRBatch; ++u) {
+      const int t = max(t1 - u, s);
+      gn[u] = ld_raw16(gp + (int64_t)min(t + 1, T - 1) * HD);
+      row_load<ST, HD>(p, bh, t, c0, arow0 + t / D, t % D == D - 1, in[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRBatch; ++u) {
+      const int t = t1 - u;
+      if (t >= s) {
+        float gf[VEC], dk[VEC], dv[VEC];
+        unpack16(gn[u], gf, (ST*)nullptr);
+        dh_from<ST, HD>(p, bh, t, c0, W, t % D == D - 1, in[u], dk, dv);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          const float gj = t + 1 < T ? gf[j] : 0.f;
+          lk[j] = dk[j] + gj * lk[j];
+          lv[j] = dv[j] + gj * lv[j];
+          A[j] *= gj;
+        }
+      }
     }
   }
   float* a = p.agg + ((bh * p.nchunk + ch) * 3) * HD + c0;
@@ -724,18 +785,34 @@ __global__ __launch_bounds__(256) void bwd_rscan_agg_kernel(const BwdParams p) {
   }
 }
 
+// lambda after each chunk: one lane per channel walks the chunks backwards,
+// the maps of 16 chunks loaded per round trip
 template <int HD>
 __global__ __launch_bounds__(HD) void bwd_rscan_carry_kernel(const BwdParams p) {
+  constexpr int CB = 16;
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
   float lk = 0.f, lv = 0.f;  // lambda at the position after the chunk
-  for (int ch = p.nchunk - 1; ch >= 0; --ch) {
-    float* cr = p.carry + ((bh * p.nchunk + ch) * 2) * HD + c;
-    cr[0] = lk;
-    cr[HD] = lv;
-    const float* a = p.agg + ((bh * p.nchunk + ch) * 3) * HD + c;
-    lk = a[0] * lk + a[HD];
-    lv = a[0] * lv + a[2 * HD];
+  for (int ch1 = p.nchunk - 1; ch1 >= 0; ch1 -= CB) {
+    float a[CB][3];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float* ap = p.agg + ((bh * p.nchunk + max(ch1 - u, 0)) * 3) * HD + c;
+      a[u][0] = ap[0];
+      a[u][1] = ap[HD];
+      a[u][2] = ap[2 * HD];
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int ch = ch1 - u;
+      if (ch >= 0) {
+        float* cr = p.carry + ((bh * p.nchunk + ch) * 2) * HD + c;
+        cr[0] = lk;
+        cr[HD] = lv;
+        lk = a[u][0] * lk + a[u][1];
+        lv = a[u][0] * lv + a[u][2];
+      }
+    }
   }
 }
 
@@ -752,6 +829,7 @@ __global__ __launch_bounds__(256) void bwd_rscan_apply_kernel(const BwdParams p)
   const int D = p.ht.D[h];
   const int W = p.ht.W[h];
   const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t arow0 = (int64_t)b * p.R + p.ht.aoff[h];
   const int64_t off = bh * T * HD + c0;
   const ST* gp = reinterpret_cast<const ST*>(p.g) + off;
   const ST* kp = reinterpret_cast<const ST*>(p.k) + off;
@@ -771,37 +849,56 @@ __global__ __launch_bounds__(256) void bwd_rscan_apply_kernel(const BwdParams p)
     lv[j] = cr[HD + j];
   }
   // g of the position after t: loaded once before the loop, then the
-  // previous iteration's g_t (each g row is read once per chunk)
+  // previous row's g_t (each g row is read once per chunk)
   float gn[VEC];
   unpack16(ld_raw16(gp + (int64_t)min(e + 1, T - 1) * HD), gn, (ST*)nullptr);
-  for (int t = e; t >= s; --t) {
-    const int64_t r = (int64_t)t * HD;
-    const int64_t rp = (int64_t)max(t - 1, 0) * HD;
-    float gt[VEC], kv[VEC], vv[VEC], pk[VEC], pv[VEC];
-    unpack16(ld_raw16(gp + r), gt, (ST*)nullptr);
-    unpack16(ld_raw16(kp + r), kv, (ST*)nullptr);
-    unpack16(ld_raw16(vp + r), vv, (ST*)nullptr);
-    unpack16(ld_raw16(hkp + rp), pk, (ST*)nullptr);
-    unpack16(ld_raw16(hvp + rp), pv, (ST*)nullptr);
-    float dk[VEC], dv[VEC];
-    dh_row<ST, HD>(p, b, h, bh, t, c0, W, D, dk, dv);
-    float ok[VEC], ov[VEC], og[VEC];
+  for (int t1 = e; t1 >= s; t1 -= kRBatch) {
+    u32x4 G[kRBatch], K[kRBatch], V[kRBatch], PK[kRBatch], PV[kRBatch];
+    RowIn<ST> in[kRBatch];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      const float gj = t + 1 < T ? gn[j] : 0.f;
-      lk[j] = dk[j] + gj * lk[j];
-      lv[j] = dv[j] + gj * lv[j];
-      const float hk_prev = t > 0 ? pk[j] : 0.f;
-      const float hv_prev = t > 0 ? pv[j] : 0.f;
-      ok[j] = (1.f - gt[j]) * lk[j];
-      ov[j] = (1.f - gt[j]) * lv[j];
-      og[j] = lk[j] * (hk_prev - kv[j]) + lv[j] * (hv_prev - vv[j]);
+    for (int u = 0; u < kRBatch; ++u) {
+      const int t = max(t1 - u, s);
+      const int64_t r = (int64_t)t * HD;
+      const int64_t rp = (int64_t)max(t - 1, 0) * HD;
+      G[u] = ld_raw16(gp + r);
+      K[u] = ld_raw16(kp + r);
+      V[u] = ld_raw16(vp + r);
+      PK[u] = ld_raw16(hkp + rp);
+      PV[u] = ld_raw16(hvp + rp);
+      row_load<ST, HD>(p, bh, t, c0, arow0 + t / D, t % D == D - 1, in[u]);
     }
-    st_raw16(dkp + r, pack16(ok, (ST*)nullptr));
-    st_raw16(dvp + r, pack16(ov, (ST*)nullptr));
-    st_raw16(dgp + r, pack16(og, (ST*)nullptr));
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) gn[j] = gt[j];
+    for (int u = 0; u < kRBatch; ++u) {
+      const int t = t1 - u;
+      if (t >= s) {
+        const int64_t r = (int64_t)t * HD;
+        float gt[VEC], kv[VEC], vv[VEC], pk[VEC], pv[VEC];
+        unpack16(G[u], gt, (ST*)nullptr);
+        unpack16(K[u], kv, (ST*)nullptr);
+        unpack16(V[u], vv, (ST*)nullptr);
+        unpack16(PK[u], pk, (ST*)nullptr);
+        unpack16(PV[u], pv, (ST*)nullptr);
+        float dk[VEC], dv[VEC];
+        dh_from<ST, HD>(p, bh, t, c0, W, t % D == D - 1, in[u], dk, dv);
+        float ok[VEC], ov[VEC], og[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          const float gj = t + 1 < T ? gn[j] : 0.f;
+          lk[j] = dk[j] + gj * lk[j];
+          lv[j] = dv[j] + gj * lv[j];
+          const float hk_prev = t > 0 ? pk[j] : 0.f;
+          const float hv_prev = t > 0 ? pv[j] : 0.f;
+          ok[j] = (1.f - gt[j]) * lk[j];
+          ov[j] = (1.f - gt[j]) * lv[j];
+          og[j] = lk[j] * (hk_prev - kv[j]) + lv[j] * (hv_prev - vv[j]);
+        }
+        st_raw16(dkp + r, pack16(ok, (ST*)nullptr));
+        st_raw16(dvp + r, pack16(ov, (ST*)nullptr));
+        st_raw16(dgp + r, pack16(og, (ST*)nullptr));
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) gn[j] = gt[j];
+      }
+    }
   }
 }
 
@@ -820,6 +917,11 @@ int launch_t(const BwdParams& p, hipStream_t st) {
   }
   if (p.nkt > 0)
     hipLaunchKernelGGL((bwd_dkv_kernel<ST, HD>), dim3(ngrp * p.nkt), dim3(256), 0, st, p);
+  if (p.nsplit > 1 && p.kc_split > 0) {
+    const int64_t n4 = p.kc_split / 4;
+    hipLaunchKernelGGL(bwd_anchor_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                       p.dKc, p.dVc, n4, p.nsplit);
+  }
   const int ncb = (p.nchunk + RCfg<ST, HD>::CPB - 1) / RCfg<ST, HD>::CPB;
   hipLaunchKernelGGL((bwd_rscan_agg_kernel<ST, HD>), dim3(ncb, p.H, p.B), dim3(256), 0, st, p);
   hipLaunchKernelGGL((bwd_rscan_carry_kernel<HD>), dim3(p.B * p.H), dim3(HD), 0, st, p);
