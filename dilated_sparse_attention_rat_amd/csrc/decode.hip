@@ -213,21 +213,55 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   }
 }
 
+// Merge of the splits' partials by log-sum-exp.  The splits' maxima and row
+// sums are read by one lane per split and reduced over the workgroup; each
+// channel's accumulators are then summed in split order with the loads of
+// eight splits in flight at a time (a loop with one dependent load per
+// split costs a memory round trip per split).
+template <int HD>
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* s_tmp) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float w = shfl_xor_f(v, o);
+    v = is_max ? fmaxf(v, w) : v + w;
+  }
+  if ((threadIdx.x & 63) == 0) s_tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = s_tmp[0];
+#pragma unroll
+  for (int w = 1; w < HD / 64; ++w) r = is_max ? fmaxf(r, s_tmp[w]) : r + s_tmp[w];
+  __syncthreads();  // s_tmp is reused
+  return r;
+}
+
 template <typename ST, int HD>
 __global__ __launch_bounds__(HD) void decode_combine_kernel(const DecodeParams p) {
   __shared__ float s_red[4];
+  __shared__ float s_tmp[HD / 64];
   const int bhi = blockIdx.x;
   const int b = bhi / p.H;
   const int h = bhi - b * p.H;
   const int c = threadIdx.x;
-  const float* part = p.part + (int64_t)bhi * p.splits * (HD + 2);
-  float M = -1e30f;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, part[s * (HD + 2)]);
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float w = exp2f(part[s * (HD + 2)] - M);
-    L += part[s * (HD + 2) + 1] * w;
-    A += part[s * (HD + 2) + 2 + c] * w;
+  const int S = p.splits;
+  const float* part = p.part + (int64_t)bhi * S * (HD + 2);
+  float m = -1e30f;
+  for (int s = c; s < S; s += HD) m = fmaxf(m, part[s * (HD + 2)]);
+  const float M = block_reduce<HD>(m, true, s_tmp);
+  float l = 0.f;
+  for (int s = c; s < S; s += HD) l += part[s * (HD + 2) + 1] * exp2f(part[s * (HD + 2)] - M);
+  const float L = block_reduce<HD>(l, false, s_tmp);
+  float A = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float mv[8], av[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, S - 1);
+      mv[u] = part[s * (HD + 2)];
+      av[u] = part[s * (HD + 2) + 2 + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) A += av[u] * exp2f(mv[u] - M);
   }
   finish_step<ST, HD>(p, b, h, M, L, A, s_red);
 }

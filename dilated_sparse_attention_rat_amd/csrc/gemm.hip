@@ -208,15 +208,19 @@ __device__ __forceinline__ void lds_barrier() {
 // cannot tell which LDS stage a builtin load writes, and waits for every one
 // in flight before each LDS read.  Nothing is returned in registers (the
 // address is read at issue); completion is waited for with vmcnt before the
-// barrier that publishes a stage.  One wait state separates the M0 write
-// from its use.
+// barrier that publishes a stage.  M0 (the LDS base) is saved and restored
+// around the load, so the compiler's own use of M0 is undisturbed; one wait
+// state separates the M0 write from its use.
 __device__ __forceinline__ void dma16(const void* src, const bf16* dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(
       (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)dst));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(base)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
