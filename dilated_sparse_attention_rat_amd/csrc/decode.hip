@@ -130,23 +130,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
 
-  for (int kb = kbeg + rg; kb < kend; kb += RPP * kU) {
-    u32x4 ku[kU], vu[kU];
-    bool ok[kU];
+  // Rows kb + u*RPP (u < kU) per iteration, the next iteration's loads
+  // issued before this one's rows are consumed (two register sets, the loop
+  // unrolled by two).  Loads past kend re-read row kend-1 (always masked),
+  // so every load is unconditional and waits cover only the rows in use.
+  constexpr int STEP = RPP * kU;
+  auto load = [&](int k0, u32x4 (&ku)[kU], u32x4 (&vu)[kU]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int key = kb + u * RPP;
-      ok[u] = key < kend;
-      if (ok[u]) {
-        const ST* ks = key < na ? kc + (int64_t)key * HD : kr + (int64_t)(key - na) * HD;
-        const ST* vs = key < na ? vc + (int64_t)key * HD : vr + (int64_t)(key - na) * HD;
-        ku[u] = ld_raw16_nt(ks + c0);
-        vu[u] = ld_raw16_nt(vs + c0);
-      } else {
-        ku[u] = u32x4{0u, 0u, 0u, 0u};
-        vu[u] = ku[u];
-      }
+      const int key = min(k0 + u * RPP, kend - 1);
+      const ST* ks = key < na ? kc + (int64_t)key * HD : kr + (int64_t)(key - na) * HD;
+      const ST* vs = key < na ? vc + (int64_t)key * HD : vr + (int64_t)(key - na) * HD;
+      ku[u] = ld_raw16_nt(ks + c0);
+      vu[u] = ld_raw16_nt(vs + c0);
     }
+  };
+  auto consume = [&](int k0, const u32x4 (&ku)[kU], const u32x4 (&vu)[kU]) {
     float sc[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -157,7 +156,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
       for (int i = 0; i < VEC; ++i) d += q[i] * kf[i];
 #pragma unroll
       for (int msk = LPR / 2; msk >= 1; msk >>= 1) d += shfl_xor_f(d, msk);
-      sc[u] = ok[u] ? d : -INFINITY;
+      sc[u] = k0 + u * RPP < kend ? d : -INFINITY;
     }
     float mx = sc[0];
 #pragma unroll
@@ -176,6 +175,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
       unpack16(vu[u], vf, (ST*)nullptr);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] += pu * vf[i];
+    }
+  };
+  {
+    u32x4 ka[kU], va[kU], kn[kU], vn[kU];
+    int kb = kbeg + rg;
+    if (kb < kend) load(kb, ka, va);
+    for (; kb < kend; kb += 2 * STEP) {
+      if (kb + STEP < kend) load(kb + STEP, kn, vn);
+      consume(kb, ka, va);
+      if (kb + STEP >= kend) break;
+      if (kb + 2 * STEP < kend) load(kb + 2 * STEP, ka, va);
+      consume(kb + STEP, kn, vn);
     }
   }
 
