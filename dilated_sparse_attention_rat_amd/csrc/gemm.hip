@@ -239,8 +239,24 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int n0 = blockIdx.x * kWideBN;
-  const int m0 = blockIdx.y * kWideBM;
+  // Tile order.  Workgroup i runs on XCD i % 8 (each XCD has its own L2).
+  // With the plain raster, a grid of 8 n-tiles gives each XCD one n-tile and
+  // every m-tile, so every XCD streams all of A.  When both tile counts are
+  // multiples of 8, XCD x takes m-tiles [x Mt/8, (x+1) Mt/8) and walks the
+  // n-tiles in blocks of 8: at any time its workgroups cover a few m-tiles
+  // by 8 n-tiles, and no A tile is fetched by more than one XCD.
+  int tm = blockIdx.y, tn = blockIdx.x;
+  if ((gridDim.x & 7) == 0 && (gridDim.y & 7) == 0) {
+    const int pid = blockIdx.x + blockIdx.y * gridDim.x;
+    const int x = pid & 7;
+    const int s = pid >> 3;
+    const int mx = gridDim.y >> 3;  // m-tiles per XCD
+    const int r = s % (mx * 8);
+    tm = x * mx + r / 8;
+    tn = (s / (mx * 8)) * 8 + (r & 7);
+  }
+  const int n0 = tn * kWideBN;
+  const int m0 = tm * kWideBM;
   const int wn = wave & 1;   // wave's n offset 128*wn (its B half)
   const int wm = wave >> 1;  // wave's m offset 128*wm
   const int N = p.ngroups * p.Ng;
