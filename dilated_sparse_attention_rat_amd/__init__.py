@@ -10,6 +10,7 @@ from .binding import (RAT_DTYPE_BF16, RAT_DTYPE_F32, RAT_ERR_CAPACITY,  # noqa: 
                       alloc_cache, backward_workspace, decode_workspace, lib,
                       layer_workspace, rat_anchor_rows, rat_layer_prefill,
                       rat_layer_workspace_bytes, rat_prefill_backward,
+                      rat_stack_prefill, rat_stack_workspace_bytes, stack_workspace,
                       rat_prefill_backward_workspace_bytes,
                       rat_decode_step, rat_decode_step_noalloc, rat_decode_workspace_bytes,
                       rat_dilated_attn_prefill,

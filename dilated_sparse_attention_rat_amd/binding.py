@@ -35,6 +35,7 @@ EXPORTED = [
     "rat_decode_workspace_bytes", "rat_decode_step", "rat_decode_step_noalloc",
     "rat_prefill_backward_workspace_bytes", "rat_prefill_backward",
     "rat_layer_workspace_bytes", "rat_layer_prefill",
+    "rat_stack_workspace_bytes", "rat_stack_prefill",
     "rat_topk_cache_build", "rat_decode_step_topk",
 ]
 
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.rat_layer_workspace_bytes.restype = i64
         L.rat_layer_prefill.argtypes = [i32, i32, i32, i64, i32, i32, P, P, f32, i64] + [P] * 16 + [sz, P]
         L.rat_layer_prefill.restype = i32
+        L.rat_stack_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32]
+        L.rat_stack_workspace_bytes.restype = i64
+        L.rat_stack_prefill.argtypes = [i32, i32, i32, i32, i64, i32, i32, P, P, f32, i64] + [P] * 15 + [sz, P]
+        L.rat_stack_prefill.restype = i32
         L.rat_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, P, P, i32]
         L.rat_decode_workspace_bytes.restype = i64
         L.rat_decode_step.argtypes = [i32, i32, i32, i32, P, P, f32, i64, i64,
@@ -529,6 +534,68 @@ def rat_layer_prefill(x, w_q, w_k, w_v, w_g, b_g, w_o, out, D, W, H: int, hd: in
     args += [ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
              _stream(stream, dev)]
     _check("rat_layer_prefill", lib().rat_layer_prefill(*args))
+
+
+def rat_stack_workspace_bytes(dtype_code: int, B: int, H: int, T: int, hd: int, dm: int) -> int:
+    r = lib().rat_stack_workspace_bytes(dtype_code, B, H, T, hd, dm)
+    if r < 0:
+        raise RatError("rat_stack_workspace_bytes", int(r))
+    return int(r)
+
+
+def rat_stack_prefill(x, layers, out, H: int, hd: int, T_cap: int, caches, workspace,
+                      scale: float = 0.0, stream=None):
+    """A stack of RAT+ layers over a prefill (layer-wise hybrid).  x, out:
+    [B,T,dm]; layers: one dict per layer with D, W (per head) and w_q, w_k,
+    w_v, w_g, b_g, w_o as for rat_layer_prefill; caches: one alloc_cache dict
+    per layer (sized by that layer's D and W)."""
+    torch = _torch()
+    B, T, dm = x.shape
+    st = x.dtype
+    dev = x.device
+    n = len(layers)
+    if n < 1 or len(caches) != n:
+        raise ValueError("one cache per layer, at least one layer")
+    HD = H * hd
+    D = np.ascontiguousarray(np.stack([_heads(l["D"], H) for l in layers]).astype(np.int32))
+    W = np.ascontiguousarray(np.stack([_heads(l["W"], H) for l in layers]).astype(np.int32))
+    arrs = {k: (ctypes.c_void_p * n)() for k in
+            ("w_q", "w_k", "w_v", "w_g", "b_g", "w_o", "Kc", "Vc", "k_ring", "v_ring",
+             "state_k", "state_v")}
+    for i, (ly, c) in enumerate(zip(layers, caches)):
+        R, _ = rat_anchor_rows(H, T_cap, D[i])
+        WS, _ = rat_ring_rows(H, W[i])
+        for k in ("w_q", "w_k", "w_v", "w_g"):
+            arrs[k][i] = _dev(ly[k], k, (dm, HD), st, dev)
+        arrs["b_g"][i] = _dev(ly["b_g"], "b_g", (HD,), torch.float32, dev)
+        arrs["w_o"][i] = _dev(ly["w_o"], "w_o", (HD, dm), st, dev)
+        arrs["Kc"][i] = _opt(c["Kc"], "Kc", (B, R, hd), st, dev)
+        arrs["Vc"][i] = _opt(c["Vc"], "Vc", (B, R, hd), st, dev)
+        arrs["k_ring"][i] = _opt(c["k_ring"], "k_ring", (B, WS, hd), st, dev)
+        arrs["v_ring"][i] = _opt(c["v_ring"], "v_ring", (B, WS, hd), st, dev)
+        arrs["state_k"][i] = _dev(c["state_k"], "state_k", (B, H, hd), torch.float32, dev)
+        arrs["state_v"][i] = _dev(c["state_v"], "state_v", (B, H, hd), torch.float32, dev)
+    need = rat_stack_workspace_bytes(_dtype_code(x), B, H, T, hd, dm)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    args = [_dtype_code(x), n, B, H, T, hd, dm, _ptr(D), _ptr(W), float(scale), T_cap,
+            _dev(x, "x", (B, T, dm), st, dev)]
+    args += [ctypes.cast(arrs[k], ctypes.c_void_p) for k in ("w_q", "w_k", "w_v", "w_g", "b_g", "w_o")]
+    args += [_dev(out, "out", (B, T, dm), st, dev)]
+    args += [ctypes.cast(arrs[k], ctypes.c_void_p)
+             for k in ("Kc", "Vc", "k_ring", "v_ring", "state_k", "state_v")]
+    args += [ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+             _stream(stream, dev)]
+    _check("rat_stack_prefill", lib().rat_stack_prefill(*args))
+
+
+def stack_workspace(dtype_code: int, B: int, H: int, T: int, hd: int, dm: int, device):
+    """Zero-filled stack workspace (zero it again only after a failed call)."""
+    torch = _torch()
+    n = rat_stack_workspace_bytes(dtype_code, B, H, T, hd, dm)
+    return torch.zeros(((n + 15) // 16) * 4, dtype=torch.int32, device=device)
 
 
 def layer_workspace(dtype_code: int, B: int, H: int, T: int, hd: int, device):

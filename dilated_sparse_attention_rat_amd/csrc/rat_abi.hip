@@ -797,16 +797,22 @@ int64_t rat_layer_workspace_bytes(int dtype, int B, int H, int64_t T, int hd) {
   return L.bytes;
 }
 
-int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const int32_t* D,
-                      const int32_t* W, float scale, int64_t T_cap, const void* x,
-                      const void* w_q, const void* w_k, const void* w_v, const void* w_g,
-                      const float* b_g, const void* w_o, void* out, float* lse, void* Kc,
-                      void* Vc, void* k_ring, void* v_ring, float* state_k, float* state_v,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Every check rat_layer_prefill (and the scan and attention it runs) makes
+// before launching anything.  RAT_OK with nothing to do when B, H or T is 0.
+int layer_check(int dtype, int B, int H, int64_t T, int hd, int dm, const int32_t* D,
+                const int32_t* W, float scale, int64_t T_cap, const void* x, const void* w_q,
+                const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                const void* w_o, const void* out, const float* lse, const void* Kc,
+                const void* Vc, const void* k_ring, const void* v_ring, const float* state_k,
+                const float* state_v, const void* workspace, size_t workspace_bytes) {
   int st = check_common(dtype, B, H, hd, D, W);
   if (st != RAT_OK) return st;
   if (T < 0 || T_cap > kMaxT || dm <= 0) return RAT_ERR_INVALID_ARG;
   if (T > T_cap) return RAT_ERR_CAPACITY;
+  if (!(scale <= 0.f) && !std::isfinite(scale)) return RAT_ERR_INVALID_ARG;
   if (B == 0 || H == 0 || T == 0) return RAT_OK;
   const void* ptrs[] = {x, w_q, w_k, w_v, w_g, b_g, w_o, out};
   for (const void* ptr : ptrs)
@@ -822,6 +828,32 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const 
   if (!layer_layout(dtype, B, H, T, hd, L)) return RAT_ERR_UNSUPPORTED;
   if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < L.bytes)
     return RAT_ERR_WORKSPACE;
+  // the cache the scan and attention write and read
+  HeadTables ht;
+  int64_t R, WS;
+  st = fill_tables(H, T_cap, D, W, ht, R, WS);
+  if (st != RAT_OK) return st;
+  if (state_k == nullptr || state_v == nullptr || !aligned16(state_k) || !aligned16(state_v))
+    return RAT_ERR_INVALID_ARG;
+  if (WS > 0 && (!k_ring || !v_ring || !aligned16(k_ring) || !aligned16(v_ring)))
+    return RAT_ERR_INVALID_ARG;
+  if (R > 0 && (!Kc || !Vc || !aligned16(Kc) || !aligned16(Vc))) return RAT_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return RAT_ERR_INVALID_ARG;
+  return RAT_OK;
+}
+
+// The launches of one layer (arguments already checked by layer_check).
+int layer_run(int dtype, int B, int H, int64_t T, int hd, int dm, const int32_t* D,
+              const int32_t* W, float scale, int64_t T_cap, const void* x, const void* w_q,
+              const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+              const void* w_o, void* out, float* lse, void* Kc, void* Vc, void* k_ring,
+              void* v_ring, float* state_k, float* state_v, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  if (B == 0 || H == 0 || T == 0) return RAT_OK;
+  const int64_t HD = (int64_t)H * hd;
+  LayerLayout L;
+  layer_layout(dtype, B, H, T, hd, L);
+  int st = RAT_OK;
   char* ws = static_cast<char*>(workspace);
   char* act = ws + L.off_act;
   void* q = act;
@@ -876,6 +908,87 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const 
   gp.ldc = dm;
   st = map_hip(launch_gemm(dtype, gp, stream));
   if (st != RAT_OK) return st;
+  return RAT_OK;
+}
+
+
+// Stack workspace: one layer workspace (reused layer after layer), then the
+// activations between layers [B, T, dm].
+int64_t stack_tmp_offset(int dtype, int B, int H, int64_t T, int hd) {
+  LayerLayout L;
+  if (!layer_layout(dtype, B, H, T, hd, L)) return -1;
+  return (L.bytes + 255) / 256 * 256;
+}
+}  // namespace
+
+extern "C" {
+
+int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm, const int32_t* D,
+                      const int32_t* W, float scale, int64_t T_cap, const void* x,
+                      const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+                      const float* b_g, const void* w_o, void* out, float* lse, void* Kc,
+                      void* Vc, void* k_ring, void* v_ring, float* state_k, float* state_v,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = layer_check(dtype, B, H, T, hd, dm, D, W, scale, T_cap, x, w_q, w_k, w_v, w_g,
+                             b_g, w_o, out, lse, Kc, Vc, k_ring, v_ring, state_k, state_v,
+                             workspace, workspace_bytes);
+  if (st != RAT_OK) return st;
+  return layer_run(dtype, B, H, T, hd, dm, D, W, scale, T_cap, x, w_q, w_k, w_v, w_g, b_g, w_o,
+                   out, lse, Kc, Vc, k_ring, v_ring, state_k, state_v, workspace, workspace_bytes,
+                   stream);
+}
+
+int64_t rat_stack_workspace_bytes(int dtype, int B, int H, int64_t T, int hd, int dm) {
+  const int64_t lw = rat_layer_workspace_bytes(dtype, B, H, T, hd);
+  if (lw < 0) return lw;
+  if (dm <= 0 || B < 0 || T < 0) return RAT_ERR_INVALID_ARG;
+  const int64_t es = dtype == RAT_DTYPE_BF16 ? 2 : 4;
+  return stack_tmp_offset(dtype, B, H, T, hd) + (int64_t)B * T * dm * es;
+}
+
+int rat_stack_prefill(int dtype, int nlayers, int B, int H, int64_t T, int hd, int dm,
+                      const int32_t* D, const int32_t* W, float scale, int64_t T_cap,
+                      const void* x, const void* const* w_q, const void* const* w_k,
+                      const void* const* w_v, const void* const* w_g, const float* const* b_g,
+                      const void* const* w_o, void* out, void* const* Kc, void* const* Vc,
+                      void* const* k_ring, void* const* v_ring, float* const* state_k,
+                      float* const* state_v, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (nlayers < 1 || !D || !W || !w_q || !w_k || !w_v || !w_g || !b_g || !w_o || !Kc || !Vc ||
+      !k_ring || !v_ring || !state_k || !state_v)
+    return RAT_ERR_INVALID_ARG;
+  const int64_t need = rat_stack_workspace_bytes(dtype, B, H, T, hd, dm);
+  if (need < 0) return (int)need;
+  if (B == 0 || H == 0 || T == 0) {
+    for (int l = 0; l < nlayers; ++l) {
+      const int st = check_common(dtype, B, H, hd, D + (int64_t)l * H, W + (int64_t)l * H);
+      if (st != RAT_OK) return st;
+    }
+    return T > T_cap ? RAT_ERR_CAPACITY : RAT_OK;
+  }
+  if (workspace == nullptr || !aligned16(workspace) || (int64_t)workspace_bytes < need)
+    return RAT_ERR_WORKSPACE;
+  char* tmp = static_cast<char*>(workspace) + stack_tmp_offset(dtype, B, H, T, hd);
+  const size_t lw = (size_t)stack_tmp_offset(dtype, B, H, T, hd);
+  // layer l reads x (l = 0) or the activations between layers, and writes
+  // them (out for the last layer); a layer reads its input only in its first
+  // launch and writes its output in its last, so one buffer serves both
+  auto in_of = [&](int l) -> const void* { return l == 0 ? x : tmp; };
+  auto out_of = [&](int l) -> void* { return l == nlayers - 1 ? out : tmp; };
+  for (int l = 0; l < nlayers; ++l) {
+    const int st = layer_check(dtype, B, H, T, hd, dm, D + (int64_t)l * H, W + (int64_t)l * H,
+                               scale, T_cap, in_of(l), w_q[l], w_k[l], w_v[l], w_g[l], b_g[l],
+                               w_o[l], out_of(l), nullptr, Kc[l], Vc[l], k_ring[l], v_ring[l],
+                               state_k[l], state_v[l], workspace, lw);
+    if (st != RAT_OK) return st;
+  }
+  for (int l = 0; l < nlayers; ++l) {
+    const int st = layer_run(dtype, B, H, T, hd, dm, D + (int64_t)l * H, W + (int64_t)l * H,
+                             scale, T_cap, in_of(l), w_q[l], w_k[l], w_v[l], w_g[l], b_g[l],
+                             w_o[l], out_of(l), nullptr, Kc[l], Vc[l], k_ring[l], v_ring[l],
+                             state_k[l], state_v[l], workspace, lw, stream);
+    if (st != RAT_OK) return st;
+  }
   return RAT_OK;
 }
 

@@ -399,6 +399,39 @@ int rat_layer_prefill(int dtype, int B, int H, int64_t T, int hd, int dm,
                       float* state_k, float* state_v, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace rat_stack_prefill needs: one layer workspace
+ * (reused by every layer) and the activations between layers [B, T, dm].
+ * Zero-fill it once (the scan workspace inside it is reused across calls);
+ * negative status on invalid sizes.
+ */
+int64_t rat_stack_workspace_bytes(int dtype, int B, int H, int64_t T, int hd, int dm);
+
+/*
+ * A stack of nlayers RAT+ layers over a prefill, each with its own D and W
+ * per head: the layer-wise hybrid of the deep dive, section 六 (some layers
+ * dense, D = 1, others dilated), and the RAT+ abstract's hybrid layer
+ * compositions.  Layer l is rat_layer_prefill on the previous layer's output
+ * (layer 0 on x): x_{l+1} = out_l, stored in the storage type between
+ * layers.  The pages give no residual path or normalisation around a layer,
+ * so none is applied.
+ * D, W: host int32 [nlayers][H].  w_q, w_k, w_v, w_g, b_g, w_o: host arrays
+ * of nlayers device pointers with the shapes of rat_layer_prefill.  Kc, Vc,
+ * k_ring, v_ring, state_k, state_v: host arrays of nlayers device pointers,
+ * each layer's cache as rat_layer_prefill (sized by that layer's D and W).
+ * Writes out [B, T, dm] and every layer's cache.  Every layer's arguments
+ * are checked before the first launch, so a failed call writes nothing.
+ * workspace: rat_stack_workspace_bytes bytes.  No lse is produced.
+ */
+int rat_stack_prefill(int dtype, int nlayers, int B, int H, int64_t T, int hd, int dm,
+                      const int32_t* D, const int32_t* W, float scale, int64_t T_cap,
+                      const void* x, const void* const* w_q, const void* const* w_k,
+                      const void* const* w_v, const void* const* w_g,
+                      const float* const* b_g, const void* const* w_o, void* out,
+                      void* const* Kc, void* const* Vc, void* const* k_ring,
+                      void* const* v_ring, float* const* state_k, float* const* state_v,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

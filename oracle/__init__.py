@@ -10,6 +10,6 @@ against closed forms, brute force and library routines; nothing in it is
 """
 from .oracle import (anchor_offsets, attention, attention_rows, backward, build,  # noqa: F401
                      build_cache, decode_step, in_keyset, keyset_size, layer_prefill, lib,
-                     num_threads, prefill, round_bf16, scan, set_threads)
+                     num_threads, prefill, round_bf16, scan, set_threads, stack_prefill)
 from .topk import (TOPK_BLOCK, block_means, decode_step_topk, keys_topk,  # noqa: F401
                    select_blocks)

@@ -269,3 +269,22 @@ def layer_prefill(x, w_q, w_k, w_v, w_g, b_g, w_o, H: int, hd: int, D, W, scale,
     o = rnd(r["o"]).transpose(0, 2, 1, 3).reshape(B, T, H * hd)
     r["out"] = o @ _f64(w_o)
     return r
+
+
+def stack_prefill(x, layers, H: int, hd: int, scale, st_bf16: bool):
+    """A stack of layers over a prefill (the layer-wise hybrid: each layer
+    has its own per-head D and W).  layers: one dict per layer with D, W,
+    w_q, w_k, w_v, w_g, b_g, w_o.  The input of layer l+1 is the out of
+    layer l rounded to the storage type, as stored between layers; nothing
+    else (no residual, no normalisation) joins them.  Returns the list of
+    per-layer results of layer_prefill; the last one's "out" is the stack's
+    output (not rounded)."""
+    rnd = round_bf16 if st_bf16 else (lambda a: a)
+    res = []
+    h = _f64(x)
+    for i, ly in enumerate(layers):
+        if i > 0:
+            h = rnd(res[-1]["out"])
+        res.append(layer_prefill(h, ly["w_q"], ly["w_k"], ly["w_v"], ly["w_g"], ly["b_g"],
+                                 ly["w_o"], H, hd, ly["D"], ly["W"], scale, st_bf16))
+    return res

@@ -234,6 +234,40 @@ def test_layer_validation(L):
     assert layer(B=0) == rb.RAT_OK
 
 
+
+def test_stack_validation(L):
+    """The stack checks every layer before its first launch: a bad second
+    layer (a zero D, a missing weight) is an error with nothing run."""
+    H, n = 2, 2
+    assert L.rat_stack_workspace_bytes(0, 1, H, 100, 128, 64) > \
+        L.rat_layer_workspace_bytes(0, 1, H, 100, 128)
+    assert L.rat_stack_workspace_bytes(0, 1, H, 100, 128, 0) == rb.RAT_ERR_INVALID_ARG
+    assert L.rat_stack_workspace_bytes(0, 1, H, 100, 96, 64) == rb.RAT_ERR_UNSUPPORTED
+
+    def stack(nl=n, D=4, D2=4, T=16, T_cap=16, ws_bytes=1 << 30, B=1, null_wo2=False,
+              null_arr=False):
+        d = np.full((max(nl, 1), H), D, np.int32)
+        d[-1] = D2
+        w = np.zeros((max(nl, 1), H), np.int32)
+        arr = (ctypes.c_void_p * max(nl, 1))(*([FAKE] * max(nl, 1)))
+        wo = (ctypes.c_void_p * max(nl, 1))(*([FAKE] * max(nl, 1)))
+        if null_wo2:
+            wo[nl - 1] = None
+        a = None if null_arr else arr
+        return L.rat_stack_prefill(0, nl, B, H, T, 64, 64, d.ctypes.data_as(ctypes.c_void_p),
+                                   w.ctypes.data_as(ctypes.c_void_p), 0.0, T_cap, _p(),
+                                   a, arr, arr, arr, arr, wo, _p(), arr, arr, arr, arr, arr, arr,
+                                   _p(), ws_bytes, None)
+
+    assert stack(nl=0) == rb.RAT_ERR_INVALID_ARG
+    assert stack(null_arr=True) == rb.RAT_ERR_INVALID_ARG
+    assert stack(D2=0) == rb.RAT_ERR_INVALID_ARG
+    assert stack(null_wo2=True) == rb.RAT_ERR_INVALID_ARG
+    assert stack(T=17) == rb.RAT_ERR_CAPACITY
+    assert stack(ws_bytes=64) == rb.RAT_ERR_WORKSPACE
+    assert stack(B=0) == rb.RAT_OK
+    assert stack(B=0, D2=0) == rb.RAT_ERR_INVALID_ARG
+
 def _dec(L, dtype=0, B=1, H=2, hd=64, D=4, W=0, pos=5, T_cap=16, splits=0, ws=0, ws_bytes=0,
          q=FAKE):
     d, w, dp, wp = _tables(H, D, W)

@@ -486,6 +486,79 @@ def test_layer_projections_bruteforce():
     np.testing.assert_allclose(r["out"], out, rtol=1e-10, atol=1e-12)
 
 
+
+def _one_channel_layer(x, D, a, wo, scale, rnd):
+    """Closed form of a layer with H = hd = d_model = 1, input projections
+    q = k = v = a*x (rounded to the storage type, as stored) and a gate of
+    exactly 0 (b_g = -1000: the recurrence then hands its input through),
+    written from the definitions: the query at t attends to its own position
+    and to the stride-D anchors j < t (j mod D = D-1), softmax with the given
+    scale; out = o * wo with o as stored."""
+    h = [rnd(a * v) for v in x]
+    out = []
+    for t in range(len(h)):
+        keys = [j for j in range(t + 1) if j == t or j % D == D - 1]
+        e = [math.exp(scale * h[t] * h[j]) for j in keys]
+        o = sum(w * h[j] for w, j in zip(e, keys)) / sum(e)
+        out.append(rnd(o) * wo)
+    return out
+
+
+@pytest.mark.parametrize("st_bf16", [False, True], ids=["f64", "bf16"])
+def test_stack_two_layers_closed_form(st_bf16):
+    """Two layers of different dilation (D = 1, then D = 2) over T = 5: the
+    stack's output is the closed form of the second layer applied to the
+    first one's output, rounded to the storage type in between.  Swapping
+    the layers, or (bf16) handing the unrounded output over, gives another
+    result, so a stack that runs its layers in the wrong order, skips one or
+    hands over the wrong tensor fails."""
+    def rnd(v):
+        return float(oracle.round_bf16(np.array([v]))[0]) if st_bf16 else v
+
+    x = [0.9, -1.3, 0.4, 2.1, -0.7]
+    zero = np.zeros((1, 1))
+
+    def layer(D, a, wo):
+        w = np.full((1, 1), a)
+        return dict(D=[D], W=[0], w_q=w, w_k=w, w_v=w, w_g=zero, b_g=np.array([-1000.0]),
+                    w_o=np.full((1, 1), wo))
+
+    scale = 0.8
+    res = oracle.stack_prefill(np.array(x).reshape(1, 5, 1),
+                               [layer(1, 1.0, 1.7), layer(2, 1.3, -0.6)], 1, 1, scale, st_bf16)
+    mid = _one_channel_layer(x, 1, 1.0, 1.7, scale, rnd)
+    ref = _one_channel_layer([rnd(v) for v in mid], 2, 1.3, -0.6, scale, rnd)
+    np.testing.assert_allclose(res[0]["out"].ravel(), mid, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(res[1]["out"].ravel(), ref, rtol=1e-12, atol=0)
+    swapped = _one_channel_layer(
+        [rnd(v) for v in _one_channel_layer(x, 2, 1.3, -0.6, scale, rnd)], 1, 1.0, 1.7, scale, rnd)
+    assert np.abs(np.array(swapped) - np.array(ref)).max() > 1e-3
+    if st_bf16:
+        unrounded = _one_channel_layer(mid, 2, 1.3, -0.6, scale, rnd)
+        assert np.abs(np.array(unrounded) - np.array(ref)).max() > 1e-3
+
+
+def test_stack_zero_output_projection_propagates_zeros():
+    """A layer whose W_o is zero hands the next layer x = 0: its projections
+    and states are then 0 and so is every later layer's output, whatever its
+    weights; the first layer's own state is untouched by that."""
+    B, T, H, hd, dm = 2, 20, 2, 4, 6
+    HD = H * hd
+
+    def layer(wo, D, W):
+        return dict(D=D, W=W, w_q=_rand((dm, HD)), w_k=_rand((dm, HD)), w_v=_rand((dm, HD)),
+                    w_g=_rand((dm, HD)), b_g=_rand((HD,)), w_o=wo)
+
+    ls = [layer(np.zeros((HD, dm)), [3, 1], [2, 0]), layer(_rand((HD, dm)), [1, 5], [0, 3]),
+          layer(_rand((HD, dm)), [2, 2], [1, 1])]
+    x = _rand((B, T, dm))
+    res = oracle.stack_prefill(x, ls, H, hd, 0.5, False)
+    assert np.abs(res[0]["state_k"]).max() > 0
+    for r in res:
+        assert np.all(r["out"] == 0.0)
+    for r in res[1:]:
+        assert np.all(r["state_k"] == 0.0) and np.all(r["state_v"] == 0.0)
+
 MUTANTS = [
     ("backward drops the softmax mean", "const double ds = p[j] * (dp[j] - delta);",
      "const double ds = p[j] * dp[j];", ["backward"]),
