@@ -10,7 +10,7 @@
 // 2.1 -- the forget gate is input dependent (a projection of x).
 //
 // Design (bf16, gfx950): the main kernel is gemm_bf16_dma_kernel below
-// (K % 32 == 0): 256 x 256 tiles on 32x32x16 MFMAs at one wave per SIMD,
+// (K % 32 == 0): 256 x 256 tiles on 32x32x16 MFMAs at two waves per SIMD,
 // direct-to-LDS loads, output regrouped through LDS.  gemm_bf16_kernel
 // covers any K % 8 == 0:
 //  * it computes C^T = B^T A^T on v_mfma_f32_16x16x32_bf16, so an
@@ -160,13 +160,14 @@ void gemm_bf16_kernel(const GemmParams p) {
 }
 
 // Direct-to-LDS variant (bf16, K % 32 == 0): workgroup tile 256 (n) x 256
-// (m), 4 waves of 128 x 128, one workgroup per CU, on
-// v_mfma_f32_32x32x16_bf16.  A lone wave per SIMD keeps the matrix pipe full
-// with the 32 x 32 form (the 16 x 16 form reaches about 57% of the bf16 rate
-// from one wave, measured), and has 512 registers, so its 128 x 128 fp32
-// accumulators (256 registers) sit in the accumulation registers; per FLOP
-// the tile reads half the LDS bytes and half the global bytes of a
-// 128-wide tile.  Every K step's tiles are fetched with
+// (m), 8 waves of 64 (n) x 128 (m), two per SIMD, one workgroup per CU, on
+// v_mfma_f32_32x32x16_bf16 (the 32 x 32 form keeps the matrix pipe busier
+// from few waves than the 16 x 16 form, which reaches about 57% of the bf16
+// rate from one wave per SIMD, measured).  A wave's 64 x 128 fp32
+// accumulators take 128 registers, so two waves fit a SIMD: one wave's LDS
+// reads and waits run beside the other's MFMAs (6% faster than four waves
+// of 128 x 128 at one per SIMD, measured).  Per FLOP the workgroup tile
+// reads half the global bytes of a 128-wide tile.  Every K step's tiles are fetched with
 // global_load_lds_dwordx4 (lane l's 16 bytes land at the instruction's LDS
 // base + 16 l, checked on the device), so no register staging: a ring of
 // four LDS stages (32 KB each) holds the step being computed and the three
@@ -174,9 +175,10 @@ void gemm_bf16_kernel(const GemmParams p) {
 //  * Fragments: MFMA lane l covers row l % 32 of its operand and k slots
 //    8 (l / 32) + s.  A^T fragments are single 16-byte reads of the
 //    row-major A tile [256 m][32 k]; B^T fragments come out of two
-//    transposing reads of the B tile (two halves of [32 k][128 n], one per
-//    wave column), 16-lane group G reading k rows 8 (G / 2) + 0..3 (then 4
-//    on) of columns 16 (G % 2) + 0..15.
+//    transposing reads of the B tile (two halves of [32 k][128 n]; wave
+//    column wn reads columns 64 (wn % 2) .. +63 of half wn / 2), 16-lane
+//    group G reading k rows 8 (G / 2) + 0..3 (then 4 on) of columns
+//    16 (G % 2) + 0..15 of a 32-column block.
 //  * Swizzles (tiles unpadded): A row r holds 16-byte chunk c at
 //    c ^ ((r >> 2) & 3), so 16 lanes reading 16 rows cover all banks; B row
 //    r holds chunk c at c ^ 4 (r & 3), so the 4 rows x 64 bytes of one
@@ -225,7 +227,7 @@ __device__ __forceinline__ void dma16(const void* src, const bf16* dst) {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_dma_kernel(const GemmParams p) {
   // one array per stage, indexed statically
   __shared__ __attribute__((aligned(1024))) bf16 sA0[kWideAStage];
@@ -257,25 +259,25 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
   }
   const int n0 = tn * kWideBN;
   const int m0 = tm * kWideBM;
-  const int wn = wave & 1;   // wave's n offset 128*wn (its B half)
-  const int wm = wave >> 1;  // wave's m offset 128*wm
+  const int wn = wave & 3;   // wave's n offset 64*wn (B half wn / 2)
+  const int wm = wave >> 2;  // wave's m offset 128*wm
   const int N = p.ngroups * p.Ng;
 
-  // this lane's sources: A instruction j < 4 covers rows 16 (4 wave + j) ..
-  // +15 of the tile; B instruction j < 4 is number q = 4 wave + j of the
+  // this lane's sources: A instruction j < 2 covers rows 16 (2 wave + j) ..
+  // +15 of the tile; B instruction j < 2 is number q = 2 wave + j of the
   // sixteen, rows 4 (q % 8) .. +3 of half q / 8
-  const bf16* asrc[4];
+  const bf16* asrc[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 16 * (4 * wave + j) + (lane >> 2);
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * (2 * wave + j) + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);
     const int m = min(m0 + row, p.M - 1);
     asrc[j] = reinterpret_cast<const bf16*>(p.A) + (int64_t)m * p.lda + 8 * c;
   }
-  const bf16* bsrc[4];
+  const bf16* bsrc[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = 4 * wave + j;
+  for (int j = 0; j < 2; ++j) {
+    const int q = 2 * wave + j;
     const int row = 4 * (q & 7) + (lane >> 4);
     const int c = (lane & 15) ^ (4 * (row & 3));
     const int n = min(n0 + 128 * (q >> 3) + 8 * c, N - 8);
@@ -285,17 +287,17 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
   auto issue = [&](bf16* __restrict__ sa, bf16* __restrict__ sb, int ks) {
     const int64_t k0 = (int64_t)ks * kGemmBK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(asrc[j] + k0, sa + (4 * wave + j) * 16 * kGemmBK);
+    for (int j = 0; j < 2; ++j) dma16(asrc[j] + k0, sa + (2 * wave + j) * 16 * kGemmBK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = 4 * wave + j;
+    for (int j = 0; j < 2; ++j) {
+      const int q = 2 * wave + j;
       dma16(bsrc[j] + k0 * p.ldb, sb + (q >> 3) * kWideHalf + (q & 7) * 4 * 128);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -308,7 +310,7 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
   const int G = lane >> 4;
   const int tj = (lane >> 2) & 3;
   const int tq = lane & 3;
-  const int bofs = wn * kWideHalf + (8 * (G >> 1) + tj) * 128 + 4 * (tq & 1);
+  const int bofs = (wn >> 1) * kWideHalf + (8 * (G >> 1) + tj) * 128 + 4 * (tq & 1);
   auto read_a = [&](const bf16* __restrict__ sa, int kh, Frag<bf16>* af) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -318,14 +320,14 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
   };
   auto read_b = [&](const bf16* __restrict__ sb, int kh, Frag<bf16>* bf) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int c = 4 * nb + 2 * (G & 1) + (tq >> 1);
+    for (int nb = 0; nb < 2; ++nb) {
+      const int c = 8 * (wn & 1) + 4 * nb + 2 * (G & 1) + (tq >> 1);
       bf[nb] = frag_ld_tr(sb + bofs + kh * 16 * 128 + 8 * (c ^ (4 * tj)), 4 * 128);
     }
   };
   auto mma_half = [&](const Frag<bf16>* bf, const Frag<bf16>* af) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[nb].v, af[mb].v, acc[nb][mb], 0, 0, 0);
@@ -335,23 +337,23 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
   // Step s computes stage s % 4: its first k half from fragments read ahead,
   // its second from fragments read at the step's start.  Between the two,
   // once this thread's loads of step s + 1 are done (those of step s + 2,
-  // eight, may still be in flight), the barrier makes every wave's part of
+  // four, may still be in flight), the barrier makes every wave's part of
   // step s + 1 visible and frees stage (s + 3) % 4, last read at step s - 1,
   // for the loads of step s + 3; the first half's fragments of step s + 1
   // are then read under the second half's MFMAs, and the barrier wait sits
   // under the first half's.
-  Frag<bf16> af0[4], bf0[4];
+  Frag<bf16> af0[4], bf0[2];
   auto step = [&](int s, const bf16* __restrict__ sa, const bf16* __restrict__ sb,
                   const bf16* __restrict__ sa1, const bf16* __restrict__ sb1,
                   bf16* __restrict__ na, bf16* __restrict__ nb2) {
     if (s >= nks) return;
-    Frag<bf16> af1[4], bf1[4];
+    Frag<bf16> af1[4], bf1[2];
     read_a(sa, 1, af1);
     read_b(sb, 1, bf1);
     mma_half(bf0, af0);
     if (s + 1 < nks) {
       if (s + 2 < nks)
-        RAT_WAIT_VM_LGKM(8);
+        RAT_WAIT_VM_LGKM(4);
       else
         RAT_WAIT_VM_LGKM(0);
       lds_barrier();
@@ -365,9 +367,9 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
   if (nks > 1) issue(sA1, sB1, 1);
   if (nks > 2) issue(sA2, sB2, 2);
   if (nks > 2)
-    RAT_WAIT_VM_LGKM(16);
-  else if (nks > 1)
     RAT_WAIT_VM_LGKM(8);
+  else if (nks > 1)
+    RAT_WAIT_VM_LGKM(4);
   else
     RAT_WAIT_VM_LGKM(0);
   lds_barrier();
@@ -381,21 +383,23 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
   }
 
   // Epilogue through LDS: element 4 e + i of lane l in block (nb, mb) is
-  // C[m][n + i] with m = 128 wm + 32 mb + l % 32, n = 128 wn + 32 nb + 8 e +
+  // C[m][n + i] with m = 128 wm + 32 mb + l % 32, n = 64 wn + 32 nb + 8 e +
   // 4 (l / 32) (tile coordinates), i.e. 8-byte pieces of 32 different rows
   // per store instruction.  Each wave instead writes one 32-row block at a
-  // time into its own LDS region (rows 136 elements apart, so the 32 rows of
-  // one write pass spread over the banks and every row starts 16-byte
-  // aligned), then reads it back as 16-byte row pieces and stores 4 whole
-  // 256-byte row segments per instruction.  Every stage's loads were waited
-  // for in the loop; the barrier frees the stage buffers of all waves.
+  // time into its own LDS region (one of the eight stage arrays; rows 72
+  // elements apart, so the 32 rows of one write pass spread over the banks
+  // and every row starts 16-byte aligned), then reads it back as 16-byte row
+  // pieces and stores 8 whole 128-byte row segments per instruction.  Every
+  // stage's loads were waited for in the loop; the barrier frees the stage
+  // buffers of all waves.
   __syncthreads();
-  constexpr int kCS = 136;  // staging row stride (elements)
-  bf16* sC = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3;
+  constexpr int kCS = 72;  // staging row stride (elements)
+  bf16* sC = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : wave == 3 ? sA3
+           : wave == 4 ? sB0 : wave == 5 ? sB1 : wave == 6 ? sB2 : sB3;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const f32x4 v = {acc[nb][mb][4 * e], acc[nb][mb][4 * e + 1], acc[nb][mb][4 * e + 2],
@@ -403,12 +407,12 @@ void gemm_bf16_dma_kernel(const GemmParams p) {
         st4(sC + l32 * kCS + 32 * nb + 8 * e + 4 * lh, v);
       }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 4 * i + (lane >> 4);
-      const int c8 = 8 * (lane & 15);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const int c8 = 8 * (lane & 7);
       const u32x4 v = *reinterpret_cast<const u32x4*>(sC + row * kCS + c8);
       const int m = m0 + 128 * wm + 32 * mb + row;
-      const int n = n0 + 128 * wn + c8;
+      const int n = n0 + 64 * wn + c8;
       if (m < p.M && n < N) {
         const int grp = n / p.Ng;
         bf16* dst = reinterpret_cast<bf16*>(p.C[grp]) + (int64_t)m * p.ldc + (n - grp * p.Ng);
@@ -444,7 +448,7 @@ int launch_gemm(int dtype, const GemmParams& p, void* stream) {
     if (p.K % kGemmBK == 0 && p.K > 0) {
       const dim3 grid((unsigned)((N + kWideBN - 1) / kWideBN),
                       (unsigned)((p.M + kWideBM - 1) / kWideBM));
-      hipLaunchKernelGGL(gemm_bf16_dma_kernel, grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL(gemm_bf16_dma_kernel, grid, dim3(512), 0, st, p);
     } else {
       const dim3 grid((unsigned)((N + kGemmBN - 1) / kGemmBN),
                       (unsigned)((p.M + kGemmBM - 1) / kGemmBM));
