@@ -99,6 +99,77 @@ def _run_chunks(inp, chunks, D, W, T_cap, dtype, first_plain=True, decode_steps=
                 dec=to_np(torch.stack(dec, dim=2)) if dec else None, T=t0)
 
 
+
+def _run_chunks_two_streams(inp, chunks, D, W, T_cap, dtype):
+    """The chunks of _run_chunks (first chunk through the plain entry points)
+    as a two-stream pipeline: chunk i's scan on one stream beside chunk
+    i-1's attention on the other.  Three rings and two hk/hv buffers are
+    used in turn, so the scan of chunk i waits only for the attention of
+    chunk i-2, the last reader of the ring and state buffers it overwrites
+    (each attention reads the ring of the chunk before it)."""
+    import dilated_sparse_attention_rat_amd as rat
+    B, H, Ttot, hd = inp["q"].shape
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    R, _ = rat.rat_anchor_rows(H, T_cap, D)
+    WS, _ = rat.rat_ring_rows(H, W)
+    Kc = torch.full((B, R, hd), NAN, dtype=st, device="cuda")
+    Vc = torch.full_like(Kc, NAN)
+    rings = [(torch.full((B, WS, hd), NAN, dtype=st, device="cuda"),
+              torch.full((B, WS, hd), NAN, dtype=st, device="cuda")) if WS > 0 else (None, None)
+             for _ in range(3)]
+    states = [(torch.full((B, H, hd), NAN, dtype=torch.float32, device="cuda"),
+               torch.full((B, H, hd), NAN, dtype=torch.float32, device="cuda")) for _ in range(2)]
+    n = len(chunks)
+    starts = np.concatenate([[0], np.cumsum(chunks)]).astype(int)
+    ins = [{k: to_dev(np.ascontiguousarray(inp[k][:, :, starts[i]:starts[i + 1]]), dtype)
+            for k in "qkvg"} for i in range(n)]
+    tmax = max(chunks)
+    hkv = [(torch.empty(B * H * tmax * hd, dtype=st, device="cuda"),
+            torch.empty(B * H * tmax * hd, dtype=st, device="cuda")) for _ in range(2)]
+    wss = [rat.scan_workspace(B, H, T, hd, "cuda") for T in chunks]
+    os_ = [torch.full_like(ins[i]["q"], NAN) for i in range(n)]
+    lses = [torch.full((B, H, chunks[i]), NAN, dtype=torch.float32, device="cuda") for i in range(n)]
+    torch.cuda.synchronize()
+    s_scan, s_attn = torch.cuda.Stream(), torch.cuda.Stream()
+    ev_s = [torch.cuda.Event() for _ in range(n)]
+    ev_a = [torch.cuda.Event() for _ in range(n)]
+    for i in range(n):
+        t0, T = int(starts[i]), chunks[i]
+        cur, prev = rings[i % 3], rings[(i - 1) % 3]
+        sc, sp = states[i % 2], states[1 - i % 2]
+        hk, hv = (x[:B * H * T * hd].view(B, H, T, hd) for x in hkv[i % 2])
+        say(f"  chunk {i}: t0={t0} T={T} (two streams)")
+        with torch.cuda.stream(s_scan):
+            if i >= 2:
+                s_scan.wait_event(ev_a[i - 2])
+            x = ins[i]
+            if i == 0:
+                rat.rat_scan_prefill(x["k"], x["v"], x["g"], D, W, T_cap, Kc, Vc, sc[0], sc[1],
+                                     wss[i], hk=hk, hv=hv, k_ring=cur[0], v_ring=cur[1])
+            else:
+                rat.rat_scan_prefill_continue(x["k"], x["v"], x["g"], D, W, T_cap, t0, sp[0], sp[1],
+                                              Kc, Vc, sc[0], sc[1], wss[i], hk=hk, hv=hv,
+                                              k_ring_in=prev[0], v_ring_in=prev[1], k_ring=cur[0],
+                                              v_ring=cur[1])
+            ev_s[i].record(s_scan)
+        with torch.cuda.stream(s_attn):
+            s_attn.wait_event(ev_s[i])
+            if i == 0:
+                rat.rat_dilated_attn_prefill(x["q"], hk, hv, Kc, Vc, D, W, T_cap, os_[i], lses[i])
+            else:
+                rat.rat_dilated_attn_prefill_continue(x["q"], hk, hv, Kc, Vc, D, W, T_cap, t0, os_[i],
+                                                      k_ring_prev=prev[0], v_ring_prev=prev[1],
+                                                      lse=lses[i])
+            ev_a[i].record(s_attn)
+    torch.cuda.synchronize()
+    for ws in wss:
+        assert int(ws[2].item()) == 0, "scan workspace reports a timed-out wait"
+    kr, vr = rings[(n - 1) % 3]
+    sk, sv = states[(n - 1) % 2]
+    return dict(o=to_np(torch.cat(os_, dim=2)), lse=to_np(torch.cat(lses, dim=2)), Kc=to_np(Kc),
+                Vc=to_np(Vc), kr=None if kr is None else to_np(kr),
+                vr=None if vr is None else to_np(vr), sk=to_np(sk), sv=to_np(sv))
+
 def _check_layout(chk, out, D, W, T_cap):
     """Anchor rows and the live ring hold the GPU's own states at their
     positions (bit-exact); anchor rows beyond the sequence stay untouched."""
@@ -208,3 +279,31 @@ def test_workload_sized_second_chunk_sampled():
         chk(check_float, f"o[{b},{h}]", out["o"][b, h, r["t"]], r["o"], "bf16")
         chk(check_state_ulp, f"hk[{b},{h}]", out["hk"][b, h, 2048:], r["hk"][2048:], "bf16")
     chk.done()
+
+
+PIPE = [
+    # label, B, H, chunks, hd, D, W
+    ("hybrid-window", 2, 3, [300, 200, 77, 150], 128, [4, 1, 16], [0, 37, 3]),
+    ("chunks-shorter-than-window", 1, 2, [100, 5, 3, 1, 40, 64], 128, [3, 8], [64, 0]),
+]
+
+
+@pytest.mark.parametrize("case", PIPE, ids=[c[0] for c in PIPE])
+def test_two_stream_pipeline_equals_one_stream(case):
+    """Chunk i's scan on a second stream beside chunk i-1's attention gives
+    the outputs, anchors, final state and live ring of the one-stream chunk
+    sequence, bit for bit (the kernels are deterministic and the buffer
+    rotation leaves no read of a buffer that a concurrent launch writes)."""
+    label, B, H, chunks, hd, D, W = case
+    T = sum(chunks)
+    say(f"[chunked] two streams {label}: B={B} H={H} chunks={chunks} D={D} W={W}")
+    inp = synth.random_case(zlib.crc32(label.encode()) % 1000, B, H, T, hd, "bf16", hd ** -0.5, 3.0)
+    D, W = np.array(D, np.int32), np.array(W, np.int32)
+    one = _run_chunks(inp, chunks, D, W, T, "bf16", True)
+    two = _run_chunks_two_streams(inp, chunks, D, W, T, "bf16")
+    for k in ("o", "lse", "Kc", "Vc", "kr", "vr", "sk", "sv"):
+        if one[k] is None:
+            assert two[k] is None, k
+            continue
+        np.testing.assert_array_equal(np.nan_to_num(two[k], nan=7.0), np.nan_to_num(one[k], nan=7.0),
+                                      err_msg=k)
