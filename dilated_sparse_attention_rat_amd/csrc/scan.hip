@@ -154,13 +154,14 @@ __device__ __forceinline__ void fold_nodes(const ScanParams& p, int64_t e0, int 
 template <typename ST, int HD, int S>
 struct ChunkRows {
   u32x4 k[S], v[S], g[S];
+  f32x4 gb[StTraits<ST>::VEC / 4];  // gate bias of the lane's channels (gated variant)
 };
 
 // Issue the loads of this lane's S rows of chunk `ticket` (kept in registers
 // for both passes).  The loads are unconditional (rows at or past T re-read
 // row T-1 and are ignored) so the compiler can count outstanding loads
 // exactly and wait only for the ones it needs.
-template <typename ST, int HD, int S>
+template <typename ST, int HD, int S, bool GATE>
 __device__ __forceinline__ void load_rows(const ScanParams& p, uint32_t ticket,
                                           ChunkRows<ST, HD, S>& rw) {
   constexpr int VEC = StTraits<ST>::VEC;
@@ -182,6 +183,14 @@ __device__ __forceinline__ void load_rows(const ScanParams& p, uint32_t ticket,
     rw.k[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.k) + off);
     rw.v[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.v) + off);
     rw.g[s] = ld_raw16_nt(reinterpret_cast<const ST*>(p.g) + off);
+  }
+  // the gate bias rides with the rows: loaded at the chunk's start instead,
+  // it would be ordered behind the previous chunk's output stores (vector
+  // memory completes in order) and hold up pass 1 until they drain
+  if constexpr (GATE) {
+    const float* gbp = p.gate_bias + (int64_t)(seq - b * p.H) * HD + c0;
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) rw.gb[j] = *reinterpret_cast<const f32x4*>(gbp + 4 * j);
   }
 }
 
@@ -214,16 +223,12 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
   const u32x4* rg = rw.g;
   // GATE: g holds the gate's pre-activation; the gate is sigmoid(g + bias)
   // with the head's per-channel bias (fused here instead of a separate pass)
-  float gbias[VEC];
-  if constexpr (GATE) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) gbias[i] = p.gate_bias[h * HD + c0 + i];
-  }
   auto gate = [&](float (&gf)[VEC]) {
     if constexpr (GATE) {
 #pragma unroll
       for (int i = 0; i < VEC; ++i)
-        gf[i] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(gf[i] + gbias[i]) * kLog2e));
+        gf[i] = __builtin_amdgcn_rcpf(
+            1.f + __builtin_amdgcn_exp2f(-(gf[i] + rw.gb[i / 4][i % 4]) * kLog2e));
     }
   };
 
@@ -424,18 +429,18 @@ void scan_kernel(const ScanParams p) {
   const uint32_t n = (uint32_t)p.nticket;
   ChunkRows<ST, HD, S> ra, rb;
   uint32_t ticket = blockIdx.x;
-  if (ticket < n) load_rows<ST, HD, S>(p, ticket, ra);
+  if (ticket < n) load_rows<ST, HD, S, GATE>(p, ticket, ra);
   while (ticket < n) {
     const uint32_t t1 = ticket + G;
     // (prefetches are unconditional -- past the end they re-load the last
     // ticket and are ignored -- so outstanding loads are counted exactly)
     scan_chunk<ST, HD, S, GATE>(p, ticket, tag, ra, s_A, s_Bk, s_Bv, s_hk, s_hv,
-                          [&] { load_rows<ST, HD, S>(p, min(t1, n - 1), rb); });
+                          [&] { load_rows<ST, HD, S, GATE>(p, min(t1, n - 1), rb); });
     __syncthreads();  // LDS is reused by the next chunk
     if (t1 >= n) break;
     const uint32_t t2 = t1 + G;
     scan_chunk<ST, HD, S, GATE>(p, t1, tag, rb, s_A, s_Bk, s_Bv, s_hk, s_hv,
-                          [&] { load_rows<ST, HD, S>(p, min(t2, n - 1), ra); });
+                          [&] { load_rows<ST, HD, S, GATE>(p, min(t2, n - 1), ra); });
     __syncthreads();
     ticket = t2;
   }
