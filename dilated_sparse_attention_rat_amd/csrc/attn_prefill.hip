@@ -14,7 +14,8 @@
 //    flight; 2 for MFMA-bound calls: twice the reuse of every LDS operand);
 //    a workgroup takes a pair of query tiles (i, nq-1-i) so all workgroups of
 //    a head cost about the same (single tiles, heaviest first, when pairs
-//    would leave too few workgroups); heads are ordered by per-workgroup
+//    would leave too few workgroups, or when every head's window outweighs
+//    its anchors so that tile costs hardly grow along the sequence); heads are ordered by per-workgroup
 //    cost (heaviest first) so a head-wise hybrid launch is longest-job-first;
 //  * K/V tiles of 64 keys are staged in LDS once per workgroup, both
 //    row-major for bf16: K fragments are plain ds_read_b128 and the V^T

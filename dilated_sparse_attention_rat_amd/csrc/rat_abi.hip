@@ -321,7 +321,13 @@ int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return RAT_ERR_HIP;
     const int64_t slots = (int64_t)cus * (p.qb == 1 ? 3 : 2);  // resident workgroups
-    if ((int64_t)B * H * p.np < 2 * slots) {
+    // Where every head's window holds at least as many keys as its anchors
+    // ever do, a tile's cost hardly grows along the sequence: single tiles,
+    // so that neighbouring query tiles, which share band rows, run at the
+    // same time and find them in L2.
+    bool band_bound = true;
+    for (int h = 0; h < H; ++h) band_bound = band_bound && (t0 + T) / D[h] <= W[h];
+    if ((int64_t)B * H * p.np < 2 * slots || band_bound) {
       p.np = p.nq;
       p.paired = 0;
     }
