@@ -563,7 +563,8 @@ int launch_ring_carry_t(int B, int H, int64_t WS, const HeadTables& ht, int64_t 
   constexpr int CPR = HD / StTraits<ST>::VEC;
   int64_t wmax = 0;
   for (int h = 0; h < H; ++h) wmax = std::max<int64_t>(wmax, ht.W[h]);
-  if (wmax == 0 || t0 == 0 || B == 0 || H == 0) return 0;
+  // a chunk at least as long as every window rewrites every live slot itself
+  if (wmax == 0 || t0 == 0 || B == 0 || H == 0 || T >= wmax) return 0;
   const dim3 grid((unsigned)((wmax * CPR + 255) / 256), (unsigned)H, (unsigned)B);
   hipLaunchKernelGGL((ring_carry_kernel<ST, HD>), grid, dim3(256), 0, st,
                      reinterpret_cast<const ST*>(kin), reinterpret_cast<const ST*>(vin),
