@@ -22,7 +22,10 @@
 //    fragments of the PV product come out of ds_read_b64_tr_b16, the gfx950
 //    transposing read, so staging is a plain copy (fp32 stages V transposed,
 //    keys contiguous); the global loads of tile i+1 are issued into
-//    registers before tile i's MFMAs, so their latency is hidden;
+//    registers before tile i's MFMAs, so their latency is hidden (for
+//    windowless heads, bf16, hd 128, two blocks per wave, the tiles go
+//    straight into two LDS stages with global_load_lds_dwordx4 instead, with
+//    one barrier per tile);
 //  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16),
 //    so each lane owns one query column: the row max needs two cross-lane
 //    steps, and P^T is already the B operand of O^T += V^T P^T (keys
@@ -267,7 +270,10 @@ struct TileRegs {
 // S = c*K Q^T - m.  With Q pre-scaled by c = scale*log2(e) the MFMA result
 // is directly the exp2 argument of the running softmax (the first slab's
 // MFMAs read one {-m} tuple per query block as their C operand).
-template <typename ST, int HD, int QB>
+// SW: the tile is unpadded (rows HD elements apart) with K row r holding its
+// 16-byte chunk c at c ^ (r % 16) and V row r at c ^ 2 (r % 8), the layout
+// the direct-to-LDS staging writes (else K rows KSTR and V rows VRSTR apart).
+template <typename ST, int HD, int QB, bool SW = false>
 __device__ __forceinline__ void tile_scores(const WaveState<ST, HD, QB>& ws, const ST* sK,
                                             TileRegs<ST, HD, QB>& tr) {
   using C = AttnCfg<ST, HD, QB>;
@@ -284,7 +290,9 @@ __device__ __forceinline__ void tile_scores(const WaveState<ST, HD, QB>& ws, con
   for (int s = 0; s < C::NS; ++s) {
 #pragma unroll
     for (int mb = 0; mb < C::NMB; ++mb) {
-      const Frag<ST> a = frag_ld8(sK + (16 * mb + col) * C::KSTR + 32 * s + 8 * g);
+      // 16 lanes read 16 rows at one chunk: distinct banks in either layout
+      const Frag<ST> a = SW ? frag_ld8(sK + (16 * mb + col) * HD + 8 * ((4 * s + g) ^ col))
+                            : frag_ld8(sK + (16 * mb + col) * C::KSTR + 32 * s + 8 * g);
 #pragma unroll
       for (int nb = 0; nb < QB; ++nb) {
         if (s == 0)
@@ -369,7 +377,7 @@ __device__ __forceinline__ void tile_softmax(WaveState<ST, HD, QB>& ws, TileRegs
 // P[k][query] in every element: the same bf16-rounded weights as the
 // numerator).
 template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
-          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR)>
+          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR), bool SW = false>
 __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileRegs<ST, HD, QB>& tr,
                                         const ST* sV) {
   using C = AttnCfg<ST, HD, QB>;
@@ -382,7 +390,13 @@ __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileReg
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
       Frag<ST> va;
-      if constexpr (VR) {
+      if constexpr (VR && SW) {
+        // as below; the 8-byte piece of row r sits in chunk c ^ 2 (r % 8)
+        // (rows r and r + 16 share the swizzle)
+        const int r = 32 * kk + 4 * g + (col >> 2);
+        const int c = 2 * db + ((col >> 1) & 1);
+        va = frag_ld_tr(sV + r * HD + 8 * (c ^ (2 * (r & 7))) + 4 * (col & 1), 16 * HD);
+      } else if constexpr (VR) {
         // keys 32kk + 4g + j (slots j < 4) and 32kk + 16 + 4g + j (slots
         // j >= 4) of channel 16db + col, transposed out of the row-major tile
         va = frag_ld_tr(sV + (32 * kk + 4 * g + (col >> 2)) * VS + 16 * db + 4 * (col & 3), 16 * VS);
@@ -400,14 +414,14 @@ __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileReg
 }
 
 template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
-          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR)>
+          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR), bool SW = false>
 __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST* sK,
                                             const ST* sV, int key0, int kind, bool need_mask,
                                             int W) {
   TileRegs<ST, HD, QB> tr;
-  tile_scores<ST, HD, QB>(ws, sK, tr);
+  tile_scores<ST, HD, QB, SW>(ws, sK, tr);
   tile_softmax<ST, HD, QB>(ws, tr, key0, kind, need_mask, W);
-  tile_pv<ST, HD, QB, VR, VS>(ws, tr, sV);
+  tile_pv<ST, HD, QB, VR, VS, SW>(ws, tr, sV);
 }
 
 // Key rows of one staged tile.  Anchor tiles, and band tiles at positions
@@ -436,7 +450,11 @@ struct RowMap {
 // p.t0 + lt0).  `qin` holds this tile's query inputs (already loaded).
 // Positions (queries, band keys, anchors) are absolute; rows of q, hk, hv,
 // o and lse are local to this call.
-template <typename ST, int HD, int QB, bool RING>
+// DMA (bf16, HD 128, QB 2, no ring): sK and sV hold two stages of BN x HD
+// each, filled straight from global memory (global_load_lds_dwordx4) in the
+// swizzled layout of tile_scores / tile_pv: the loads of key tile i+1 fly
+// while tile i is computed, no staging registers, one barrier per tile.
+template <typename ST, int HD, int QB, bool RING, bool DMA = false>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, int lt0, ST* sK,
                                              ST* sV, const QueryIn<ST, HD, QB>& qin) {
   using C = AttnCfg<ST, HD, QB>;
@@ -507,8 +525,36 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
       pf.load(rows, nv);
   };
 
+  // Stage st of the direct-to-LDS path: instruction j (of BN/4 per tensor,
+  // BN/16 per wave) fills rows 4j .. 4j+3; lane l lands 16 bytes at chunk
+  // l % 16 of row 4j + l / 16, so it loads the global chunk whose swizzled
+  // place that is.  Rows at or past nvalid re-read row nvalid-1 (masked).
+  auto dma_item = [&](int i, int st) {
+    static_assert(!DMA || (sizeof(ST) == 2 && HD == 128 && !RING && C::BN % 16 == 0), "DMA");
+    if constexpr (DMA) {
+      RowMap<ST, HD> rows;
+      int nv, k0;
+      item_src(i, rows, nv, k0);
+      ST* dK = sK + st * (C::BN * HD);
+      ST* dV = sV + st * (C::BN * HD);
+      const int pc = lane & 15;
+#pragma unroll
+      for (int j = 0; j < C::BN / 16; ++j) {
+        const int ins = (C::BN / 16) * wave + j;
+        const int r = 4 * ins + (lane >> 4);
+        const int64_t rs = (int64_t)min(r, nv - 1) * HD;
+        dma16(rows.kh + rs + 8 * (pc ^ (r & 15)), dK + ins * 4 * HD);
+        dma16(rows.vh + rs + 8 * (pc ^ (2 * (r & 7))), dV + ins * 4 * HD);
+      }
+    }
+  };
   Prefetch<ST, HD, QB> pf;
-  if (n_items > 0) load_item(pf, 0);
+  if constexpr (DMA) {
+    __syncthreads();  // the workgroup's previous tile loop is done with both stages
+    if (n_items > 0) dma_item(0, 0);
+  } else {
+    if (n_items > 0) load_item(pf, 0);
+  }
 
   // own position folded into the initial state (m = its score, from the
   // unscaled q in fp32; l = 1; acc = its value row).  The MFMA operand is Q
@@ -537,10 +583,23 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
   const int w_full = wave_active ? max(0, aw0 - W) / D : 0;
   const int wj0 = max(0, aw0 - W);
   for (int i = 0; i < n_items; ++i) {
-    __syncthreads();  // every wave is done reading the previous tile
-    pf.store(sK, sV);
-    __syncthreads();
-    if (i + 1 < n_items) load_item(pf, i + 1);  // overlaps this tile's MFMAs
+    const ST* tK = sK;
+    const ST* tV = sV;
+    if constexpr (DMA) {
+      // this wave's loads of tile i have landed (and every earlier memory
+      // operation); after the barrier every wave's have, and every wave is
+      // done with tile i-1, whose stage the loads of tile i+1 then refill
+      RAT_WAIT_VM_LGKM(0);
+      lds_barrier();
+      if (i + 1 < n_items) dma_item(i + 1, (i + 1) & 1);
+      tK = sK + (i & 1) * (C::BN * HD);
+      tV = sV + (i & 1) * (C::BN * HD);
+    } else {
+      __syncthreads();  // every wave is done reading the previous tile
+      pf.store(sK, sV);
+      __syncthreads();
+      if (i + 1 < n_items) load_item(pf, i + 1);  // overlaps this tile's MFMAs
+    }
     RowMap<ST, HD> rows;
     int nv, key0;
     item_src(i, rows, nv, key0);
@@ -555,7 +614,12 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
       // aw0+QW-1 - W <= key0 and key0 + BN - 1 <= aw0 - 1 (and no clamped rows)
       need_mask = !((aw0 + QW - 1 - W <= key0) && (key0 + C::BN <= aw0) && (tw0 + QW - 1 < T));
     }
-    if (part) tile_update<ST, HD, QB>(ws, sK, sV, key0, kind, need_mask, W);
+    if (part) {
+      if constexpr (DMA)
+        tile_update<ST, HD, QB, C::VROW, C::VRSTR, true>(ws, tK, tV, key0, kind, need_mask, W);
+      else
+        tile_update<ST, HD, QB>(ws, tK, tV, key0, kind, need_mask, W);
+    }
   }
 
   // ---- normalise and store --------------------------------------------------
@@ -581,13 +645,15 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
 // queries, which would need 48 more registers).  RING: a continuation whose
 // window reaches before t0 (band rows from the previous call's ring);
 // without it the band tiles are plain linear reads.
-template <typename ST, int HD, int QB, bool RING>
+template <typename ST, int HD, int QB, bool RING, bool DMA = false>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(QB == 1 ? 3 : 2, QB == 1 ? 3 : 2)))
 void attn_prefill_kernel(const AttnParams p) {
   using C = AttnCfg<ST, HD, QB>;
-  __shared__ __attribute__((aligned(16))) ST sK[C::BN * C::KSTR];
-  __shared__ __attribute__((aligned(16))) ST sV[C::VLDS];
+  // two stages of unpadded tiles for the direct-to-LDS path, one padded
+  // stage otherwise
+  __shared__ __attribute__((aligned(1024))) ST sK[DMA ? 2 * C::BN * HD : C::BN * C::KSTR];
+  __shared__ __attribute__((aligned(1024))) ST sV[DMA ? 2 * C::BN * HD : C::VLDS];
 
   // block -> (unit, pair), a unit being one (head rank, batch row), units in
   // descending cost.  Workgroup i runs on XCD i % 8, and each XCD has its own
@@ -625,10 +691,10 @@ void attn_prefill_kernel(const AttnParams p) {
   const int wave = threadIdx.x >> 6;
   QueryIn<ST, HD, QB> qin;
   qin.load(qp, hkp, hvp, qa * C::BM + 16 * QB * wave, p.T, p.q_st);
-  process_tile<ST, HD, QB, RING>(p, b, h, qa * C::BM, sK, sV, qin);
+  process_tile<ST, HD, QB, RING, DMA>(p, b, h, qa * C::BM, sK, sV, qin);
   if (ntiles == 2) {
     qin.load(qp, hkp, hvp, pr * C::BM + 16 * QB * wave, p.T, p.q_st);
-    process_tile<ST, HD, QB, RING>(p, b, h, pr * C::BM, sK, sV, qin);
+    process_tile<ST, HD, QB, RING, DMA>(p, b, h, pr * C::BM, sK, sV, qin);
   }
 }
 
@@ -797,6 +863,9 @@ int launch_t(const AttnParams& p, hipStream_t st) {
   if (p.qb == 2) {
     if (ring)
       hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 2, true>), grid, block, 0, st, p);
+    else if (sizeof(ST) == 2 && HD == 128 && p.dma)
+      hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 2, false, sizeof(ST) == 2 && HD == 128>), grid,
+                         block, 0, st, p);
     else
       hipLaunchKernelGGL((attn_prefill_kernel<ST, HD, 2, false>), grid, block, 0, st, p);
   } else {

@@ -193,38 +193,6 @@ constexpr int kWideHalf = kGemmBK * 128;          // elements of one B half
 constexpr int kWideAStage = kWideBM * kGemmBK;  // elements
 constexpr int kWideBStage = 2 * kWideHalf;
 
-// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt at its maximum; n < 64), and a
-// workgroup barrier that is a compiler-level fence only: the direct-to-LDS
-// loads are waited for explicitly, and a __syncthreads() would also wait for
-// the loads still in flight for later steps.
-#define RAT_WAIT_VM_LGKM(n) \
-  __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// global_load_lds_dwordx4 from this lane's src to LDS base dst (+ 16 bytes
-// per lane).  Written out rather than through the builtin: the compiler
-// cannot tell which LDS stage a builtin load writes, and waits for every one
-// in flight before each LDS read.  Nothing is returned in registers (the
-// address is read at issue); completion is waited for with vmcnt before the
-// barrier that publishes a stage.  M0 (the LDS base) is saved and restored
-// around the load, so the compiler's own use of M0 is undisturbed; one wait
-// state separates the M0 write from its use.
-__device__ __forceinline__ void dma16(const void* src, const bf16* dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)dst));
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(base)
-      : "memory");
-}
-
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))

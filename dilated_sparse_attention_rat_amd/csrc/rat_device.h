@@ -120,6 +120,42 @@ __device__ __forceinline__ void mma16(f32x4& c, const Frag<float>& a, const Frag
   for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[j], b.hi[j], c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS loads (global_load_lds_dwordx4) and their waits
+// ---------------------------------------------------------------------------
+// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt at its maximum; n < 64), and a
+// workgroup barrier that is a compiler-level fence only: the direct-to-LDS
+// loads are waited for explicitly, and a __syncthreads() would also wait for
+// the loads still in flight for later steps.
+#define RAT_WAIT_VM_LGKM(n) \
+  __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// global_load_lds_dwordx4 from this lane's src to LDS base dst (+ 16 bytes
+// per lane; dst is the same for every lane of the wave).  Written out rather
+// than through the builtin: the compiler cannot tell which LDS stage a
+// builtin load writes, and waits for every one in flight before each LDS
+// read.  Nothing is returned in registers (the
+// address is read at issue); completion is waited for with vmcnt before the
+// barrier that publishes a stage.  M0 (the LDS base) is saved and restored
+// around the load, so the compiler's own use of M0 is undisturbed; one wait
+// state separates the M0 write from its use.
+__device__ __forceinline__ void dma16(const void* src, const bf16* dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
+}
+
 // 8 consecutive storage elements -> fragment
 __device__ __forceinline__ Frag<bf16> frag_ld8(const bf16* p) {
   Frag<bf16> f;

@@ -75,6 +75,7 @@ struct AttnParams {
   int nq;            // query tiles per (b, h)
   int np;            // workgroups per (b, h): pairs of query tiles, or single tiles
   int paired;        // 1: workgroup pr takes tiles nq-1-pr and pr; 0: tile nq-1-pr only
+  int dma;           // K/V tiles loaded straight into LDS (bf16, hd 128, qb 2, no ring)
   float scale_log2;  // scale * log2(e)
   int64_t R;
   const void* q;
