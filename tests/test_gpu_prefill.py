@@ -54,6 +54,10 @@ SMALL = [
     ("qb2-hd64", 1, 1, 1100, 64, [1], [0], "bf16", 64 ** -0.5, 3.0, 0),
     ("qb2-window-band", 1, 2, 1300, 128, [1, 1], [300, 0], "bf16", 128 ** -0.5, 3.0, 0),
     ("qb2-f32", 1, 1, 1030, 64, [1], [0], "f32", 1.0, 2.0, 0),
+    # windowless bf16 hd 128 heads past the resident kernel's 256 anchors:
+    # the two-block launch whose K/V tiles go straight into LDS (ragged last
+    # query and key tiles, two batch rows)
+    ("qb2-dma-windowless", 2, 2, 1500, 128, [1, 3], [0, 0], "bf16", 128 ** -0.5, 3.0, 4),
     # windowless bf16 heads with at most 256 anchors: the resident-anchor
     # kernel at hd = 64 (V staged row-major, transposing fragment reads)
     ("resident-bf16-64", 1, 2, 517, 64, [3, 5], [0, 0], "bf16", 64 ** -0.5, 3.0, 0),
