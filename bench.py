@@ -463,6 +463,8 @@ def run(args, rat, synth, torch, np):
     wall = min(walls)
 
     # ---- instrumented pass: K eager steps with HIP events between kernels --
+    # (the median over the K steps: one host stall while queueing would
+    # otherwise land in the mean of the step it delays)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -472,7 +474,7 @@ def run(args, rat, synth, torch, np):
     wall_instr = time.perf_counter() - t1
     rig.check("the instrumented steps")
     del graphs
-    in_step = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3 for j in range(3)]
+    in_step = [float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3 for j in range(3)]
 
     # ---- per-kernel pass: each kernel K times back to back ----------------
     kernels = rig.kernels(K)
@@ -535,7 +537,8 @@ def run(args, rat, synth, torch, np):
         "ms_per_step_instrumented": wall_instr * 1e3 / K,
         "kernel_timing": "kernels.*.us: each kernel K times back to back between one pair of HIP "
                          "events on the launch stream (fastest of 3 such passes); us_in_step: HIP "
-                         "events around each launch inside the step (each event pair adds a few us)",
+                         "events around each launch inside the step, median over the K steps "
+                         "(each event pair adds a few us)",
         "launch": "hip graph per step" if args.graph else "eager",
         "higher_is_better": True,
         "scaling": "weak",

@@ -273,13 +273,17 @@ struct TileRegs {
 // SW: the tile is unpadded (rows HD elements apart) with K row r holding its
 // 16-byte chunk c at c ^ (r % 16) and V row r at c ^ 2 (r % 8), the layout
 // the direct-to-LDS staging writes (else K rows KSTR and V rows VRSTR apart).
-template <typename ST, int HD, int QB, bool SW = false>
+// SCHED >= 0: the compiler's instruction-group scheduling strategy of that
+// number for the block (LDS reads interleaved with the MFMAs it feeds);
+// measured per kernel, none where it does not pay.
+template <typename ST, int HD, int QB, bool SW = false, int SCHED = -1>
 __device__ __forceinline__ void tile_scores(const WaveState<ST, HD, QB>& ws, const ST* sK,
                                             TileRegs<ST, HD, QB>& tr) {
   using C = AttnCfg<ST, HD, QB>;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
+  if constexpr (SCHED >= 0) __builtin_amdgcn_iglp_opt(SCHED);
   f32x4 minit[QB];
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
@@ -377,7 +381,8 @@ __device__ __forceinline__ void tile_softmax(WaveState<ST, HD, QB>& ws, TileRegs
 // P[k][query] in every element: the same bf16-rounded weights as the
 // numerator).
 template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
-          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR), bool SW = false>
+          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR), bool SW = false,
+          int SCHED = -1>
 __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileRegs<ST, HD, QB>& tr,
                                         const ST* sV) {
   using C = AttnCfg<ST, HD, QB>;
@@ -385,6 +390,7 @@ __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileReg
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
+  if constexpr (SCHED >= 0) __builtin_amdgcn_iglp_opt(SCHED);
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) {
 #pragma unroll
@@ -414,14 +420,15 @@ __device__ __forceinline__ void tile_pv(WaveState<ST, HD, QB>& ws, const TileReg
 }
 
 template <typename ST, int HD, int QB, bool VR = AttnCfg<ST, HD, QB>::VROW,
-          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR), bool SW = false>
+          int VS = (VR ? AttnCfg<ST, HD, QB>::VRSTR : AttnCfg<ST, HD, QB>::VSTR), bool SW = false,
+          int SCHED = -1>
 __device__ __forceinline__ void tile_update(WaveState<ST, HD, QB>& ws, const ST* sK,
                                             const ST* sV, int key0, int kind, bool need_mask,
                                             int W) {
   TileRegs<ST, HD, QB> tr;
-  tile_scores<ST, HD, QB, SW>(ws, sK, tr);
+  tile_scores<ST, HD, QB, SW, SCHED>(ws, sK, tr);
   tile_softmax<ST, HD, QB>(ws, tr, key0, kind, need_mask, W);
-  tile_pv<ST, HD, QB, VR, VS, SW>(ws, tr, sV);
+  tile_pv<ST, HD, QB, VR, VS, SW, SCHED>(ws, tr, sV);
 }
 
 // Key rows of one staged tile.  Anchor tiles, and band tiles at positions
@@ -616,9 +623,11 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
     }
     if (part) {
       if constexpr (DMA)
-        tile_update<ST, HD, QB, C::VROW, C::VRSTR, true>(ws, tK, tV, key0, kind, need_mask, W);
+        tile_update<ST, HD, QB, C::VROW, C::VRSTR, true, 0>(ws, tK, tV, key0, kind, need_mask, W);
       else
-        tile_update<ST, HD, QB>(ws, tK, tV, key0, kind, need_mask, W);
+        tile_update<ST, HD, QB, C::VROW, (C::VROW ? C::VRSTR : C::VSTR), false,
+                    (QB == 2 && HD == 128 && sizeof(ST) == 2) ? 1 : -1>(ws, tK, tV, key0, kind,
+                                                                    need_mask, W);
     }
   }
 
