@@ -806,6 +806,8 @@ def bench_backward(rat, synth, torch, np, w, reps=10):
         run()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
+    if int(bws[2].item()) != 0:
+        raise ScanError("backward: a wait of the reverse scan timed out")
     us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
     es = 2 if w.dtype == "bf16" else 4
     nb, nf = backward_bytes(w, es), backward_flops(w)

@@ -646,6 +646,8 @@ def decode_workspace(B: int, H: int, hd: int, T_cap: int, D, W, device,
 
 
 def backward_workspace(B: int, H: int, T: int, hd: int, D, W, device):
+    """Zero-filled backward workspace (zero it again only after a failed
+    call: uint32 word 2 set)."""
     torch = _torch()
     n = rat_prefill_backward_workspace_bytes(B, H, T, hd, D, W)
-    return torch.empty(((n + 15) // 16) * 4, dtype=torch.int32, device=device)
+    return torch.zeros(((n + 15) // 16) * 4, dtype=torch.int32, device=device)

@@ -19,18 +19,20 @@
 //     dhv += P^T dO, dhk += scale dS^T q.  An anchor tile's queries are split
 //     over several workgroups, each writing a partial sum of the anchor
 //     gradients; window tiles write the window gradients of their positions.
-//  3. bwd_rscan_{agg,carry,apply}: the recurrence in reverse,
+//  3. bwd_rscan_kernel: the recurrence in reverse,
 //     lambda_t = dh_t + g_{t+1} lambda_{t+1} (lambda_T = 0), where dh_t is the
 //     own term, the window gradient and, at anchor positions, the anchor
 //     gradient's partial sums; dk = (1-g) lambda_k,
 //     dv = (1-g) lambda_v, dg = lambda_k (h^k_{t-1} - k) + lambda_v
-//     (h^v_{t-1} - v) with the stored states (h_{-1} = 0).  Chunks of 64
-//     positions, 16-byte accesses per lane as in the forward scan: per-chunk
-//     affine maps, a carry pass over chunks, then the chunks again from
-//     their carries.  With several partial anchor gradients, a small kernel
-//     first sums them into the first buffer.
+//     (h^v_{t-1} - v) with the stored states (h_{-1} = 0).  One persistent
+//     pass over chunks from the end of the sequence, linked by the forward
+//     scan's chunk-aggregate tree, so every row is read once.  With several
+//     partial anchor gradients, a small kernel first sums them into the
+//     first buffer.
 // The storage rounding of the states enters the derivative as the identity.
-#include "rat_device.h"
+#include <algorithm>
+
+#include "scan_tree.h"
 
 // fp32 tiles at hd = 128 need more LDS than two workgroups per CU allow, so
 // those instantiations run at one wave per SIMD (the bf16 ones at two)
@@ -619,26 +621,9 @@ void bwd_dkv_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. the recurrence in reverse (chunks of 64 positions)
+// 3. the recurrence in reverse: one persistent kernel over chunks, linked by
+//    the chunk-aggregate tree of the forward scan (csrc/scan_tree.h)
 // ---------------------------------------------------------------------------
-// Lane layout as in the forward scan: LPR lanes cover a row, VEC channels
-// each (16-byte accesses); a 256-thread workgroup holds 256/LPR chunks of one
-// (b, h), one row at a time per chunk.
-constexpr int kRChunk = 64;
-
-template <typename ST, int HD>
-struct RCfg {
-  static constexpr int VEC = StTraits<ST>::VEC;
-  static constexpr int LPR = HD / VEC;      // lanes per row
-  static constexpr int CPB = 256 / LPR;     // chunks per workgroup
-};
-
-// Every lane walks its chunk's rows one after another (the recurrence is
-// sequential within a chunk), so the loads of kRBatch consecutive rows are
-// issued together and only then consumed: one memory round trip per batch
-// instead of one per row.
-constexpr int kRBatch = 8;
-
 // Partial anchor gradients summed into split 0 (splits in a fixed order, so
 // the result is deterministic); the reverse scan then reads one buffer.
 __global__ __launch_bounds__(256) void bwd_anchor_sum_kernel(float* dKc, float* dVc, int64_t n4,
@@ -656,250 +641,247 @@ __global__ __launch_bounds__(256) void bwd_anchor_sum_kernel(float* dKc, float* 
   v[i] = sv;
 }
 
-// One row's inputs of the state gradient: q_t and dO_t (for the own term),
-// the two own-position scalars and, at an anchor position, the anchor's
-// gradient (split 0 after the sum above).
-template <typename ST>
-struct RowIn {
-  static constexpr int VEC = StTraits<ST>::VEC;
-  u32x4 q, o;
-  f32x2 own;
-  f32x4 ak[VEC / 4], av[VEC / 4];
-};
-
-template <typename ST, int HD>
-__device__ __forceinline__ void row_load(const BwdParams& p, int64_t bh, int t, int c0,
-                                         int64_t arow, bool anchor, RowIn<ST>& in) {
+// lambda_t = dh_t + a_t lambda_{t+1} with a_t = g_{t+1} (0 at t = T-1) is a
+// chain of affine maps, composed like the forward's h_t = g_t h_{t-1} +
+// (1-g_t) x_t but from the end of the sequence: ticket i is the i-th chunk
+// from the end (reversed chunk rc = i / nseq of sequence i % nseq), and the
+// tree links the reversed chunks exactly as the forward links its chunks.
+// Layout as in the forward: LPR lanes cover a row with 16-byte accesses, a
+// lane holds S consecutive rows, RG row-groups make a chunk of RG*S rows.
+//  * loads: g of rows tbase .. tbase+S (a_t and 1-g_t), q, dO and the two
+//    own-position scalars (the own term), the window gradients (W > 0) and
+//    the anchor gradients at anchor rows;
+//  * pass 1 reduces the rows to the lane's map (last row first); the
+//    row-groups are composed in LDS (from the last);
+//  * waves 0..NH-1 publish the chunk's map and the parents it completes,
+//    waves 2..2+NH-1 compose the carry: lambda after the chunk (0 after the
+//    last one);
+//  * then k, v and the stored states of rows tbase-1 .. tbase+S-2 are
+//    loaded (issued before the tree round trip they would keep 64 more
+//    registers live across it and spill: the backward of the 1.5B-like
+//    prefill took 8% longer), and pass 2 recomputes
+//    dh_t from the kept q, dO and scalars (the window and anchor gradients
+//    again, from L2), runs the rows from the carry, last row first, and
+//    writes
+//    dk = (1-g) lambda_k, dv = (1-g) lambda_v and
+//    dg = lambda_k (h^k_{t-1} - k_t) + lambda_v (h^v_{t-1} - v_t).
+// Every input row is read once (the window and anchor gradients twice, the
+// second time normally from L2).
+template <typename ST, int HD, int S>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_rscan_kernel(const BwdParams p) {
   constexpr int VEC = StTraits<ST>::VEC;
-  const int64_t i = (bh * p.T + t) * HD + c0;
-  in.own = *reinterpret_cast<const f32x2*>(p.own + 2 * (bh * p.T + t));
-  in.q = ld_raw16(reinterpret_cast<const ST*>(p.q) + i);
-  in.o = ld_raw16(reinterpret_cast<const ST*>(p.dO) + i);
-  if (anchor) {
-    const int64_t r = arow * HD + c0;
+  constexpr int LPR = HD / VEC;  // lanes per row
+  constexpr int RG = 256 / LPR;  // row-groups per chunk
+  constexpr int LC = RG * S;     // rows per chunk
+  constexpr int NH = HD / 64;    // channel halves of the tree waves
+  static_assert(HD % 64 == 0 && LPR <= 64, "layout");
+  __shared__ float s_A[RG][HD];
+  __shared__ float s_Bk[RG][HD];
+  __shared__ float s_Bv[RG][HD];
+  __shared__ float s_lk[HD];
+  __shared__ float s_lv[HD];
+  __shared__ uint32_t s_epoch;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  if (tid == 0) s_epoch = ld_acquire_u32(p.rhdr + kEpochWord);
+  __syncthreads();
+  const uint32_t epoch = s_epoch;
+  const uint32_t tag = tree_tag(epoch);
+  const int T = p.T;
+  const int nseq = p.B * p.H;
+  const uint32_t n = (uint32_t)nseq * (uint32_t)p.nchunk;
+  const int r = tid / LPR;
+  const int c0 = (tid - r * LPR) * VEC;
+
+  for (uint32_t ticket = blockIdx.x; ticket < n; ticket += gridDim.x) {
+    const int rc = (int)(ticket / (uint32_t)nseq);
+    const int seq = (int)(ticket - (uint32_t)rc * (uint32_t)nseq);
+    const int chunk = p.nchunk - 1 - rc;
+    const int b = seq / p.H;
+    const int h = seq - b * p.H;
+    const int D = p.ht.D[h];
+    const int W = p.ht.W[h];
+    const int64_t bh = (int64_t)seq;
+    const int64_t off = bh * T * HD + c0;
+    const int tbase = chunk * LC + r * S;
+    const int64_t arow0 = (int64_t)b * p.R + p.ht.aoff[h];
+
+    // ---- loads (unconditional, rows clamped to the sequence) ---------------
+    u32x4 gr[S + 1], qr[S], orow[S];
+    f32x2 own[S];
 #pragma unroll
-    for (int j = 0; j < VEC / 4; ++j) {
-      in.ak[j] = *reinterpret_cast<const f32x4*>(p.dKc + r + 4 * j);
-      in.av[j] = *reinterpret_cast<const f32x4*>(p.dVc + r + 4 * j);
+    for (int s = 0; s <= S; ++s)
+      gr[s] = ld_raw16(reinterpret_cast<const ST*>(p.g) + off + (int64_t)min(tbase + s, T - 1) * HD);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int t = min(tbase + s, T - 1);
+      qr[s] = ld_raw16(reinterpret_cast<const ST*>(p.q) + off + (int64_t)t * HD);
+      orow[s] = ld_raw16(reinterpret_cast<const ST*>(p.dO) + off + (int64_t)t * HD);
+      own[s] = *reinterpret_cast<const f32x2*>(p.own + 2 * (bh * T + t));
     }
-  }
-}
-
-// the state gradients of position t for the lane's VEC channels: own term
-// (scalars from kernel 1 times q_t and dO_t), window gradient (W > 0) and, at
-// an anchor position, the anchor's gradient
-template <typename ST, int HD>
-__device__ __forceinline__ void dh_from(const BwdParams& p, int64_t bh, int t, int c0, int W,
-                                        bool anchor, const RowIn<ST>& in,
-                                        float (&k)[StTraits<ST>::VEC],
-                                        float (&v)[StTraits<ST>::VEC]) {
-  constexpr int VEC = StTraits<ST>::VEC;
-  float qv[VEC], ov[VEC];
-  unpack16(in.q, qv, (ST*)nullptr);
-  unpack16(in.o, ov, (ST*)nullptr);
+    // dh of row s (t = tbase + s): the own term from the kept q, dO and
+    // scalars, plus the window and anchor gradients (read where they exist;
+    // pass 2 reads them again, from L2)
+    auto dh_row = [&](int s, float (&dk)[VEC], float (&dv)[VEC]) {
+      const int t = min(tbase + s, T - 1);
+      float qv[VEC], ov[VEC];
+      unpack16(qr[s], qv, (ST*)nullptr);
+      unpack16(orow[s], ov, (ST*)nullptr);
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    k[e] = in.own[0] * qv[e];
-    v[e] = in.own[1] * ov[e];
-  }
-  if (W > 0) {
-    const int64_t i = (bh * p.T + t) * HD + c0;
+      for (int e = 0; e < VEC; ++e) {
+        dk[e] = own[s][0] * qv[e];
+        dv[e] = own[s][1] * ov[e];
+      }
+      if (W > 0) {
+        const int64_t i = off + (int64_t)t * HD;
 #pragma unroll
-    for (int e = 0; e < VEC; e += 4) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(p.dhk + i + e);
-      const f32x4 c = *reinterpret_cast<const f32x4*>(p.dhv + i + e);
+        for (int e = 0; e < VEC; e += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(p.dhk + i + e);
+          const f32x4 y = *reinterpret_cast<const f32x4*>(p.dhv + i + e);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        k[e + j] += a[j];
-        v[e + j] += c[j];
+          for (int j = 0; j < 4; ++j) {
+            dk[e + j] += x[j];
+            dv[e + j] += y[j];
+          }
+        }
+      }
+      if (t % D == D - 1) {
+        const int64_t i = (arow0 + t / D) * HD + c0;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(p.dKc + i + e);
+          const f32x4 y = *reinterpret_cast<const f32x4*>(p.dVc + i + e);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dk[e + j] += x[j];
+            dv[e + j] += y[j];
+          }
+        }
+      }
+    };
+    // ---- pass 1: the lane's map (last row first) -----------------------------
+    {
+      float A[VEC], Bk[VEC], Bv[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        A[e] = 1.f;
+        Bk[e] = 0.f;
+        Bv[e] = 0.f;
+      }
+#pragma unroll
+      for (int s = S - 1; s >= 0; --s) {
+        const int t = tbase + s;
+        if (t < T) {
+          float an[VEC], dk[VEC], dv[VEC];
+          unpack16(gr[s + 1], an, (ST*)nullptr);
+          dh_row(s, dk, dv);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float a = t + 1 < T ? an[e] : 0.f;
+            A[e] *= a;
+            Bk[e] = a * Bk[e] + dk[e];
+            Bv[e] = a * Bv[e] + dv[e];
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        s_A[r][c0 + e] = A[e];
+        s_Bk[r][c0 + e] = Bk[e];
+        s_Bv[r][c0 + e] = Bv[e];
       }
     }
-  }
-  if (anchor) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      k[e] += in.ak[e / 4][e % 4];
-      v[e] += in.av[e / 4][e % 4];
-    }
-  }
-}
+    __syncthreads();
 
-template <typename ST, int HD>
-__global__ __launch_bounds__(256) void bwd_rscan_agg_kernel(const BwdParams p) {
-  using R = RCfg<ST, HD>;
-  constexpr int VEC = R::VEC;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int ch = blockIdx.x * R::CPB + (int)threadIdx.x / R::LPR;
-  const int c0 = ((int)threadIdx.x % R::LPR) * VEC;
-  if (ch >= p.nchunk) return;
-  const int T = p.T;
-  const int D = p.ht.D[h];
-  const int W = p.ht.W[h];
-  const int64_t bh = (int64_t)b * p.H + h;
-  const int64_t arow0 = (int64_t)b * p.R + p.ht.aoff[h];
-  const ST* gp = reinterpret_cast<const ST*>(p.g) + bh * T * HD + c0;
-  const int s = ch * kRChunk;
-  const int e = min(T, s + kRChunk) - 1;
-  float A[VEC], lk[VEC], lv[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    A[j] = 1.f;
-    lk[j] = 0.f;
-    lv[j] = 0.f;
-  }
-  for (int t1 = e; t1 >= s; t1 -= kRBatch) {
-    // loads of rows t1, t1-1, ... (clamped to the chunk; the clamped ones
-    // are not used)
-    u32x4 gn[kRBatch];
-    RowIn<ST> in[kRBatch];
-#pragma unroll
-    for (int u = 0; u < kRBatch; ++u) {
-      const int t = max(t1 - u, s);
-      gn[u] = ld_raw16(gp + (int64_t)min(t + 1, T - 1) * HD);
-      row_load<ST, HD>(p, bh, t, c0, arow0 + t / D, t % D == D - 1, in[u]);
+    // ---- the row-groups (from the last), the tree, the carry ----------------
+    if (wave < NH) {
+      const int half = wave;
+      const int c = 64 * half + lane;
+      float ra = 1.f, rbk = 0.f, rbv = 0.f;
+      for (int rr = RG - 1; rr >= 0; --rr) {
+        const float a = s_A[rr][c], bk = s_Bk[rr][c], bv = s_Bv[rr][c];
+        s_A[rr][c] = ra;  // map of the row-groups after rr
+        s_Bk[rr][c] = rbk;
+        s_Bv[rr][c] = rbv;
+        rbk = a * rbk + bk;
+        rbv = a * rbv + bv;
+        ra = ra * a;
+      }
+      tree_publish<HD>(p.ragg, p.rhdr, p.rnlevels, p.rlbase, p.rnodes, seq, rc, half, ra, rbk,
+                       rbv, tag, lane);
+    } else if (wave >= 2 && wave < 2 + NH) {
+      const int half = wave - 2;
+      float one = 1.f, lk = 0.f, lv = 0.f;  // lambda after the last position is 0
+      tree_carry<HD>(p.ragg, p.rhdr, p.rnlevels, p.rlbase, p.rnodes, seq, rc, half, one, lk, lv,
+                     tag, lane);
+      s_lk[64 * half + lane] = lk;
+      s_lv[64 * half + lane] = lv;
     }
+    __syncthreads();
+    // pass-2 rows: k, v of the lane's rows, the stored states of the rows
+    // before them (after the carry)
+    u32x4 kr[S], vr[S], pk[S], pv[S];
 #pragma unroll
-    for (int u = 0; u < kRBatch; ++u) {
-      const int t = t1 - u;
-      if (t >= s) {
-        float gf[VEC], dk[VEC], dv[VEC];
-        unpack16(gn[u], gf, (ST*)nullptr);
-        dh_from<ST, HD>(p, bh, t, c0, W, t % D == D - 1, in[u], dk, dv);
+    for (int s = 0; s < S; ++s) {
+      const int64_t rt = (int64_t)min(tbase + s, T - 1) * HD;
+      const int64_t rp = (int64_t)max(min(tbase + s, T - 1) - 1, 0) * HD;
+      kr[s] = ld_raw16(reinterpret_cast<const ST*>(p.k) + off + rt);
+      vr[s] = ld_raw16(reinterpret_cast<const ST*>(p.v) + off + rt);
+      pk[s] = ld_raw16(reinterpret_cast<const ST*>(p.hk) + off + rp);
+      pv[s] = ld_raw16(reinterpret_cast<const ST*>(p.hv) + off + rp);
+    }
+
+    // ---- pass 2: the rows from the carry, last row first --------------------
+    {
+      float lk[VEC], lv[VEC];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          const float gj = t + 1 < T ? gf[j] : 0.f;
-          lk[j] = dk[j] + gj * lk[j];
-          lv[j] = dv[j] + gj * lv[j];
-          A[j] *= gj;
+      for (int e = 0; e < VEC; ++e) {
+        const int c = c0 + e;
+        lk[e] = s_A[r][c] * s_lk[c] + s_Bk[r][c];
+        lv[e] = s_A[r][c] * s_lv[c] + s_Bv[r][c];
+      }
+      ST* dkp = reinterpret_cast<ST*>(p.dk) + off;
+      ST* dvp = reinterpret_cast<ST*>(p.dv) + off;
+      ST* dgp = reinterpret_cast<ST*>(p.dg) + off;
+#pragma unroll
+      for (int s = S - 1; s >= 0; --s) {
+        const int t = tbase + s;
+        if (t < T) {
+          float an[VEC], gt[VEC], kv[VEC], vv[VEC], hkp[VEC], hvp[VEC], dk[VEC], dv[VEC];
+          dh_row(s, dk, dv);
+          unpack16(gr[s + 1], an, (ST*)nullptr);
+          unpack16(gr[s], gt, (ST*)nullptr);
+          unpack16(kr[s], kv, (ST*)nullptr);
+          unpack16(vr[s], vv, (ST*)nullptr);
+          unpack16(pk[s], hkp, (ST*)nullptr);
+          unpack16(pv[s], hvp, (ST*)nullptr);
+          float ok[VEC], ov[VEC], og[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float a = t + 1 < T ? an[e] : 0.f;
+            lk[e] = dk[e] + a * lk[e];
+            lv[e] = dv[e] + a * lv[e];
+            const float hk_prev = t > 0 ? hkp[e] : 0.f;
+            const float hv_prev = t > 0 ? hvp[e] : 0.f;
+            ok[e] = (1.f - gt[e]) * lk[e];
+            ov[e] = (1.f - gt[e]) * lv[e];
+            og[e] = lk[e] * (hk_prev - kv[e]) + lv[e] * (hv_prev - vv[e]);
+          }
+          const int64_t rt = (int64_t)t * HD;
+          st_raw16(dkp + rt, pack16(ok, (ST*)nullptr));
+          st_raw16(dvp + rt, pack16(ov, (ST*)nullptr));
+          st_raw16(dgp + rt, pack16(og, (ST*)nullptr));
         }
       }
     }
+    __syncthreads();  // LDS is reused by the next chunk
   }
-  float* a = p.agg + ((bh * p.nchunk + ch) * 3) * HD + c0;
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    a[j] = A[j];
-    a[HD + j] = lk[j];
-    a[2 * HD + j] = lv[j];
-  }
-}
 
-// lambda after each chunk: one lane per channel walks the chunks backwards,
-// the maps of 16 chunks loaded per round trip
-template <int HD>
-__global__ __launch_bounds__(HD) void bwd_rscan_carry_kernel(const BwdParams p) {
-  constexpr int CB = 16;
-  const int64_t bh = blockIdx.x;
-  const int c = threadIdx.x;
-  float lk = 0.f, lv = 0.f;  // lambda at the position after the chunk
-  for (int ch1 = p.nchunk - 1; ch1 >= 0; ch1 -= CB) {
-    float a[CB][3];
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const float* ap = p.agg + ((bh * p.nchunk + max(ch1 - u, 0)) * 3) * HD + c;
-      a[u][0] = ap[0];
-      a[u][1] = ap[HD];
-      a[u][2] = ap[2 * HD];
-    }
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const int ch = ch1 - u;
-      if (ch >= 0) {
-        float* cr = p.carry + ((bh * p.nchunk + ch) * 2) * HD + c;
-        cr[0] = lk;
-        cr[HD] = lv;
-        lk = a[u][0] * lk + a[u][1];
-        lv = a[u][0] * lv + a[u][2];
-      }
-    }
-  }
-}
-
-template <typename ST, int HD>
-__global__ __launch_bounds__(256) void bwd_rscan_apply_kernel(const BwdParams p) {
-  using R = RCfg<ST, HD>;
-  constexpr int VEC = R::VEC;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int ch = blockIdx.x * R::CPB + (int)threadIdx.x / R::LPR;
-  const int c0 = ((int)threadIdx.x % R::LPR) * VEC;
-  if (ch >= p.nchunk) return;
-  const int T = p.T;
-  const int D = p.ht.D[h];
-  const int W = p.ht.W[h];
-  const int64_t bh = (int64_t)b * p.H + h;
-  const int64_t arow0 = (int64_t)b * p.R + p.ht.aoff[h];
-  const int64_t off = bh * T * HD + c0;
-  const ST* gp = reinterpret_cast<const ST*>(p.g) + off;
-  const ST* kp = reinterpret_cast<const ST*>(p.k) + off;
-  const ST* vp = reinterpret_cast<const ST*>(p.v) + off;
-  const ST* hkp = reinterpret_cast<const ST*>(p.hk) + off;
-  const ST* hvp = reinterpret_cast<const ST*>(p.hv) + off;
-  ST* dkp = reinterpret_cast<ST*>(p.dk) + off;
-  ST* dvp = reinterpret_cast<ST*>(p.dv) + off;
-  ST* dgp = reinterpret_cast<ST*>(p.dg) + off;
-  const int s = ch * kRChunk;
-  const int e = min(T, s + kRChunk) - 1;
-  const float* cr = p.carry + ((bh * p.nchunk + ch) * 2) * HD + c0;
-  float lk[VEC], lv[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    lk[j] = cr[j];
-    lv[j] = cr[HD + j];
-  }
-  // g of the position after t: loaded once before the loop, then the
-  // previous row's g_t (each g row is read once per chunk)
-  float gn[VEC];
-  unpack16(ld_raw16(gp + (int64_t)min(e + 1, T - 1) * HD), gn, (ST*)nullptr);
-  for (int t1 = e; t1 >= s; t1 -= kRBatch) {
-    u32x4 G[kRBatch], K[kRBatch], V[kRBatch], PK[kRBatch], PV[kRBatch];
-    RowIn<ST> in[kRBatch];
-#pragma unroll
-    for (int u = 0; u < kRBatch; ++u) {
-      const int t = max(t1 - u, s);
-      const int64_t r = (int64_t)t * HD;
-      const int64_t rp = (int64_t)max(t - 1, 0) * HD;
-      G[u] = ld_raw16(gp + r);
-      K[u] = ld_raw16(kp + r);
-      V[u] = ld_raw16(vp + r);
-      PK[u] = ld_raw16(hkp + rp);
-      PV[u] = ld_raw16(hvp + rp);
-      row_load<ST, HD>(p, bh, t, c0, arow0 + t / D, t % D == D - 1, in[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kRBatch; ++u) {
-      const int t = t1 - u;
-      if (t >= s) {
-        const int64_t r = (int64_t)t * HD;
-        float gt[VEC], kv[VEC], vv[VEC], pk[VEC], pv[VEC];
-        unpack16(G[u], gt, (ST*)nullptr);
-        unpack16(K[u], kv, (ST*)nullptr);
-        unpack16(V[u], vv, (ST*)nullptr);
-        unpack16(PK[u], pk, (ST*)nullptr);
-        unpack16(PV[u], pv, (ST*)nullptr);
-        float dk[VEC], dv[VEC];
-        dh_from<ST, HD>(p, bh, t, c0, W, t % D == D - 1, in[u], dk, dv);
-        float ok[VEC], ov[VEC], og[VEC];
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          const float gj = t + 1 < T ? gn[j] : 0.f;
-          lk[j] = dk[j] + gj * lk[j];
-          lv[j] = dv[j] + gj * lv[j];
-          const float hk_prev = t > 0 ? pk[j] : 0.f;
-          const float hv_prev = t > 0 ? pv[j] : 0.f;
-          ok[j] = (1.f - gt[j]) * lk[j];
-          ov[j] = (1.f - gt[j]) * lv[j];
-          og[j] = lk[j] * (hk_prev - kv[j]) + lv[j] * (hv_prev - vv[j]);
-        }
-        st_raw16(dkp + r, pack16(ok, (ST*)nullptr));
-        st_raw16(dvp + r, pack16(ov, (ST*)nullptr));
-        st_raw16(dgp + r, pack16(og, (ST*)nullptr));
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) gn[j] = gt[j];
-      }
-    }
-  }
+  // retire: the last workgroup advances the epoch
+  if (tid == 0) tree_retire(p.rhdr, epoch);
 }
 
 template <typename ST, int HD>
@@ -922,10 +904,15 @@ int launch_t(const BwdParams& p, hipStream_t st) {
     hipLaunchKernelGGL(bwd_anchor_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
                        p.dKc, p.dVc, n4, p.nsplit);
   }
-  const int ncb = (p.nchunk + RCfg<ST, HD>::CPB - 1) / RCfg<ST, HD>::CPB;
-  hipLaunchKernelGGL((bwd_rscan_agg_kernel<ST, HD>), dim3(ncb, p.H, p.B), dim3(256), 0, st, p);
-  hipLaunchKernelGGL((bwd_rscan_carry_kernel<HD>), dim3(p.B * p.H), dim3(HD), 0, st, p);
-  hipLaunchKernelGGL((bwd_rscan_apply_kernel<ST, HD>), dim3(ncb, p.H, p.B), dim3(256), 0, st, p);
+  // the reverse scan: persistent, at most as many workgroups as the device
+  // holds at once (every wait is on a smaller ticket of a resident one)
+  const void* kern = reinterpret_cast<const void*>(&bwd_rscan_kernel<ST, HD, kScanRowsPerThread>);
+  const int lim = coop_grid_limit(kern, 256);
+  if (lim <= 0) return (int)hipErrorInvalidValue;
+  const int64_t nticket = (int64_t)p.B * p.H * p.nchunk;
+  const unsigned grid = (unsigned)std::min<int64_t>(nticket, lim);
+  hipLaunchKernelGGL((bwd_rscan_kernel<ST, HD, kScanRowsPerThread>), dim3(grid), dim3(256), 0, st,
+                     p);
   return (int)hipGetLastError();
 }
 

@@ -623,10 +623,15 @@ namespace {
 // [B*H][nchunk][3][hd], carries [B*H][nchunk][2][hd].
 constexpr int kBwdMaxSplit = 8;
 
+// Backward workspace: the reverse scan's tree first (the forward scan's
+// layout: header, then the tagged tree entries; sized for either storage
+// type, so the header sits at offset 0 and a buffer zero-filled once serves
+// calls of any size that fits), then the per-call intermediates.
 struct BwdLayout {
-  int64_t R = 0, nchunk = 0;
+  int64_t R = 0;
+  int64_t tree_bytes = 0;
   int64_t off_delta = 0, off_own = 0, off_dhk = 0, off_dhv = 0, off_dkc = 0, off_dvc = 0,
-          off_agg = 0, off_carry = 0, bytes = 0;
+          bytes = 0;
 };
 
 bool bwd_layout(int B, int H, int64_t T, int hd, const int32_t* D, const int32_t* W,
@@ -637,20 +642,21 @@ bool bwd_layout(int B, int H, int64_t T, int hd, const int32_t* D, const int32_t
     L.R += T / D[h];
     window = window || (W != nullptr && W[h] > 0);
   }
-  L.nchunk = (T + 63) / 64;
+  ScanLayout tb, tf;
+  if (!scan_layout(B, H, T, hd, RAT_DTYPE_BF16, tb) || !scan_layout(B, H, T, hd, RAT_DTYPE_F32, tf))
+    return false;
+  L.tree_bytes = std::max(tb.bytes, tf.bytes);
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   const int64_t bh = (int64_t)B * H;
   const int64_t dh = window ? bh * T * hd * 4 : 0;
-  int64_t o = 0;
+  int64_t o = up(L.tree_bytes);
   L.off_delta = o; o = up(o + bh * T * 4);
   L.off_own = o; o = up(o + bh * T * 8);
   L.off_dhk = o; o = up(o + dh);
   L.off_dhv = o; o = up(o + dh);
   L.off_dkc = o; o = up(o + kBwdMaxSplit * (int64_t)B * L.R * hd * 4);
   L.off_dvc = o; o = up(o + kBwdMaxSplit * (int64_t)B * L.R * hd * 4);
-  L.off_agg = o; o = up(o + bh * L.nchunk * 3 * hd * 4);
-  L.off_carry = o; o = up(o + bh * L.nchunk * 2 * hd * 4);
-  L.bytes = std::max<int64_t>(o, 256);
+  L.bytes = o;
   return L.R <= INT32_MAX && bh * T * hd < ((int64_t)1 << 62);
 }
 
@@ -701,7 +707,15 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
   p.scale = sc;
   p.scale_log2 = sc * 1.4426950408889634f;
   p.R = R;
-  p.nchunk = (int)L.nchunk;
+  ScanLayout tl;
+  if (!scan_layout(B, H, T, hd, dtype, tl)) return RAT_ERR_UNSUPPORTED;
+  if (tl.nticket > INT32_MAX) return RAT_ERR_UNSUPPORTED;
+  p.nchunk = (int)tl.nchunk;
+  p.rnlevels = tl.nlevels;
+  for (int l = 0; l < tl.nlevels; ++l) {
+    p.rnodes[l] = tl.nodes[l];
+    p.rlbase[l] = tl.lbase[l];
+  }
   // the queries of an anchor tile are shared by nsplit workgroups (partial
   // sums) so that the key-side grid holds about two workgroups per CU
   int64_t max_na_t = 0;
@@ -722,7 +736,7 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
     const int64_t nb_t = W[h] > 0 ? (T + 63) / 64 : 0;
     nkt = std::max(nkt, na_t * nsplit + nb_t);
   }
-  if ((int64_t)B * H * L.nchunk > INT32_MAX || nkt > INT32_MAX) return RAT_ERR_UNSUPPORTED;
+  if (nkt > INT32_MAX) return RAT_ERR_UNSUPPORTED;
   p.nkt = (int)nkt;
   p.nsplit = nsplit;
   // dq with the anchors resident in LDS: bf16, no window, every head's
@@ -763,8 +777,8 @@ int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd, const int32
   p.dhv = reinterpret_cast<float*>(ws + L.off_dhv);
   p.dKc = reinterpret_cast<float*>(ws + L.off_dkc);
   p.dVc = reinterpret_cast<float*>(ws + L.off_dvc);
-  p.agg = reinterpret_cast<float*>(ws + L.off_agg);
-  p.carry = reinterpret_cast<float*>(ws + L.off_carry);
+  p.rhdr = reinterpret_cast<uint32_t*>(ws);
+  p.ragg = reinterpret_cast<uint64_t*>(ws + tl.agg_off);
   return map_hip(launch_backward(dtype, hd, p, stream));
 }
 

@@ -152,7 +152,7 @@ struct BwdParams {
   float scale;       // score scale
   float scale_log2;  // scale * log2(e)
   int64_t R;         // anchor rows per batch row (floor(T / D_h) summed over heads)
-  int nchunk;        // reverse-scan chunks of 64 positions per sequence
+  int nchunk;        // reverse-scan chunks per sequence (scan_rows_per_chunk rows each)
   int nkt;           // workgroups per head in the key-side grid (max over heads)
   int nsplit;        // workgroups sharing the queries of one anchor tile
   int nra;           // > 0: dq with the anchors resident in LDS, nra workgroups per (b, h)
@@ -176,8 +176,14 @@ struct BwdParams {
   float* dhv;
   float* dKc;        // workspace: [nsplit][B,R,hd] partial anchor gradients
   float* dVc;
-  float* agg;        // workspace: [B*H][nchunk][3][hd] reverse-scan chunk maps
-  float* carry;      // workspace: [B*H][nchunk][2][hd] lambda after each chunk
+  // the reverse scan's chunk-aggregate tree (the forward scan's protocol):
+  // header words, then [entries][3][hd] tagged words; level l holds
+  // rnodes[l] nodes per sequence from entry rlbase[l]
+  uint32_t* rhdr;
+  uint64_t* ragg;
+  int rnlevels;
+  int rnodes[kScanMaxLevels];
+  int64_t rlbase[kScanMaxLevels];
   HeadTables ht;
 };
 
@@ -216,6 +222,9 @@ int launch_topk_cache_build(int dtype, int hd, int B, int H, int64_t T, int64_t 
 constexpr int kScanThreads = 256;
 constexpr int kScanRowsPerThread = 4;
 int scan_rows_per_chunk(int dtype, int hd);
+// Largest grid of `kernel` (at `threads` per workgroup) whose workgroups can
+// all be resident at once on the current device; <= 0 on error.
+int coop_grid_limit(const void* kernel, int threads);
 
 constexpr int kAttnBN = 64;    // keys per LDS tile
 constexpr int kDecodeThreads = 256;

@@ -37,119 +37,11 @@
 #include <mutex>
 #include <utility>
 
-#include "rat_device.h"
+#include "scan_tree.h"
 
 namespace rat {
 
 namespace {
-
-constexpr uint32_t kSpinLimit = 1u << 16;
-
-__device__ __forceinline__ uint32_t ld_acquire_u32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_relaxed_u32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent_f32(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ void st_coherent_f32(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Workspace header words (uint32): the launch epoch, the error flag, and the
-// done counters that let the last block advance the epoch.  Counters sit
-// 256 bytes apart so their atomics do not queue on one address.
-constexpr int kEpochWord = 0;
-constexpr int kErrorWord = 2;
-constexpr int kTopWord = 32;
-constexpr int kDoneBase = 64;
-constexpr int kDoneStride = 64;
-constexpr int kDoneSlots = 64;
-static_assert(kDoneBase + kDoneSlots * kDoneStride <= kScanHeaderBytes / 4, "header");
-
-constexpr int kScanRadixLog2 = 3;
-static_assert((1 << kScanRadixLog2) == kScanRadix, "radix");
-
-// Wait until this wave's earlier global accesses have completed.  Every
-// workspace access below is a coherent (agent-scope, sc1) atomic access, so
-// completion order is all the publication protocol needs: data stores
-// complete before the tag store is issued, and data loads are issued only
-// after the tag load has returned.  No cache write-back or invalidation is
-// required (an agent-scope fence would write back / invalidate the whole L2
-// of the XCD on every call).
-__device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// The hd channels are independent; the tree works on 64-channel halves, one
-// wave per half with one channel per lane.  Every published value is a 64-bit
-// word (launch tag << 32 | fp32 bits) written and read with single-copy
-// atomic 64-bit accesses, so a reader that sees the current tag in a word
-// also sees its value: no separate flag, no store drain, one round trip.
-__device__ __forceinline__ void st_tagged(uint64_t* p, uint32_t tag, float v) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Publish one half of a tree node (A, Bk, Bv of this lane's channel).
-template <int HD>
-__device__ __forceinline__ void publish_node(const ScanParams& p, int64_t e, int half, float A,
-                                             float Bk, float Bv, uint32_t tag, int lane) {
-  uint64_t* d = p.agg + e * 3 * HD + 64 * half + lane;
-  st_tagged(d, tag, A);
-  st_tagged(d + HD, tag, Bk);
-  st_tagged(d + 2 * HD, tag, Bv);
-}
-
-// Compose the n (< radix) consecutive nodes [e0, e0 + n), in order, after
-// the running map (A, Bk, Bv) of one channel.  All 3n words are loaded at
-// once and re-loaded until every tag in the wave is current; every wait is
-// bounded.
-template <int HD>
-__device__ __forceinline__ void fold_nodes(const ScanParams& p, int64_t e0, int n, int half,
-                                           float& A, float& Bk, float& Bv, uint32_t tag,
-                                           int lane) {
-  if (n <= 0) return;
-  uint64_t w[kScanRadix - 1][3];
-  uint32_t spins = 0;
-  while (true) {
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < kScanRadix - 1; ++i) {
-      if (i < n) {
-        const uint64_t* d = p.agg + (e0 + i) * 3 * HD + 64 * half + lane;
-        w[i][0] = ld_tagged(d);
-        w[i][1] = ld_tagged(d + HD);
-        w[i][2] = ld_tagged(d + 2 * HD);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kScanRadix - 1; ++i)
-      if (i < n)
-        ok = ok && (uint32_t)(w[i][0] >> 32) == tag && (uint32_t)(w[i][1] >> 32) == tag &&
-             (uint32_t)(w[i][2] >> 32) == tag;
-    if (__all(ok)) break;
-    if (++spins > kSpinLimit) {
-      if (lane == 0) st_relaxed_u32(p.hdr + kErrorWord, 1u);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-#pragma unroll
-  for (int i = 0; i < kScanRadix - 1; ++i) {
-    if (i < n) {
-      const float a = __uint_as_float((uint32_t)w[i][0]);
-      Bk = a * Bk + __uint_as_float((uint32_t)w[i][1]);
-      Bv = a * Bv + __uint_as_float((uint32_t)w[i][2]);
-      A = A * a;
-    }
-  }
-}
 
 template <typename ST, int HD, int S>
 struct ChunkRows {
@@ -292,19 +184,8 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
       // A node of level l+1 is the in-order composition of its radix
       // children; the chunk that owns the last child computes and publishes
       // it.
-      int64_t node = chunk;
-      for (int lv = 0; lv < p.nlevels; ++lv) {
-        const int64_t lvl0 = p.lbase[lv] + (int64_t)seq * p.nodes[lv];
-        publish_node<HD>(p, lvl0 + node, half, ra, rbk, rbv, tag, lane);
-        if (lv + 1 >= p.nlevels || (node % kScanRadix) != kScanRadix - 1) break;
-        float fA = 1.f, fBk = 0.f, fBv = 0.f;
-        fold_nodes<HD>(p, lvl0 + node - (kScanRadix - 1), kScanRadix - 1, half, fA, fBk, fBv,
+      tree_publish<HD>(p.agg, p.hdr, p.nlevels, p.lbase, p.nodes, seq, chunk, half, ra, rbk, rbv,
                        tag, lane);
-        rbk = ra * fBk + rbk;  // then this node itself
-        rbv = ra * fBv + rbv;
-        ra = fA * ra;
-        node /= kScanRadix;
-      }
     } else if (wave >= 2 && wave < 2 + NH) {
       const int half = wave - 2;
       // the state before row 0: zero for a prefill, the given state for a
@@ -312,12 +193,8 @@ __device__ __forceinline__ void scan_chunk(const ScanParams& p, uint32_t ticket,
       float one = 1.f;
       float hin_k = p.sk_in != nullptr ? p.sk_in[(int64_t)seq * HD + 64 * half + lane] : 0.f;
       float hin_v = p.sv_in != nullptr ? p.sv_in[(int64_t)seq * HD + 64 * half + lane] : 0.f;
-      for (int lv = p.nlevels - 1; lv >= 0; --lv) {
-        const int64_t nd = (int64_t)chunk >> (kScanRadixLog2 * lv);
-        const int64_t first = nd & ~(int64_t)(kScanRadix - 1);
-        const int64_t lvl0 = p.lbase[lv] + (int64_t)seq * p.nodes[lv];
-        fold_nodes<HD>(p, lvl0 + first, (int)(nd - first), half, one, hin_k, hin_v, tag, lane);
-      }
+      tree_carry<HD>(p.agg, p.hdr, p.nlevels, p.lbase, p.nodes, seq, chunk, half, one, hin_k,
+                     hin_v, tag, lane);
       s_hk[64 * half + lane] = hin_k;
       s_hv[64 * half + lane] = hin_v;
     }
@@ -421,7 +298,7 @@ void scan_kernel(const ScanParams p) {
   if (tid == 0) s_epoch = ld_acquire_u32(p.hdr + kEpochWord);
   __syncthreads();
   const uint32_t epoch = s_epoch;
-  const uint32_t tag = (epoch % 0x3FFFFFFFu) + 1u;
+  const uint32_t tag = tree_tag(epoch);
   const uint32_t G = gridDim.x;
 
   // Two register buffers: the rows of the next chunk are loaded while the
@@ -445,22 +322,8 @@ void scan_kernel(const ScanParams p) {
     ticket = t2;
   }
 
-  // retire: two-level done count; the last workgroup advances the epoch
-  if (tid == 0) {
-    const uint32_t slot = blockIdx.x % kDoneSlots;
-    const uint32_t in_slot = (G - 1 - slot) / kDoneSlots + 1;
-    const uint32_t used = G < (uint32_t)kDoneSlots ? G : (uint32_t)kDoneSlots;
-    vm_drain();
-    uint32_t* ctr = p.hdr + kDoneBase + slot * kDoneStride;
-    if (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_slot - 1) {
-      st_relaxed_u32(ctr, 0u);
-      uint32_t* top = p.hdr + kTopWord;
-      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == used - 1) {
-        st_relaxed_u32(top, 0u);
-        st_relaxed_u32(p.hdr + kEpochWord, epoch + 1u);
-      }
-    }
-  }
+  // retire: the last workgroup advances the epoch
+  if (tid == 0) tree_retire(p.hdr, epoch);
 }
 
 // T = 0: the state is the state before row 0 (zero for a prefill)
@@ -498,25 +361,6 @@ __global__ void ring_carry_kernel(const ST* __restrict__ kin, const ST* __restri
   st_raw16(vout + off, ld_raw16(vin + off));
 }
 
-// Largest grid whose workgroups can all be resident at once (cached per
-// device and kernel; the cache is the library's only mutable state, written
-// once under a lock).
-int coop_grid_limit(const void* kernel, int threads) {
-  static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find({dev, kernel});
-  if (it != cache.end()) return it->second;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return -1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  const int lim = per_cu * cus;
-  cache[{dev, kernel}] = lim;
-  return lim;
-}
-
 template <typename ST, int HD>
 int launch_scan_t(const ScanParams& p, hipStream_t st) {
   if (p.T == 0) {
@@ -550,6 +394,25 @@ int launch_scan_t(const ScanParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+// Largest grid whose workgroups can all be resident at once (cached per
+// device and kernel; the cache is the library's only mutable state, written
+// once under a lock).
+int coop_grid_limit(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, kernel});
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  const int lim = per_cu * cus;
+  cache[{dev, kernel}] = lim;
+  return lim;
+}
 
 int scan_rows_per_chunk(int dtype, int hd) {
   const int vec = dtype == RAT_DTYPE_BF16 ? 8 : 4;

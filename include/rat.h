@@ -323,7 +323,11 @@ int rat_decode_step_topk(int dtype, int B, int H, int hd, const int32_t* D,
 
 /*
  * Bytes of device workspace rat_prefill_backward needs for (B, H, T, hd, D,
- * W).  Pure host function; returns bytes (> 0) or a negative code.
+ * W).  Zero-fill it once before its first use; afterwards it is ready for
+ * every later call of this size or smaller (it starts with the reverse
+ * scan's tree workspace, laid out as the forward scan's, whose header sits
+ * at offset 0 for every size).  Pure host function; returns bytes (> 0) or
+ * a negative code.
  */
 int64_t rat_prefill_backward_workspace_bytes(int B, int H, int64_t T, int hd,
                                              const int32_t* D, const int32_t* W);
@@ -348,8 +352,14 @@ int64_t rat_prefill_backward_workspace_bytes(int B, int H, int64_t T, int hd,
  *                             scale)
  *        lse                  [B, H, T] fp32 (rat_dilated_attn_prefill's lse)
  * Writes dq, dk, dv, dg       [B, H, T, hd] ST
- * workspace: rat_prefill_backward_workspace_bytes bytes (fp32 intermediates;
- * no initialisation needed).  scale <= 0 selects 1/sqrt(hd).
+ * workspace: rat_prefill_backward_workspace_bytes bytes, zero-filled once
+ * (the reverse scan's chunk tree, then fp32 intermediates).  The reverse
+ * recurrence is one persistent pass whose chunks wait on the maps of the
+ * chunks after them; as in rat_scan_prefill every wait is bounded, and a
+ * wait that runs out sets uint32 word 2 of the workspace (sticky until the
+ * workspace is zero-filled again) instead of hanging: a caller that finds it
+ * set discards the gradients.  One workspace must not be used by two calls
+ * at once.  scale <= 0 selects 1/sqrt(hd).
  */
 int rat_prefill_backward(int dtype, int B, int H, int64_t T, int hd,
                          const int32_t* D, const int32_t* W, float scale,

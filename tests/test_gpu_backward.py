@@ -44,7 +44,9 @@ def check_grad(name, got, ref, dtype):
     assert mn <= tmean, f"{name}: relative mean error {mn}"
 
 
-def gpu_forward_backward(inp, dO, D, W, dtype):
+def gpu_forward_backward(inp, dO, D, W, dtype, bws=None, raw=False):
+    """GPU forward, then the backward on `bws` (a fresh zero-filled
+    workspace if None); the workspace's error word must stay 0."""
     import dilated_sparse_attention_rat_amd as rat
     q, k, v, g, do = (to_dev(a, dtype) for a in (inp["q"], inp["k"], inp["v"], inp["g"], dO))
     B, H, T, hd = q.shape
@@ -58,10 +60,14 @@ def gpu_forward_backward(inp, dO, D, W, dtype):
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
     rat.rat_dilated_attn_prefill(q, hk, hv, c["Kc"], c["Vc"], D, W, T, o, lse)
     grads = [torch.full_like(q, float("nan")) for _ in range(4)]
-    bws = rat.backward_workspace(B, H, T, hd, D, W, "cuda")
-    bws.fill_(-1)  # the backward needs no initialised workspace
+    if bws is None:
+        bws = rat.backward_workspace(B, H, T, hd, D, W, "cuda")
     rat.rat_prefill_backward(q, k, v, g, hk, hv, o, lse, do, D, W, *grads, bws)
     torch.cuda.synchronize()
+    assert int(ws[2].item()) == 0, "a wait of the forward scan timed out"
+    assert int(bws[2].item()) == 0, "a wait of the reverse scan timed out"
+    if raw:
+        return grads
     return dict(zip(("dq", "dk", "dv", "dg"), (to_np(x) for x in grads)))
 
 
@@ -120,3 +126,26 @@ def test_backward_workload_size_sampled():
         for n in ("dq", "dk", "dv", "dg"):
             chk(check_grad, n, got[n][sl], ref[n], w.dtype)
     chk.done()
+
+
+def test_backward_workspace_reused_bitwise():
+    """One zero-filled workspace serves repeated calls and smaller calls: the
+    reverse scan's chunk tree is tagged per launch, so the gradients equal,
+    bit for bit, those computed on a fresh workspace (its composition order
+    is fixed)."""
+    import dilated_sparse_attention_rat_amd as rat
+    B, H, hd, D, W = 2, 3, 128, np.array([4, 1, 16], np.int32), np.array([0, 37, 3], np.int32)
+    big = synth.random_case(77, B, H, 1500, hd, "bf16", hd ** -0.5, 3.0)
+    dO_big = synth.random_case(78, B, H, 1500, hd, "bf16", 1.0, 0.0)["q"]
+    bws = rat.backward_workspace(B, H, 1500, hd, D, W, "cuda")
+    say("[backward] one workspace: T=1500 twice, then T=700")
+    first = gpu_forward_backward(big, dO_big, D, W, "bf16", bws=bws, raw=True)
+    again = gpu_forward_backward(big, dO_big, D, W, "bf16", bws=bws, raw=True)
+    for a, b in zip(first, again):
+        assert torch.equal(a, b), "repeated call differs"
+    small = {n: np.ascontiguousarray(big[n][:, :, :700]) for n in "qkvg"}
+    dO_small = np.ascontiguousarray(dO_big[:, :, :700])
+    reused = gpu_forward_backward(small, dO_small, D, W, "bf16", bws=bws, raw=True)
+    fresh = gpu_forward_backward(small, dO_small, D, W, "bf16", raw=True)
+    for a, b in zip(reused, fresh):
+        assert torch.equal(a, b), "smaller call on a reused workspace differs"
