@@ -84,6 +84,11 @@ CASES = [
     ("bf16-resident", 2, 3, 1000, 128, [4, 16, 8], [0, 0, 0], "bf16"),
     ("bf16-64-resident", 1, 2, 517, 64, [3, 5], [0, 0], "bf16"),
     ("resident-no-anchor", 1, 2, 40, 128, [64, 100], [0, 0], "bf16"),
+    # reverse-scan trees of three and four levels (64-row chunks at bf16,
+    # hd 128: 71 and 516 chunks; 32-row chunks at fp32: 79 chunks)
+    ("bf16-tree-3-levels", 1, 2, 4500, 128, [16, 4], [0, 64], "bf16"),
+    ("bf16-tree-4-levels", 1, 1, 33000, 128, [256], [0], "bf16"),
+    ("f32-tree-3-levels", 1, 1, 2500, 128, [8], [16], "f32"),
 ]
 
 

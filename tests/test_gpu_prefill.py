@@ -61,6 +61,8 @@ SMALL = [
     # windowless bf16 heads with at most 256 anchors: the resident-anchor
     # kernel at hd = 64 (V staged row-major, transposing fragment reads)
     ("resident-bf16-64", 1, 2, 517, 64, [3, 5], [0, 0], "bf16", 64 ** -0.5, 3.0, 0),
+    # a chunk tree of four levels (516 chunks of 64 rows)
+    ("scan-tree-4-levels", 1, 1, 33000, 128, [256], [0], "bf16", 128 ** -0.5, 3.0, 0),
 ]
 
 
