@@ -93,11 +93,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   __shared__ float s_acc[RPP][HD];
   __shared__ float s_red[4];
 
-  const int bhi = blockIdx.x;
-  const int split = blockIdx.y;
-  const int b = bhi / p.H;
-  const int h = bhi - b * p.H;
-  const int64_t bh = bhi;
+  // block -> (head, batch row, split): classes of heads by keys read, most
+  // first (a head-wise hybrid's long dense splits start in the first wave of
+  // workgroups, the short ones fill in beside them); within a class, batch
+  // row by batch row, then head, then split
+  const int blk = blockIdx.x;
+  int r0 = 0, base = 0, r1 = p.class_end[0];
+  while (blk >= base + (r1 - r0) * p.B * p.splits) {
+    base += (r1 - r0) * p.B * p.splits;
+    r0 = r1;
+    r1 = p.class_end[r0];
+  }
+  const int per_b = (r1 - r0) * p.splits;
+  const int local = blk - base;
+  const int b = local / per_b;
+  const int rem = local - b * per_b;
+  const int rank = r0 + rem / p.splits;
+  const int split = rem - (rem / p.splits) * p.splits;
+  const int h = p.perm[rank];
+  const int64_t bh = (int64_t)b * p.H + h;
   const int D = p.ht.D[h];
   const int W = p.ht.W[h];
   const int pos = p.pos;
@@ -282,11 +296,11 @@ int launch_t(const DecodeParams& p, hipStream_t st) {
   const int nbh = p.B * p.H;
   if (nbh == 0) return 0;
   if (p.splits == 1) {
-    hipLaunchKernelGGL((decode_kernel<ST, HD, true>), dim3(nbh, 1), dim3(kDecodeThreads), 0, st, p);
+    hipLaunchKernelGGL((decode_kernel<ST, HD, true>), dim3(nbh), dim3(kDecodeThreads), 0, st, p);
     return (int)hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_kernel<ST, HD, false>), dim3(nbh, p.splits), dim3(kDecodeThreads), 0,
-                     st, p);
+  hipLaunchKernelGGL((decode_kernel<ST, HD, false>), dim3(nbh * p.splits), dim3(kDecodeThreads),
+                     0, st, p);
   int e = (int)hipGetLastError();
   if (e) return e;
   hipLaunchKernelGGL((decode_combine_kernel<ST, HD>), dim3(nbh), dim3(HD), 0, st, p);

@@ -513,8 +513,25 @@ int decode_impl(int dtype, int B, int H, int hd, const int32_t* D, const int32_t
     if (!workspace || !aligned16(workspace) || (int64_t)workspace_bytes < need)
       return RAT_ERR_WORKSPACE;
   }
-  if ((int64_t)B * H > INT32_MAX / 2) return RAT_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > INT32_MAX / 2 || (int64_t)B * H * s > INT32_MAX) return RAT_ERR_UNSUPPORTED;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)hd);
+  // heads in the grid by the keys they read, most first: a head-wise hybrid's
+  // long (dense) splits then start in the first wave of workgroups and the
+  // short ones fill in beside them
+  {
+    int64_t keys[kMaxHeads];
+    for (int h = 0; h < H; ++h) {
+      keys[h] = std::max<int64_t>(0, pos - W[h]) / D[h] + std::min<int64_t>(W[h], pos);
+      p.perm[h] = h;
+    }
+    std::stable_sort(p.perm, p.perm + H, [&](int a, int b) { return keys[a] > keys[b]; });
+    for (int r = 0; r < H;) {
+      int e = r + 1;
+      while (e < H && keys[p.perm[e]] == keys[p.perm[r]]) ++e;
+      for (int i = r; i < e; ++i) p.class_end[i] = e;
+      r = e;
+    }
+  }
   p.B = B;
   p.H = H;
   p.splits = s;

@@ -116,6 +116,11 @@ struct DecodeParams {
   void* o;
   float* part;       // [B*H][splits][2 + hd] (m, l, acc) when splits > 1
   HeadTables ht;
+  // grid order: heads by keys read, most first (perm[rank] = head); heads
+  // reading as many keys form a class, ranks [r, class_end[r]) for the first
+  // rank r of a class, and a class's blocks run batch row by batch row
+  int32_t perm[kMaxHeads];
+  int32_t class_end[kMaxHeads];
 };
 
 // Decode with top-k block selection: the decode step's fields plus the
