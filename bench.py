@@ -378,8 +378,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the RAT+ hot path "
-              "shards over (batch, head) with no exchange, and multi-GPU runs are not part "
-              "of this build", file=sys.stderr)
+              "shards over (batch, head) with no exchange, and multi-GPU runs are not "
+              "implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

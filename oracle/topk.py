@@ -8,7 +8,7 @@ attention beats plain attention sparsified the same way; zhichai.net deep
 dive "RAT+ 深度拆解", section 四 -- dilation and top-k block selection
 combine: the dilated anchors cover the whole past, the selected blocks add
 density where the query needs it.  The pages give no block size, scoring
-rule or k; this oracle follows the reading stated in the design doc:
+rule or k; this oracle takes the following reading of them:
 
   * blocks are the aligned runs of TOPK_BLOCK positions [64m, 64m+63];
   * a block is eligible for the query at position t when it lies entirely
