@@ -186,22 +186,34 @@ def topk_decode_bytes(B, H, hd, D, W, pos, k, es=2, blk=64):
     return B * tot
 
 
-def kernel_source_hash(name):
-    p = os.path.join(ROOT, "dilated_sparse_attention_rat_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# the source files of each profiled kernel (the kernel file, then the
+# kernel-specific header it includes)
+KERNEL_SOURCES = {
+    "scan_kernel": ("scan.hip", "scan_tree.h"),
+    "attn_prefill_kernel": ("attn_prefill.hip", "attn_tile.h"),
+    "attn_resident_kernel": ("attn_resident.hip", "attn_tile.h"),
+}
 
 
-def traffic_from_profiles(kernel_file, launch_key):
+def kernel_source_hash(*names):
+    """sha256[:16] of the named csrc files, concatenated in order."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "dilated_sparse_attention_rat_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, launch_key):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+    on the current sources of the kernel (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
         e = d.get(launch_key)
-        if not e or e.get("source_sha") != kernel_source_hash(kernel_file):
+        if not e or e.get("source_sha") != kernel_source_hash(*KERNEL_SOURCES[kernel]):
             return None
         return float(e["bytes_per_launch"])
     except Exception:
@@ -340,9 +352,10 @@ class PrefillRig:
                               tflops=af / attn_us / 1e6, kernel=attn_kernel_name(w),
                               roofline=roof_for("attention", ab, af, attn_us)),
         }
-        ks["scan"]["roofline"]["traffic"] = traffic_from_profiles("scan.hip", f"scan_w{self.wid}")
+        ks["scan"]["roofline"]["traffic"] = traffic_from_profiles("scan_kernel",
+                                                                  f"scan_w{self.wid}")
         ks["attention"]["roofline"]["traffic"] = traffic_from_profiles(
-            "attn_prefill.hip", f"attn_w{self.wid}")
+            attn_kernel_name(w), f"attn_w{self.wid}")
         ks["attention"]["mfma_frac_useful"] = af / attn_us / 1e6 / MFMA_BF16_PEAK_TFLOPS
         ks["attention"]["hbm_frac"] = ab / attn_us / 1e3 / HBM_PEAK_GBS
         if with_decode:

@@ -214,6 +214,7 @@ int launch_ring_carry(int dtype, int hd, int B, int H, int64_t WS, const HeadTab
                       int64_t t0, int64_t T, const void* kr_in, const void* vr_in, void* kr_out,
                       void* vr_out, void* stream);
 int launch_attn_prefill(int dtype, int hd, const AttnParams& p, void* stream);
+int launch_attn_resident(int dtype, int hd, const AttnParams& p, void* stream);
 int launch_decode(int dtype, int hd, const DecodeParams& p, void* stream);
 int launch_backward(int dtype, int hd, const BwdParams& p, void* stream);
 int launch_decode_topk(int dtype, int hd, const TopkParams& p, void* stream);
