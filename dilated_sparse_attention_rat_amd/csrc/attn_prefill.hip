@@ -287,18 +287,28 @@ void attn_prefill_kernel(const AttnParams p) {
   // fetched into two L2s rather than all eight, and the cost per XCD stays
   // level even where a group mixes heavy and light heads.  The units past
   // the last full group are dealt round-robin.
+  // In a paired launch the groups from gsingle on take single tiles instead
+  // (nq per unit, heaviest first): they run last, and the hardware hands
+  // them out in decreasing cost as slots free up, which shortens the tail.
   const int L = blockIdx.x;
-  const int grouped = (p.B * p.H) / 8 * 8 * p.np;
+  const int nfull = (p.B * p.H) / 8;
+  const int gs = min(p.gsingle, nfull);
+  const int paired_blocks = gs * 8 * p.np;
+  const int single_blocks = (nfull - gs) * 8 * p.nq;
   int u, pr;
-  if (L < grouped) {
-    const int x = L & 7;
-    const int s = L >> 3;
-    const int grp = s / p.np;
-    pr = s - grp * p.np;
-    u = 8 * grp + (pr < (p.np + 1) / 2 ? x : 7 - x);
+  bool tail = false;
+  if (L < paired_blocks + single_blocks) {
+    tail = L >= paired_blocks;
+    const int np_u = tail ? p.nq : p.np;
+    const int r = tail ? L - paired_blocks : L;
+    const int x = r & 7;
+    const int s = r >> 3;
+    const int g = s / np_u;
+    pr = s - g * np_u;
+    u = 8 * ((tail ? gs : 0) + g) + (pr < (np_u + 1) / 2 ? x : 7 - x);
   } else {
-    const int r = L - grouped;
-    u = grouped / p.np + r / p.np;
+    const int r = L - paired_blocks - single_blocks;
+    u = 8 * nfull + r / p.np;
     pr = r - (r / p.np) * p.np;
   }
   const int rank = u / p.B;
@@ -306,7 +316,7 @@ void attn_prefill_kernel(const AttnParams p) {
   const int h = p.perm[rank];
 
   const int qa = p.nq - 1 - pr;  // heavy tile first, then its partner
-  const int ntiles = p.paired && pr < qa ? 2 : 1;
+  const int ntiles = p.paired && !tail && pr < qa ? 2 : 1;
   const int64_t bh = (int64_t)b * p.H + h;
   const int64_t off = bh * p.T * HD;
   const ST* qp = reinterpret_cast<const ST*>(p.q) + (bh / p.H) * p.q_sb + (bh % p.H) * p.q_sh;
@@ -324,7 +334,7 @@ void attn_prefill_kernel(const AttnParams p) {
 
 template <typename ST, int HD>
 int launch_t(const AttnParams& p, hipStream_t st) {
-  const int64_t nblk = (int64_t)p.H * p.B * p.np;
+  const int64_t nblk = p.nblk;
   if (nblk == 0) return 0;
   // the ring-reading variant only where a window reaches before t0
   const bool ring = p.t0 > 0 && p.WS > 0;

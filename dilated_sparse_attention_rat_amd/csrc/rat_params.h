@@ -75,6 +75,8 @@ struct AttnParams {
   int nq;            // query tiles per (b, h)
   int np;            // workgroups per (b, h): pairs of query tiles, or single tiles
   int paired;        // 1: workgroup pr takes tiles nq-1-pr and pr; 0: tile nq-1-pr only
+  int gsingle;       // paired launches: groups of 8 units from gsingle on take single tiles
+  int64_t nblk;      // workgroups of the streamed launch
   int dma;           // K/V tiles loaded straight into LDS (bf16, hd 128, qb 2, no ring)
   float scale_log2;  // scale * log2(e)
   int64_t R;
@@ -233,6 +235,7 @@ int scan_rows_per_chunk(int dtype, int hd);
 int coop_grid_limit(const void* kernel, int threads);
 
 constexpr int kAttnBN = 64;    // keys per LDS tile
+constexpr int kAttnTailDiv = 4;  // a paired launch runs its last 1/kAttnTailDiv of full groups as single tiles
 constexpr int kDecodeThreads = 256;
 constexpr int kTopkBlock = RAT_TOPK_BLOCK;   // positions per selectable block
 constexpr int kTopkMaxK = RAT_TOPK_MAX_K;    // blocks selected per (b, h), at most
