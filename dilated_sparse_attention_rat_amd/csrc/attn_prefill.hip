@@ -288,8 +288,9 @@ void attn_prefill_kernel(const AttnParams p) {
   // level even where a group mixes heavy and light heads.  The units past
   // the last full group are dealt round-robin.
   // In a paired launch the groups from gsingle on take single tiles instead
-  // (nq per unit, heaviest first): they run last, and the hardware hands
-  // them out in decreasing cost as slots free up, which shortens the tail.
+  // (nq per unit): they run last, tile by tile across all of those groups,
+  // heaviest first, and the hardware hands them out in decreasing cost as
+  // slots free up, which shortens the tail.
   const int L = blockIdx.x;
   const int nfull = (p.B * p.H) / 8;
   const int gs = min(p.gsingle, nfull);
@@ -297,15 +298,21 @@ void attn_prefill_kernel(const AttnParams p) {
   const int single_blocks = (nfull - gs) * 8 * p.nq;
   int u, pr;
   bool tail = false;
-  if (L < paired_blocks + single_blocks) {
-    tail = L >= paired_blocks;
-    const int np_u = tail ? p.nq : p.np;
-    const int r = tail ? L - paired_blocks : L;
+  if (L < paired_blocks) {
+    const int x = L & 7;
+    const int s = L >> 3;
+    const int g = s / p.np;
+    pr = s - g * p.np;
+    u = 8 * g + (pr < (p.np + 1) / 2 ? x : 7 - x);
+  } else if (L < paired_blocks + single_blocks) {
+    tail = true;
+    const int r = L - paired_blocks;
     const int x = r & 7;
     const int s = r >> 3;
-    const int g = s / np_u;
-    pr = s - g * np_u;
-    u = 8 * ((tail ? gs : 0) + g) + (pr < (np_u + 1) / 2 ? x : 7 - x);
+    const int ntg = nfull - gs;  // tail groups
+    pr = s / ntg;
+    const int g = gs + (s - pr * ntg);
+    u = 8 * g + (pr < (p.nq + 1) / 2 ? x : 7 - x);
   } else {
     const int r = L - paired_blocks - single_blocks;
     u = 8 * nfull + r / p.np;
