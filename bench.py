@@ -36,6 +36,7 @@ work, on all host cores and on one.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -462,6 +463,13 @@ def run(args, rat, synth, torch, np):
     # in a pass whose kernels all ran at their usual speed).
     K = args.steps
     walls = []
+    # Python's cyclic collector off while steps are queued: a full collection
+    # over the interpreter's heap (torch and numpy loaded) stalls the host
+    # that launches the steps for tens of ms (a per-step probe saw single
+    # launches of 1 and 31 ms among ~0.1 ms ones), which empties the GPU's
+    # queue inside a timed pass
+    gc.collect()
+    gc.disable()
     for _ in range(2):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -485,6 +493,7 @@ def run(args, rat, synth, torch, np):
         rig.step(sets[i % 2], evs[i])
     torch.cuda.synchronize()
     wall_instr = time.perf_counter() - t1
+    gc.enable()
     rig.check("the instrumented steps")
     del graphs
     in_step = [float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3 for j in range(3)]
