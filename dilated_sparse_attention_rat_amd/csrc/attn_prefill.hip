@@ -157,16 +157,20 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int b, int h, 
       RowMap<ST, HD> rows;
       int nv, k0;
       item_src(i, rows, nv, k0);
-      ST* dK = sK + st * (C::BN * HD);
-      ST* dV = sV + st * (C::BN * HD);
+      // wave-uniform LDS bases and tile rows in SGPRs; per lane only a
+      // 32-bit byte offset (row clamp, row, swizzled chunk)
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      const uint32_t lK = lds_addr(sK + st * (C::BN * HD));
+      const uint32_t lV = lds_addr(sV + st * (C::BN * HD));
       const int pc = lane & 15;
 #pragma unroll
       for (int j = 0; j < C::BN / 16; ++j) {
-        const int ins = (C::BN / 16) * wave + j;
+        const int ins = (C::BN / 16) * wv + j;
         const int r = 4 * ins + (lane >> 4);
-        const int64_t rs = (int64_t)min(r, nv - 1) * HD;
-        dma16(rows.kh + rs + 8 * (pc ^ (r & 15)), dK + ins * 4 * HD);
-        dma16(rows.vh + rs + 8 * (pc ^ (2 * (r & 7))), dV + ins * 4 * HD);
+        const uint32_t ro = (uint32_t)min(r, nv - 1) * (uint32_t)(HD * sizeof(ST));
+        const uint32_t lo = (uint32_t)(ins * 4 * HD * sizeof(ST));
+        dma16s(rows.kh, ro + 16u * (uint32_t)(pc ^ (r & 15)), lK + lo);
+        dma16s(rows.vh, ro + 16u * (uint32_t)(pc ^ (2 * (r & 7))), lV + lo);
       }
     }
   };

@@ -156,6 +156,22 @@ __device__ __forceinline__ void dma16(const void* src, const bf16* dst) {
       : "memory");
 }
 
+// dma16 with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (the scalar-base form of the same load): no 64-bit address
+// arithmetic per lane.  lds_base is the wave-uniform LDS byte address.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const bf16* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+
 // 8 consecutive storage elements -> fragment
 __device__ __forceinline__ Frag<bf16> frag_ld8(const bf16* p) {
   Frag<bf16> f;
