@@ -187,12 +187,12 @@ def topk_decode_bytes(B, H, hd, D, W, pos, k, es=2, blk=64):
     return B * tot
 
 
-# the source files of each profiled kernel (the kernel file, then the
-# kernel-specific header it includes)
+# the source files of each profiled kernel (the kernel file, the
+# kernel-specific header it includes, and the shared device header)
 KERNEL_SOURCES = {
-    "scan_kernel": ("scan.hip", "scan_tree.h"),
-    "attn_prefill_kernel": ("attn_prefill.hip", "attn_tile.h"),
-    "attn_resident_kernel": ("attn_resident.hip", "attn_tile.h"),
+    "scan_kernel": ("scan.hip", "scan_tree.h", "rat_device.h"),
+    "attn_prefill_kernel": ("attn_prefill.hip", "attn_tile.h", "rat_device.h"),
+    "attn_resident_kernel": ("attn_resident.hip", "attn_tile.h", "rat_device.h"),
 }
 
 
