@@ -538,6 +538,16 @@ void bwd_dkv_kernel(const BwdParams p) {
     qt0 = a0;
   }
 
+  // queries that see the lane's key: an interval [vlo, vhi] (anchor: from
+  // (key+1)D + W on; window: key+1 .. key+W; both below T), tested per
+  // element with one unsigned compare (no per-element branch); an empty
+  // interval (a key past the last valid one, or one no query sees) is moved
+  // to 2^30, which no query position reaches
+  int vlo = anchor ? (int)min<int64_t>((int64_t)(key + 1) * D + W, T) : key + 1;
+  int vhi = anchor ? T - 1 : min(T - 1, key + W);
+  if (key >= nkeys || vhi < vlo) vlo = vhi = 0x40000000;
+  const uint32_t vspan = (uint32_t)(vhi - vlo);
+
   Stage4<ST, HD, !C::TR> pq, po;
   float lpre = 0.f, dpre = 0.f;
   auto load = [&](int qt) {
@@ -580,17 +590,14 @@ void bwd_dkv_kernel(const BwdParams p) {
       }
     // element (query t = tq0 + 16mb + 4g + e, the lane's key)
     f32x4 P[C::NMB], dS[C::NMB];
+    const int tb = tq0 + 4 * g - vlo;  // query t = tq0 + 16mb + 4g + e, relative to vlo
 #pragma unroll
     for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = tq0 + 16 * mb + 4 * g + e;
-        bool vis = t < T && key < nkeys;
-        if (anchor)
-          vis = vis && (int64_t)(key + 1) * D + W <= t;
-        else
-          vis = vis && key <= t - 1 && key >= t - W;
-        const float pe = vis ? __builtin_amdgcn_exp2f(S[mb][e]) : 0.f;
+        const bool vis = (uint32_t)(tb + 16 * mb + e) <= vspan;
+        const float ex = __builtin_amdgcn_exp2f(S[mb][e]);
+        const float pe = vis ? ex : 0.f;
         P[mb][e] = pe;
         dS[mb][e] = pe * dP[mb][e];
       }
