@@ -345,10 +345,9 @@ int attn_impl(int dtype, int B, int H, int64_t T, int hd, const int32_t* D, cons
   }
   if (p.nblk > INT32_MAX) return RAT_ERR_UNSUPPORTED;
   // K/V tiles straight into LDS (two stages, no staging registers) for the
-  // streamed two-block kernel over windowless heads
-  bool windowless = true;
-  for (int h = 0; h < H; ++h) windowless = windowless && W[h] == 0;
-  p.dma = p.mode == 0 && dtype == RAT_DTYPE_BF16 && hd == 128 && p.qb == 2 && windowless;
+  // streamed two-block kernel (a continuation whose window reaches into the
+  // previous ring keeps register staging)
+  p.dma = p.mode == 0 && dtype == RAT_DTYPE_BF16 && hd == 128 && p.qb == 2;
   p.scale_log2 = sc * 1.4426950408889634f;
   p.q = q;
   p.q_sb = (int64_t)H * T * hd;
